@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the transposed-convolution / pooling hot path on one MI355X.
+
+A step is one pass of the whole path over its full-size synthetic workloads,
+inputs already resident in HBM:
+  fused3d_f32   ConvTranspose3d(3->16,k3,s2,p1) -> x0.5 -> AvgPool3d(2) -> +bias -> x1.0
+                on [128,3,16,32,32] fp32 -> [128,16,15,31,31]
+  avgpool3d     AvgPool3d(k3,s2,p1), divisor 27, [16,32,128,128,256] -> [16,32,64,64,128]
+  convT1d       ConvTranspose1d(32->64,k5,s1,p0,d3) [32,32,131072] -> [32,64,131084]
+  fused3d_bf16  the fused chain 32->64 with bf16 x and w, [16,32,16,32,32] -> [16,64,15,31,31]
+
+Prints ONE JSON line: value = algorithmic HBM bytes of a step / step time
+(GB/s), per-op ms / GB/s / GFLOP/s, the roofline of the kernel that takes the
+most time (timed live with HIP events on the launch stream), and the CPU oracle
+timed on a bounded sample of the same workloads.
+
+  python bench.py [--steps K] [--warmup W] [--ops a,b] [--no-cpu-baseline]
+  python bench.py --ops copy        # plain 1 GiB device copy (counter calibration)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_F32_PEAK_TFLOPS = 157.3   # dense fp32 matrix
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # dense bf16 matrix
+
+OP_SOURCES = {
+    "fused3d_f32": "fused3d_f32.hip",
+    "avgpool3d": "avgpool3d.hip",
+    "convT1d": "convT1d_f32.hip",
+    "fused3d_bf16": "fused3d_bf16.hip",
+}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(op):
+    p = os.path.join(ROOT, "transposed_conv_pooling_amd", "csrc", OP_SOURCES[op])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(op):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when absent or taken on a different version of the kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p)).get(op)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha256_16") != source_hash(op):
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- workloads --
+class Op:
+    def __init__(self, name, run, alg_bytes, flops, bound, peak, inputs, oracle_sample):
+        self.name, self.run, self.alg_bytes, self.flops = name, run, alg_bytes, flops
+        self.bound, self.peak = bound, peak
+        self.inputs = inputs
+        self.oracle_sample = oracle_sample    # () -> (seconds, fraction of the op)
+
+
+def make_ops(names, dev):
+    import torch
+
+    import synth
+    import transposed_conv_pooling_amd as ct
+
+    ops = []
+
+    def nbytes(*ts):
+        return int(sum(t.numel() * t.element_size() for t in ts))
+
+    if "fused3d_f32" in names:
+        wl = synth.WORKLOADS["c2"]
+        log(f"inputs: {wl.description}")
+        t = synth.make_inputs(wl)
+        x, w, b = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "bias"))
+        out = torch.empty((128, 16, 15, 31, 31), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, b=b, out=out):
+            ct.ct_convT3d_scale_pool_bias(x, w, None, b, 0.5, 1.0, out=out)
+
+        def sample(t=t):
+            import oracle
+            t0 = time.perf_counter()
+            oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
+            return time.perf_counter() - t0, 1.0, "all 128 batch items"
+
+        ops.append(Op("fused3d_f32", run, nbytes(x, w, b, out),
+                      2 * out.numel() * 3 * 8, "hbm", HBM_PEAK_GBS,
+                      [wl.description], sample))
+
+    if "avgpool3d" in names:
+        wl = synth.WORKLOADS["c3"]
+        log(f"inputs: {wl.description} (8.6 GB host generation)")
+        xh = synth.normal(wl.seed, synth.STREAM_X, wl.x_shape)
+        x = torch.from_numpy(xh).to(dev)
+        out = torch.empty((16, 32, 64, 64, 128), dtype=torch.float32, device=dev)
+
+        def run(x=x, out=out):
+            ct.ct_avgpool3d(x, 3, 2, 1, True, out=out)
+
+        def sample(xh=xh):
+            import oracle
+            k = 128
+            t0 = time.perf_counter()
+            oracle.avgpool3d(xh.reshape(512, 128, 128, 256)[:k], 3, 2, 1, True)
+            return time.perf_counter() - t0, k / 512.0, f"{k} of 512 (n,c) slices"
+
+        ops.append(Op("avgpool3d", run, nbytes(x, out), 27 * out.numel(), "hbm",
+                      HBM_PEAK_GBS, [wl.description], sample))
+
+    if "convT1d" in names:
+        wl = synth.WORKLOADS["c4"]
+        log(f"inputs: {wl.description}")
+        t = synth.make_inputs(wl)
+        x, w = torch.from_numpy(t["x"]).to(dev), torch.from_numpy(t["w"]).to(dev)
+        out = torch.empty((32, 64, 131084), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, out=out):
+            ct.ct_convT1d(x, w, None, 1, 0, 3, out=out)
+
+        def sample(t=t):
+            import oracle
+            n = 8
+            t0 = time.perf_counter()
+            oracle.convT1d(t["x"][:n], t["w"], None, 1, 0, 3)
+            return time.perf_counter() - t0, n / 32.0, f"{n} of 32 batch items"
+
+        flops = 2 * 32 * 32 * 131072 * 5 * 64
+        ops.append(Op("convT1d", run, nbytes(x, w, out), flops, "mfma",
+                      MFMA_F32_PEAK_TFLOPS, [wl.description], sample))
+
+    if "fused3d_bf16" in names:
+        wl = synth.WORKLOADS["c5"]
+        log(f"inputs: {wl.description}")
+        t = synth.make_inputs(wl)
+        x = torch.from_numpy(t["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(t["w_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+        b = torch.from_numpy(t["bias"]).to(dev)
+        out = torch.empty((16, 64, 15, 31, 31), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, b=b, out=out):
+            ct.ct_convT3d_scale_pool_bias(x, w, None, b, 0.5, 1.0, out=out)
+
+        def sample(t=t):
+            import oracle
+            t0 = time.perf_counter()
+            oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
+            return time.perf_counter() - t0, 1.0, "all 16 batch items"
+
+        ops.append(Op("fused3d_bf16", run, nbytes(x, w, b, out), 2 * out.numel() * 32 * 8,
+                      "hbm", HBM_PEAK_GBS, [wl.description], sample))
+
+    if "copy" in names:
+        n = 1 << 28                      # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+
+        def run(src=src, dst=dst):
+            dst.copy_(src)
+
+        ops.append(Op("copy", run, 2 * 4 * n, 0, "hbm", HBM_PEAK_GBS,
+                      ["device copy 1 GiB fp32"], None))
+    return ops
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--ops", default="fused3d_f32,avgpool3d,convT1d,fused3d_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the ops shard with no exchange along batch, but only the single-GPU "
+              "kernel is built and measured)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    names = [s for s in args.ops.split(",") if s]
+    ops = make_ops(names, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        for op in ops:
+            op.run()
+    torch.cuda.synchronize()
+
+    ev = {op.name: [] for op in ops}
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_start = torch.cuda.Event(enable_timing=True)
+    step_end = torch.cuda.Event(enable_timing=True)
+    step_start.record(stream)
+    for _ in range(args.steps):
+        for op in ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            op.run()
+            b.record(stream)
+            ev[op.name].append((a, b))
+    step_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    gpu_ms_per_step = step_start.elapsed_time(step_end) / args.steps
+
+    per_op = {}
+    total_bytes = 0
+    for op in ops:
+        ms = [a.elapsed_time(b) for a, b in ev[op.name]]
+        avg = float(np.mean(ms))
+        d = {"ms": round(avg, 5), "ms_min": round(float(np.min(ms)), 5),
+             "alg_bytes": op.alg_bytes, "GB_s": round(op.alg_bytes / avg / 1e6, 1),
+             "hbm_frac": round(op.alg_bytes / avg / 1e6 / HBM_PEAK_GBS, 4)}
+        if op.flops:
+            d["GFLOP_s"] = round(op.flops / avg / 1e6, 1)
+        if op.name == "convT1d":
+            d["mfma_frac"] = round(op.flops / avg / 1e9 / MFMA_F32_PEAK_TFLOPS, 4)
+        d["workload"] = op.inputs[0]
+        per_op[op.name] = d
+        if op.name != "copy":
+            total_bytes += op.alg_bytes
+
+    dom = max(ops, key=lambda o: per_op[o.name]["ms"])
+    dms = per_op[dom.name]["ms"]
+    if dom.bound == "mfma":
+        achieved = dom.flops / dms / 1e9            # TFLOP/s
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": dom.peak,
+                "unit": "TFLOP/s", "frac": round(achieved / dom.peak, 4)}
+    else:
+        achieved = dom.alg_bytes / dms / 1e6        # GB/s
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": dom.peak,
+                "unit": "GB/s", "frac": round(achieved / dom.peak, 4)}
+    roof["kernel"] = dom.name
+    roof["traffic"] = measured_traffic(dom.name) if dom.name in OP_SOURCES else None
+
+    cpu = None
+    if not args.no_cpu_baseline and all(o.oracle_sample for o in ops):
+        import oracle
+        log("cpu baseline: oracle on a bounded sample of each workload")
+        est_s, samples = 0.0, []
+        for op in ops:
+            secs, frac, what = op.oracle_sample()
+            est_s += secs / frac
+            samples.append(f"{op.name}: {what} in {secs:.2f} s")
+        cpu = {"value": round(total_bytes / est_s / 1e9, 4), "unit": "GB/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": "; ".join(samples) + f"; full step extrapolated to {est_s:.1f} s"}
+
+    value = total_bytes / (ms_per_step / 1e3) / 1e9 if total_bytes else per_op["copy"]["GB_s"]
+    line = {
+        "metric": "achieved HBM GB/s (and % of peak) per op; convT1d GFLOP/s; ms/call",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Philox N(0,1) activations and biases, U(+-1/sqrt(fan)) weights)",
+        "config": {"workload": "one full-size pass of " + ", ".join(o.name for o in ops),
+                   "ops": {o.name: o.inputs[0] for o in ops}},
+        "ops": per_op,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

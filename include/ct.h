@@ -1,0 +1,177 @@
+/*
+ * ct.h - C ABI of the transposed-convolution / pooling library (libct.so),
+ * hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * Operations (each defined on a POPCORNBENCH web page, one problem per page):
+ *   [p50] "Kimi-K2.6 l2_p50": ConvTranspose3d -> x scale1 -> AvgPool3d(2) ->
+ *         + bias -> x scale2, fused into one kernel that never materialises
+ *         the pre-pool tensor.
+ *   [p46] "Kimi-K2.6 l1_p46": AvgPool3d(k3, s2, p1) with zero padding counted
+ *         in the divisor (count_include_pad, divisor 27).
+ *   [p74] "Kimi-K2.6 l1_p74": ConvTranspose1d with dilation (k5, s1, p0, d3 on
+ *         the page).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, contiguous, row-major (NCDHW / NCL).  Weights are
+ *     laid out [Cin][Cout][k...] as PyTorch's transposed convolutions store
+ *     them.  Output sizes follow PyTorch's formulas (ct_convT_out_len,
+ *     ct_pool_out_len).
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or from any allocator
+ *     of the current device).  The caller owns every buffer, allocates the
+ *     output, and keeps all buffers alive until the work on `stream` is done.
+ *     The library allocates no device memory and keeps no state besides a
+ *     per-thread error string.
+ *   - fp32 pointers must be 4-byte aligned, bf16 pointers 2-byte aligned.
+ *     The output must not overlap any input.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing synchronises.  A device fault surfaces at the
+ *     caller's next synchronisation, not in the return value.
+ *   - Every call returns a ct_status.  All argument checks run before any HIP
+ *     call, so a rejected call touches neither the GPU nor the HIP runtime.
+ *     ct_last_error() gives a human-readable reason for the last non-OK
+ *     status on the calling thread.
+ */
+#ifndef CT_H
+#define CT_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CT_API __attribute__((visibility("default")))
+#else
+#define CT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CT_OK = 0,
+    CT_EINVAL = 1,       /* null required pointer, bad size, empty output, misalignment, overlap */
+    CT_EUNSUPPORTED = 2, /* well-formed request this library does not implement */
+    CT_EHIP = 3          /* the HIP runtime reported an error when launching */
+} ct_status;
+
+typedef enum {
+    CT_F32 = 0,          /* IEEE binary32 */
+    CT_BF16 = 1          /* bfloat16 (upper half of a binary32) */
+} ct_dtype;
+
+/*
+ * Output length of a transposed convolution along one axis:
+ *   (in - 1) * stride - 2 * pad + dilation * (k - 1) + out_pad + 1.
+ * [p50], passage deriving the ConvTranspose3d output shape (16/32/32 ->
+ * 31/63/63); [p74], opening passage (L_out = L + 12 at k5 d3).
+ * Pure host arithmetic; may return a value <= 0 for impossible geometry.
+ */
+CT_API int64_t ct_convT_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad,
+                         int64_t out_pad, int64_t dilation);
+
+/*
+ * Output length of an average pool along one axis, floor mode:
+ *   floor((in + 2 * pad - k) / stride) + 1.
+ * [p50], passage on AvgPool3d(2) (31 -> 15); [p46], opening passage
+ * (128 -> 64, 256 -> 128).  Returns <= 0 when no window fits.
+ * stride == 0 means stride = k (PyTorch's default).
+ */
+CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad);
+
+/*
+ * Fused ConvTranspose3d -> x scale1 -> AvgPool3d -> + bias -> x scale2
+ * ([p50], problem statement and the model's forward):
+ *
+ *   Y   = ConvTranspose3d(x, w, stride, pad, out_pad) + conv_bias
+ *   out = ((AvgPool3d_{pool_k, pool_s}(Y * scale1)) + bias) * scale2
+ *
+ * computed directly per pooled voxel from the 2x2x2 input taps each pooled
+ * voxel depends on ([p50], passages on the stride-2 parity rule and on
+ * grouping the 27 weight terms by input tap); the pre-pool tensor Y is never
+ * written.
+ *
+ *   x          [N, Cin, D, H, W], dtype x_dtype
+ *   w          [Cin, Cout, k, k, k], dtype w_dtype
+ *   conv_bias  [Cout] fp32, or NULL (= 0)
+ *   bias       [Cout] fp32, or NULL (= 0); the page's [Cout,1,1,1] parameter
+ *   out        [N, Cout, Dp, Hp, Wp] fp32, with Do = ct_convT_out_len(D, k,
+ *              stride, pad, out_pad, 1) and Dp = ct_pool_out_len(Do, pool_k,
+ *              pool_s, 0) (likewise H, W).  At k3 s2 p1 with a 2-pool,
+ *              Dp = D - 1 for every D ([p50], passage on arbitrary sizes).
+ *
+ * Implemented: k = 3, stride = 2, pad = 1, out_pad = 0, pool_k = 2,
+ * pool_s = 2 (or 0, meaning pool_k), with (x_dtype, w_dtype) = (CT_F32,
+ * CT_F32) or (CT_BF16, CT_BF16); accumulation and output are fp32.
+ * Other geometry -> CT_EUNSUPPORTED.  D, H or W equal to 1 gives an empty
+ * output -> CT_EINVAL.
+ */
+CT_API ct_status ct_convT3d_scale_pool_bias(
+    const void *x, int x_dtype,
+    const void *w, int w_dtype,
+    const float *conv_bias, const float *bias,
+    float scale1, float scale2,
+    int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout,
+    int k, int stride, int pad, int out_pad, int pool_k, int pool_s,
+    float *out, void *stream);
+
+/*
+ * AvgPool3d over zero padding ([p46], opening passages):
+ *   out[n,c,d,h,w] = (sum over kd,kh,kw < k of x[n,c, d*s - p + kd,
+ *                     h*s - p + kh, w*s - p + kw]) / k^3
+ * where taps outside the input read as 0 and the divisor is always k^3
+ * (count_include_pad).
+ *
+ *   x    [N, C, D, H, W] fp32
+ *   out  [N, C, Do, Ho, Wo] fp32, Do = ct_pool_out_len(D, k, stride, pad)
+ *
+ * Implemented: k = 3, stride = 2 (or 0, meaning k), pad = 1,
+ * count_include_pad = 1.  Other values -> CT_EUNSUPPORTED.  Any N, C, D, H,
+ * W >= 1 (sizes per (n, c) slice below 2^31 elements).
+ */
+CT_API ct_status ct_avgpool3d(const float *x,
+                       int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                       int k, int stride, int pad, int count_include_pad,
+                       float *out, void *stream);
+
+/*
+ * Transposed 1D convolution ([p74], gather form derived on the page):
+ *   y[n,co,o] = sum_ci sum_{k<K} x[n,ci,(o + pad - dilation*k)/stride]
+ *               * w[ci,co,k]  (+ bias[co])
+ * over the terms whose index is an integer inside [0, L); with stride 1 and
+ * pad 0 this is y[n,co,o] = sum_ci sum_k x[n,ci,o - dilation*k] w[ci,co,k].
+ * The weights are used unflipped.
+ *
+ *   x     [N, Cin, L], dtype x_dtype
+ *   w     [Cin, Cout, K], dtype w_dtype
+ *   bias  [Cout] fp32, or NULL (= 0)
+ *   out   [N, Cout, L_out] fp32, L_out = ct_convT_out_len(L, K, stride, pad,
+ *         out_pad, dilation)
+ *
+ * Implemented: stride = 1, pad = 0, out_pad = 0, any K >= 1 and
+ * dilation >= 1, (x_dtype, w_dtype) = (CT_F32, CT_F32), as long as the
+ * weights (64 * K * Cin4 floats, Cin4 = Cin rounded up to a multiple of 4)
+ * and one input strip (Cin4 rows of 256 + dilation*(K-1) floats, padded)
+ * fit the 160 KiB LDS of one gfx950 workgroup (Cin=32, K=5, dilation 3
+ * needs 74 KiB).  Other values -> CT_EUNSUPPORTED.  Computed as an implicit GEMM on the
+ * fp32 matrix cores (full fp32 products, fp32 accumulation).
+ */
+CT_API ct_status ct_convT1d(const void *x, int x_dtype,
+                     const void *w, int w_dtype,
+                     const float *bias,
+                     int64_t N, int64_t Cin, int64_t L, int64_t Cout,
+                     int K, int stride, int pad, int dilation, int out_pad,
+                     float *out, void *stream);
+
+/* Static name of a status code ("CT_OK", ...). */
+CT_API const char *ct_status_str(int status);
+
+/* Reason for the last non-OK status returned on this thread ("" if none). */
+CT_API const char *ct_last_error(void);
+
+/* Library version string. */
+CT_API const char *ct_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CT_H */

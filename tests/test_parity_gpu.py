@@ -1,0 +1,252 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Tolerances (elementwise, |gpu - oracle| <= atol + rtol * |oracle|):
+  fp32 inputs:  atol 1e-4, rtol 1e-5
+  bf16 inputs:  atol 1e-4, rtol 2e-2 (the oracle consumes the same
+                bf16-rounded values, widened exactly)
+Outputs are pre-filled with NaN so an element the kernel never writes fails.
+Small cases span several tiles plus ragged tails; the full-size workloads are
+checked on every element (fused fp32) or on sampled (n, c) slices / batch
+items that the oracle recomputes from scratch.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+import transposed_conv_pooling_amd as ct  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = (1e-4, 1e-5)
+BF16_TOL = (1e-4, 2e-2)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def assert_close(got, ref, tol, what=""):
+    atol, rtol = tol
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    ok = err <= atol + rtol * np.abs(ref)          # NaN -> not ok
+    if not ok.all():
+        idx = np.argwhere(~ok)
+        i0 = tuple(idx[0])
+        raise AssertionError(
+            f"{what}: {len(idx)} of {ok.size} elements out of tolerance; first at {i0}: "
+            f"gpu={got[i0]!r} oracle={ref[i0]!r}; max err {np.nanmax(err):.3g}")
+
+
+def nan_like(shape, dev):
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=dev)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ------------------------------------------------------------ fused fp32 ----
+def run_fused(dev, x, w, cb, b, s1, s2, dtype="f32"):
+    N, Cin, D, H, W = x.shape
+    Cout = w.shape[1]
+    if dtype == "bf16":
+        xg = torch.from_numpy(synth.to_bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        wg = torch.from_numpy(synth.to_bf16_bits(w).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        xg, wg = torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev)
+    cbg = None if cb is None else torch.from_numpy(cb).to(dev)
+    bg = None if b is None else torch.from_numpy(b).to(dev)
+    out = nan_like((N, Cout, D - 1, H - 1, W - 1), dev)
+    ct.ct_convT3d_scale_pool_bias(xg, wg, cbg, bg, s1, s2, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+FUSED_SMALL = [
+    # N, Cin, Cout, D, H, W
+    (1, 1, 1, 2, 2, 2),
+    (2, 3, 16, 8, 16, 16),
+    (2, 3, 16, 5, 7, 40),
+    (1, 4, 20, 3, 9, 17),
+    (3, 2, 33, 4, 4, 4),
+    (1, 5, 7, 6, 5, 18),
+    (1, 32, 64, 3, 5, 33),
+    (1, 7, 3, 2, 3, 49),
+]
+
+
+@pytest.mark.parametrize("shape", FUSED_SMALL, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("with_cb", [False, True], ids=["nocb", "cb"])
+def test_fused_f32_small(dev, shape, with_cb):
+    N, Cin, Cout, D, H, W = shape
+    log(f"fused f32 {shape} cb={with_cb}")
+    seed = 1000 + sum(shape)
+    x = synth.normal(seed, 0, (N, Cin, D, H, W))
+    bound = 1.0 / np.sqrt(Cin * 27)
+    w = synth.uniform(seed, 1, (Cin, Cout, 3, 3, 3), -bound, bound)
+    b = synth.normal(seed, 2, (Cout,))
+    cb = synth.normal(seed, 3, (Cout,)) if with_cb else None
+    got = run_fused(dev, x, w, cb, b, 0.5, 1.0)
+    ref = oracle.convT3d_scale_pool_bias(x, w, cb, b, 0.5, 1.0)
+    assert_close(got, ref, F32_TOL, f"fused {shape}")
+
+
+def test_fused_f32_other_scales_no_bias(dev):
+    x = synth.uniform(77, 0, (2, 3, 6, 9, 21), 0.0, 1.0)      # the page's torch.rand inputs
+    w = synth.uniform(77, 1, (3, 5, 3, 3, 3), -0.2, 0.2)
+    got = run_fused(dev, x, w, None, None, -1.7, 0.3)
+    ref = oracle.convT3d_scale_pool_bias(x, w, None, None, -1.7, 0.3)
+    assert_close(got, ref, F32_TOL, "fused scales")
+
+
+def test_fused_f32_c1_workload(dev):
+    wl = synth.WORKLOADS["c1"]
+    t = synth.make_inputs(wl, conv_bias=True)
+    log(wl.description)
+    for cb in (None, t["conv_bias"]):
+        got = run_fused(dev, t["x"], t["w"], cb, t["bias"], 0.5, 1.0)
+        ref = oracle.convT3d_scale_pool_bias(t["x"], t["w"], cb, t["bias"], 0.5, 1.0)
+        assert got.shape == (2, 16, 7, 15, 15)
+        assert_close(got, ref, F32_TOL, "c1")
+
+
+def test_fused_f32_c2_full(dev):
+    """Full-size [128,3,16,32,32] -> [128,16,15,31,31], every element."""
+    wl = synth.WORKLOADS["c2"]
+    log(wl.description)
+    t = synth.make_inputs(wl)
+    got = run_fused(dev, t["x"], t["w"], None, t["bias"], 0.5, 1.0)
+    ref = oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
+    assert got.shape == (128, 16, 15, 31, 31)
+    assert_close(got, ref, F32_TOL, "c2")
+
+
+def test_fused_f32_nan_propagates_locally(dev):
+    """A NaN input reaches exactly the pooled voxels whose 2x2x2 taps contain it."""
+    x = synth.normal(5, 0, (1, 2, 5, 6, 7))
+    x[0, 1, 2, 3, 4] = np.nan
+    w = synth.uniform(5, 1, (2, 3, 3, 3, 3), -0.2, 0.2)
+    got = run_fused(dev, x, w, None, None, 0.5, 1.0)
+    nan = np.isnan(got)
+    exp = np.zeros_like(nan)
+    exp[0, :, 1:3, 2:4, 3:5] = True
+    assert np.array_equal(nan, exp)
+
+
+# ------------------------------------------------------------ avgpool3d ----
+POOL_SMALL = [
+    (1, 1, 1, 1, 1),
+    (1, 1, 2, 2, 2),
+    (2, 3, 9, 10, 13),
+    (1, 2, 5, 6, 256),
+    (1, 1, 3, 4, 260),        # two column chunks, vector path
+    (1, 1, 4, 5, 514),        # two column chunks, element path
+    (1, 2, 33, 35, 64),       # several plane chunks and row groups
+    (2, 1, 7, 3, 1),
+]
+
+
+@pytest.mark.parametrize("shape", POOL_SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_pool_small(dev, shape):
+    log(f"pool {shape}")
+    x = synth.normal(2000 + sum(shape), 0, shape)
+    xg = torch.from_numpy(x).to(dev)
+    dims = [(n - 1) // 2 + 1 for n in shape[2:]]
+    out = nan_like(shape[:2] + tuple(dims), dev)
+    ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), oracle.avgpool3d(x, 3, 2, 1, True), F32_TOL, f"pool {shape}")
+
+
+def test_pool_misaligned_input_takes_element_path(dev):
+    shape = (2, 2, 6, 7, 64)
+    x = synth.normal(31, 0, shape)
+    buf = torch.empty(x.size + 1, dtype=torch.float32, device=dev)
+    buf[1:] = torch.from_numpy(x.reshape(-1)).to(dev)
+    xg = buf[1:].view(shape)                        # 4-byte but not 16-byte aligned
+    out = nan_like((2, 2, 3, 4, 32), dev)
+    ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), oracle.avgpool3d(x, 3, 2, 1, True), F32_TOL, "misaligned")
+
+
+def test_pool_constant_input_border_values(dev):
+    """All-ones input: 8/27 at corners, 12/27 on edges, 18/27 on faces, 1 inside."""
+    x = torch.ones((1, 2, 16, 16, 32), dtype=torch.float32, device=dev)
+    out = ct.ct_avgpool3d(x, 3, 2, 1, True)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()[0, 0]
+    assert abs(o[0, 0, 0] - 8 / 27) < 1e-6 and abs(o[0, 0, 5] - 12 / 27) < 1e-6
+    assert abs(o[0, 3, 5] - 18 / 27) < 1e-6 and abs(o[3, 3, 5] - 1.0) < 1e-6
+    assert abs(o[-1, -1, -1] - 1.0) < 1e-6
+
+
+def test_pool_c3_full_sampled(dev):
+    """Full-size [16,32,128,128,256] (2^31 elements); 6 whole (n, c) slices
+    recomputed by the oracle, plus global finiteness."""
+    wl = synth.WORKLOADS["c3"]
+    log(wl.description)
+    x = synth.normal(wl.seed, synth.STREAM_X, wl.x_shape)
+    xg = torch.from_numpy(x).to(dev)
+    out = nan_like((16, 32, 64, 64, 128), dev)
+    ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
+    torch.cuda.synchronize()
+    del xg
+    assert bool(torch.isfinite(out).all())
+    for (n, c) in [(0, 0), (0, 31), (7, 13), (11, 2), (15, 0), (15, 31)]:
+        got = out[n, c].cpu().numpy()
+        ref = oracle.avgpool3d(x[n, c], 3, 2, 1, True)
+        assert_close(got, ref, F32_TOL, f"c3 slice {(n, c)}")
+
+
+# -------------------------------------------------------------- convT1d ----
+CONV1D_SMALL = [
+    # N, Cin, Cout, L, K, dilation, bias
+    (1, 1, 1, 10, 1, 1, False),
+    (2, 32, 64, 700, 5, 3, False),
+    (1, 3, 5, 50, 4, 2, True),
+    (2, 8, 70, 300, 3, 7, True),
+    (1, 4, 16, 5, 5, 3, False),          # L shorter than the halo
+    (1, 36, 64, 513, 5, 3, False),
+    (3, 32, 64, 256, 5, 3, True),
+]
+
+
+@pytest.mark.parametrize("case", CONV1D_SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_conv1d_small(dev, case):
+    N, Cin, Cout, L, K, d, with_bias = case
+    log(f"convT1d {case}")
+    seed = 3000 + N + Cin + Cout + L
+    x = synth.normal(seed, 0, (N, Cin, L))
+    bnd = 1.0 / np.sqrt(Cin * K)
+    w = synth.uniform(seed, 1, (Cin, Cout, K), -bnd, bnd)
+    b = synth.normal(seed, 2, (Cout,)) if with_bias else None
+    Lo = L + d * (K - 1)
+    out = nan_like((N, Cout, Lo), dev)
+    ct.ct_convT1d(torch.from_numpy(x).to(dev), torch.from_numpy(w).to(dev),
+                  None if b is None else torch.from_numpy(b).to(dev), 1, 0, d, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), oracle.convT1d(x, w, b, 1, 0, d), F32_TOL, f"convT1d {case}")
+
+
+def test_conv1d_c4_full_sampled(dev):
+    """Full-size [32,32,131072] -> [32,64,131084]; batch items 0, 17, 31
+    recomputed by the oracle, plus global finiteness."""
+    wl = synth.WORKLOADS["c4"]
+    log(wl.description)
+    t = synth.make_inputs(wl)
+    out = nan_like((32, 64, 131084), dev)
+    ct.ct_convT1d(torch.from_numpy(t["x"]).to(dev), torch.from_numpy(t["w"]).to(dev), None,
+                  1, 0, 3, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    for n in (0, 17, 31):
+        ref = oracle.convT1d(t["x"][n:n + 1], t["w"], None, 1, 0, 3)
+        assert_close(out[n:n + 1].cpu().numpy(), ref, F32_TOL, f"c4 n={n}")

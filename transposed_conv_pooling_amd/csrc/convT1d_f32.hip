@@ -1,0 +1,181 @@
+// convT1d_f32.hip - dilated ConvTranspose1d (stride 1, pad 0) as an implicit
+// GEMM on the gfx950 fp32 matrix cores.
+//
+// Method ([p74] "Kimi-K2.6 l1_p74"): with stride 1 and pad 0 the transposed
+// convolution is the gather
+//     y[n,co,o] = sum_ci sum_{k<K} x[n,ci,o - dil*k] * w[ci,co,k]
+// over in-range input positions, weights unflipped (passages on the gather
+// formula and the dilation worked examples).  For one batch item it is the
+// GEMM  Y[co][o] = sum_kappa A[co][kappa] * B[kappa][o]  with
+// kappa = (k, ci), A[co][(k,ci)] = w[ci,co,k] and B[(k,ci)][o] =
+// x[ci, o - dil*k] (passage on the implicit-GEMM view, M = Cout,
+// K = Cin*K); B is never materialised (no im2col).
+//
+// MI355X mapping:
+//  * v_mfma_f32_16x16x4_f32 (full fp32 products and accumulation):
+//      A (16x4):  lane l supplies A[co = l%16][kappa = l/16]
+//      B (4x16):  lane l supplies B[kappa = l/16][o = l%16]
+//      D (16x16): lane l holds D[co = 4*(l/16) + r][o = l%16]
+//    kappa runs k-major with ci padded to a multiple of 4 (Cin4), so the 4
+//    kappas of one MFMA share one tap k.
+//  * A workgroup (4 waves) owns a 64-channel x 256-output tile; each wave
+//    computes 64 channels x 64 outputs = 16 MFMA accumulators.  Workgroups
+//    are persistent: they stage the weights once into LDS in fragment order
+//    (lane-consecutive, conflict-free) and then walk tiles.
+//  * Per tile the input strip x[n, :, o0-halo .. o0+255] (halo =
+//    dil*(K-1), zero outside [0,L)) is staged in LDS once; the K shifted
+//    views of the gather are different LDS offsets into that strip, read
+//    at a row stride of 16 mod 64 words so the four 16-lane groups of a
+//    fragment read hit disjoint banks.
+//  * Outputs are written with non-temporal stores, 16 consecutive outputs
+//    (64 bytes) per lane group.
+#include "ct_internal.h"
+
+namespace ct {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTO = 256;              // outputs per tile (64 per wave)
+constexpr int kCO = 64;               // output channels per tile
+
+__global__ __launch_bounds__(kThreads)
+void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
+                        const float *__restrict__ bias, int Cin, int Cin4, int L,
+                        int Cout, int K, int dil, int Lo, int tiles_per_n,
+                        int ntiles, int xs_str, float *__restrict__ y)
+{
+    extern __shared__ float lds[];
+    const int ksteps = (Cin4 * K) >> 2;
+    float *wfrag = lds;                               // [4 m][ksteps][64]
+    float *xs = lds + 4 * ksteps * 64;                // [Cin4][xs_str]
+    const int halo = dil * (K - 1);
+    const int ts = kTO + halo;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int cog = blockIdx.y;                       // 64-channel group
+
+    // Weights in fragment order: wfrag[(m*ksteps + j)*64 + l] = A[co][kappa]
+    // with co = cog*64 + 16m + l%16, kappa = 4j + l/16 = k*Cin4 + ci.
+    for (int e = threadIdx.x; e < 4 * ksteps * 64; e += kThreads) {
+        const int l = e & 63;
+        const int j = (e >> 6) % ksteps;
+        const int m = (e >> 6) / ksteps;
+        const int co = cog * kCO + 16 * m + (l & 15);
+        const int kap = 4 * j + (l >> 4);
+        const int k = kap / Cin4, ci = kap - k * Cin4;
+        wfrag[e] = (co < Cout && ci < Cin) ? w[((int64_t)ci * Cout + co) * K + k] : 0.0f;
+    }
+
+    float bv[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = cog * kCO + 16 * m + 4 * (lane >> 4) + r;
+            bv[m][r] = (bias && co < Cout) ? bias[co] : 0.0f;
+        }
+
+    const int kq = lane >> 4;
+    const int col = lane & 15;
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int n = tile / tiles_per_n;
+        const int o0 = (tile - n * tiles_per_n) * kTO;
+        __syncthreads();          // previous tile's strip fully consumed (and weights staged)
+        // stage x[n, ci, o0 - halo + t], t < ts
+        const float *xn = x + (int64_t)n * Cin * L;
+        for (int e = threadIdx.x; e < Cin4 * ts; e += kThreads) {
+            const int ci = e / ts, t = e - ci * ts;
+            const int pos = o0 - halo + t;
+            xs[ci * xs_str + t] = (ci < Cin && pos >= 0 && pos < L) ? xn[(int64_t)ci * L + pos] : 0.0f;
+        }
+        __syncthreads();
+
+        v4f acc[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[m][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+
+        // B row base for this lane: xs[ci][halo - dil*k + 64*wave + 16b + col]
+        const int obase = halo + 64 * wave + col;
+#pragma unroll 2
+        for (int j = 0; j < ksteps; ++j) {
+            const int kap = 4 * j + kq;
+            const int k = kap / Cin4, ci = kap - k * Cin4;
+            const float *xb = xs + ci * xs_str + obase - dil * k;
+            float av[4], bvv[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) av[m] = wfrag[(m * ksteps + j) * 64 + lane];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) bvv[b] = xb[16 * b];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bvv[b], acc[m][b], 0, 0, 0);
+        }
+
+        float *yn = y + (int64_t)n * Cout * Lo;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = cog * kCO + 16 * m + 4 * kq + r;
+                if (co >= Cout) continue;
+                float *yr = yn + (int64_t)co * Lo;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int o = o0 + 64 * wave + 16 * b + col;
+                    if (o < Lo) __builtin_nontemporal_store(acc[m][b][r] + bv[m][r], yr + o);
+                }
+            }
+    }
+}
+
+}  // namespace
+
+// LDS bytes the kernel needs for a geometry (weights + input strip).
+size_t convT1d_f32_lds_bytes(int64_t Cin, int K, int dilation)
+{
+    const int64_t cin4 = (Cin + 3) & ~int64_t(3);
+    const int64_t ksteps = cin4 * K / 4;
+    const int64_t ts = kTO + (int64_t)dilation * (K - 1);
+    int64_t str = ((ts + 63) / 64) * 64 + 16;        // % 64 == 16
+    if (str - 64 >= ts) str -= 64;
+    return (size_t)(4 * ksteps * 64 + cin4 * str) * sizeof(float);
+}
+
+hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
+                              int64_t N, int64_t Cin, int64_t L, int64_t Cout,
+                              int K, int dilation, float *out, hipStream_t stream)
+{
+    const int cin4 = (int)((Cin + 3) & ~int64_t(3));
+    const int64_t Lo = L + (int64_t)dilation * (K - 1);
+    const int tiles_per_n = (int)((Lo + kTO - 1) / kTO);
+    const int64_t ntiles = N * tiles_per_n;
+    const int64_t ts = kTO + (int64_t)dilation * (K - 1);
+    int64_t str = ((ts + 63) / 64) * 64 + 16;
+    if (str - 64 >= ts) str -= 64;
+    const size_t lds = convT1d_f32_lds_bytes(Cin, K, dilation);
+    hipError_t e = hipFuncSetAttribute((const void *)convT1d_f32_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int per_cu = lds <= 80 * 1024 ? 2 : 1;
+    int64_t gx = (int64_t)cus * per_cu;
+    if (gx > ntiles) gx = ntiles;
+    const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
+    hipLaunchKernelGGL(convT1d_f32_kernel, dim3((unsigned)gx, gy), dim3(kThreads), lds, stream,
+                       x, w, bias, (int)Cin, cin4, (int)L, (int)Cout, K, dilation, (int)Lo,
+                       tiles_per_n, (int)ntiles, (int)str, out);
+    return hipGetLastError();
+}
+
+}  // namespace ct

@@ -1,0 +1,253 @@
+// ct_api.hip - the extern "C" boundary declared in include/ct.h.
+//
+// Each entry point validates every argument on the host first (no HIP call
+// happens before a request is accepted), then calls one launcher from the
+// kernel files and maps a launch error to CT_EHIP.
+#include <cstdarg>
+#include <initializer_list>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "ct.h"
+#include "ct_internal.h"
+
+namespace ct {
+size_t convT1d_f32_lds_bytes(int64_t Cin, int K, int dilation);
+}
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+constexpr size_t kLdsMax = 160 * 1024;      // gfx950 LDS per workgroup
+
+thread_local char g_err[512] = "";
+
+ct_status fail(ct_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+ct_status ok()
+{
+    g_err[0] = '\0';
+    return CT_OK;
+}
+
+// a * b into *r; false on overflow or negative operands.
+bool mul(int64_t a, int64_t b, int64_t *r)
+{
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *r = a * b;
+    return true;
+}
+
+bool prod(std::initializer_list<int64_t> v, int64_t *r)
+{
+    int64_t p = 1;
+    for (int64_t t : v)
+        if (!mul(p, t, &p)) return false;
+    *r = p;
+    return true;
+}
+
+bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
+{
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int64_t floor_div(int64_t a, int64_t b)
+{
+    int64_t q = a / b;
+    if ((a % b != 0) && (a < 0)) --q;
+    return q;
+}
+
+int dtype_size(int dt) { return dt == CT_F32 ? 4 : dt == CT_BF16 ? 2 : 0; }
+
+ct_status hip_status(hipError_t e, const char *what)
+{
+    if (e == hipSuccess) return ok();
+    return fail(CT_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ct_convT_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad,
+                         int64_t out_pad, int64_t dilation)
+{
+    return (in - 1) * stride - 2 * pad + dilation * (k - 1) + out_pad + 1;
+}
+
+int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad)
+{
+    if (stride == 0) stride = k;
+    if (stride <= 0) return 0;
+    return floor_div(in + 2 * pad - k, stride) + 1;
+}
+
+const char *ct_status_str(int status)
+{
+    switch (status) {
+    case CT_OK: return "CT_OK";
+    case CT_EINVAL: return "CT_EINVAL";
+    case CT_EUNSUPPORTED: return "CT_EUNSUPPORTED";
+    case CT_EHIP: return "CT_EHIP";
+    default: return "CT_UNKNOWN_STATUS";
+    }
+}
+
+const char *ct_last_error(void) { return g_err; }
+
+const char *ct_version(void) { return "transposed_conv_pooling_amd 0.1.0 (gfx950)"; }
+
+ct_status ct_convT3d_scale_pool_bias(
+    const void *x, int x_dtype, const void *w, int w_dtype,
+    const float *conv_bias, const float *bias, float scale1, float scale2,
+    int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout,
+    int k, int stride, int pad, int out_pad, int pool_k, int pool_s,
+    float *out, void *stream)
+{
+    if (!x || !w || !out)
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: x, w and out must be non-null");
+    const int xs = dtype_size(x_dtype), ws = dtype_size(w_dtype);
+    if (!xs || !ws)
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: unknown dtype (%d, %d)", x_dtype, w_dtype);
+    if (N < 1 || Cin < 1 || D < 1 || H < 1 || W < 1 || Cout < 1)
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: sizes must be >= 1 (N=%lld Cin=%lld D=%lld H=%lld W=%lld Cout=%lld)",
+                    (long long)N, (long long)Cin, (long long)D, (long long)H, (long long)W, (long long)Cout);
+    if (k < 1 || stride < 1 || pad < 0 || out_pad < 0 || pool_k < 1 || pool_s < 0)
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: invalid geometry k=%d stride=%d pad=%d out_pad=%d pool_k=%d pool_s=%d",
+                    k, stride, pad, out_pad, pool_k, pool_s);
+    const int ps = pool_s == 0 ? pool_k : pool_s;
+    int64_t od[3], pd[3];
+    const int64_t in[3] = {D, H, W};
+    for (int i = 0; i < 3; ++i) {
+        od[i] = ct_convT_out_len(in[i], k, stride, pad, out_pad, 1);
+        pd[i] = od[i] > 0 ? ct_pool_out_len(od[i], pool_k, ps, 0) : 0;
+        if (pd[i] <= 0)
+            return fail(CT_EINVAL, "convT3d_scale_pool_bias: empty output along axis %d (input %lld -> conv %lld -> pool %lld)",
+                        i, (long long)in[i], (long long)od[i], (long long)pd[i]);
+    }
+    if (k != 3 || stride != 2 || pad != 1 || out_pad != 0 || pool_k != 2 || ps != 2)
+        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: only k=3 stride=2 pad=1 out_pad=0 pool 2/2 is implemented");
+    if (x_dtype != w_dtype)
+        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: x and w dtypes must match");
+    if (!aligned(x, xs) || !aligned(w, ws) || !aligned(out, 4) ||
+        (conv_bias && !aligned(conv_bias, 4)) || (bias && !aligned(bias, 4)))
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: misaligned pointer");
+    int64_t nx, nw, no;
+    if (!prod({N, Cin, D, H, W, (int64_t)xs}, &nx) || !prod({Cin, Cout, 27, (int64_t)ws}, &nw) ||
+        !prod({N, Cout, pd[0], pd[1], pd[2], 4}, &no))
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: tensor size overflows");
+    // kernel index limits
+    const int64_t wblocks = (pd[2] + 15) / 16;
+    int64_t nmb;
+    if (!prod({N, pd[0], pd[1], wblocks}, &nmb) || nmb > kI32Max / 8 || D * H * W > kI32Max ||
+        Cout > 65535 * 16)
+        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: problem too large for one launch");
+    if (x_dtype == CT_F32 && Cin > 128)
+        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: fp32 path supports Cin <= 128");
+    if (x_dtype == CT_BF16 && (Cin > 256))
+        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: bf16 path supports Cin <= 256");
+    if (overlap(out, no, x, nx) || overlap(out, no, w, nw) ||
+        overlap(out, no, conv_bias, Cout * 4) || overlap(out, no, bias, Cout * 4))
+        return fail(CT_EINVAL, "convT3d_scale_pool_bias: out overlaps an input");
+
+    hipError_t e;
+    if (x_dtype == CT_F32)
+        e = ct::launch_fused3d_f32((const float *)x, (const float *)w, conv_bias, bias, scale1,
+                                   scale2, N, Cin, D, H, W, Cout, out, (hipStream_t)stream);
+    else
+        e = ct::launch_fused3d_bf16((const uint16_t *)x, (const uint16_t *)w, conv_bias, bias,
+                                    scale1, scale2, N, Cin, D, H, W, Cout, out,
+                                    (hipStream_t)stream);
+    return hip_status(e, "convT3d_scale_pool_bias launch");
+}
+
+ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                       int k, int stride, int pad, int count_include_pad, float *out,
+                       void *stream)
+{
+    if (!x || !out) return fail(CT_EINVAL, "avgpool3d: x and out must be non-null");
+    if (N < 1 || C < 1 || D < 1 || H < 1 || W < 1)
+        return fail(CT_EINVAL, "avgpool3d: sizes must be >= 1");
+    if (k < 1 || stride < 0 || pad < 0 || 2 * pad > k ||
+        (count_include_pad != 0 && count_include_pad != 1))
+        return fail(CT_EINVAL, "avgpool3d: invalid geometry k=%d stride=%d pad=%d count_include_pad=%d "
+                    "(pad must be <= k/2)", k, stride, pad, count_include_pad);
+    const int s = stride == 0 ? k : stride;
+    int64_t o[3];
+    const int64_t in[3] = {D, H, W};
+    for (int i = 0; i < 3; ++i) {
+        o[i] = ct_pool_out_len(in[i], k, s, pad);
+        if (o[i] <= 0)
+            return fail(CT_EINVAL, "avgpool3d: empty output along axis %d", i);
+    }
+    if (k != 3 || s != 2 || pad != 1 || count_include_pad != 1)
+        return fail(CT_EUNSUPPORTED, "avgpool3d: only k=3 stride=2 pad=1 count_include_pad=1 is implemented");
+    if (!aligned(x, 4) || !aligned(out, 4)) return fail(CT_EINVAL, "avgpool3d: misaligned pointer");
+    int64_t nx, no, slice;
+    if (!prod({N, C, D, H, W, 4}, &nx) || !prod({N, C, o[0], o[1], o[2], 4}, &no) ||
+        !prod({D, H, W}, &slice))
+        return fail(CT_EINVAL, "avgpool3d: tensor size overflows");
+    const int64_t hgroups = (o[1] + 15) / 16, dchunks = (o[0] + 15) / 16, wchunks = (o[2] + 127) / 128;
+    int64_t nwg;
+    if (slice > kI32Max || !prod({N, C, hgroups, dchunks, wchunks}, &nwg) || nwg > kI32Max)
+        return fail(CT_EUNSUPPORTED, "avgpool3d: problem too large for one launch");
+    if (overlap(out, no, x, nx)) return fail(CT_EINVAL, "avgpool3d: out overlaps x");
+    hipError_t e = ct::launch_avgpool3d_k3s2p1(x, N * C, D, H, W, out, (hipStream_t)stream);
+    return hip_status(e, "avgpool3d launch");
+}
+
+ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, const float *bias,
+                     int64_t N, int64_t Cin, int64_t L, int64_t Cout, int K, int stride, int pad,
+                     int dilation, int out_pad, float *out, void *stream)
+{
+    if (!x || !w || !out) return fail(CT_EINVAL, "convT1d: x, w and out must be non-null");
+    const int xs = dtype_size(x_dtype), ws = dtype_size(w_dtype);
+    if (!xs || !ws) return fail(CT_EINVAL, "convT1d: unknown dtype (%d, %d)", x_dtype, w_dtype);
+    if (N < 1 || Cin < 1 || L < 1 || Cout < 1) return fail(CT_EINVAL, "convT1d: sizes must be >= 1");
+    if (K < 1 || stride < 1 || pad < 0 || dilation < 1 || out_pad < 0)
+        return fail(CT_EINVAL, "convT1d: invalid geometry K=%d stride=%d pad=%d dilation=%d out_pad=%d",
+                    K, stride, pad, dilation, out_pad);
+    const int64_t Lo = ct_convT_out_len(L, K, stride, pad, out_pad, dilation);
+    if (Lo <= 0) return fail(CT_EINVAL, "convT1d: empty output (L_out=%lld)", (long long)Lo);
+    if (stride != 1 || pad != 0 || out_pad != 0)
+        return fail(CT_EUNSUPPORTED, "convT1d: only stride=1 pad=0 out_pad=0 is implemented");
+    if (x_dtype != CT_F32 || w_dtype != CT_F32)
+        return fail(CT_EUNSUPPORTED, "convT1d: only fp32 x and w are implemented");
+    if (!aligned(x, 4) || !aligned(w, 4) || !aligned(out, 4) || (bias && !aligned(bias, 4)))
+        return fail(CT_EINVAL, "convT1d: misaligned pointer");
+    int64_t nx, nw, no;
+    if (!prod({N, Cin, L, 4}, &nx) || !prod({Cin, Cout, (int64_t)K, 4}, &nw) ||
+        !prod({N, Cout, Lo, 4}, &no))
+        return fail(CT_EINVAL, "convT1d: tensor size overflows");
+    const int64_t tiles = (Lo + 255) / 256;
+    int64_t ntiles;
+    if (Lo > kI32Max - 256 || !prod({N, tiles}, &ntiles) || ntiles > kI32Max ||
+        (Cout + 63) / 64 > 65535 || Cin > 4096 || K > 4096 ||
+        (int64_t)dilation * (K - 1) > 65536)
+        return fail(CT_EUNSUPPORTED, "convT1d: problem too large for one launch");
+    if (ct::convT1d_f32_lds_bytes(Cin, K, dilation) > kLdsMax)
+        return fail(CT_EUNSUPPORTED, "convT1d: Cin*K and dilation*(K-1) too large for LDS "
+                    "(needs %zu bytes)", ct::convT1d_f32_lds_bytes(Cin, K, dilation));
+    if (overlap(out, no, x, nx) || overlap(out, no, w, nw) || overlap(out, no, bias, Cout * 4))
+        return fail(CT_EINVAL, "convT1d: out overlaps an input");
+    hipError_t e = ct::launch_convT1d_f32((const float *)x, (const float *)w, bias, N, Cin, L,
+                                          Cout, K, dilation, out, (hipStream_t)stream);
+    return hip_status(e, "convT1d launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// ct_internal.h - launchers shared between the C-ABI shim (ct_api.hip) and
+// the kernel files.  Every launcher assumes its arguments were validated by
+// the shim: sizes positive, pointers non-null and aligned, geometry one the
+// kernel implements, and all per-launch index ranges within int32 where the
+// kernel says so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ct {
+
+// Fused ConvTranspose3d(k3, s2, p1) -> *s1 -> AvgPool3d(2) -> +bias -> *s2,
+// fp32 x and w.  Output [N, Cout, D-1, H-1, W-1].
+hipError_t launch_fused3d_f32(const float *x, const float *w,
+                              const float *conv_bias, const float *bias,
+                              float s1, float s2, int64_t N, int64_t Cin,
+                              int64_t D, int64_t H, int64_t W, int64_t Cout,
+                              float *out, hipStream_t stream);
+
+// Same chain with bf16 x and w (fp32 accumulation and output).
+hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w,
+                               const float *conv_bias, const float *bias,
+                               float s1, float s2, int64_t N, int64_t Cin,
+                               int64_t D, int64_t H, int64_t W, int64_t Cout,
+                               float *out, hipStream_t stream);
+
+// AvgPool3d(k3, s2, p1), divisor 27, over NC independent [D][H][W] slices.
+hipError_t launch_avgpool3d_k3s2p1(const float *x, int64_t NC, int64_t D,
+                                   int64_t H, int64_t W, float *out,
+                                   hipStream_t stream);
+
+// ConvTranspose1d, stride 1, pad 0, any K and dilation, fp32.
+hipError_t launch_convT1d_f32(const float *x, const float *w,
+                              const float *bias, int64_t N, int64_t Cin,
+                              int64_t L, int64_t Cout, int K, int dilation,
+                              float *out, hipStream_t stream);
+
+// Workgroup index remapped so that each XCD (blocks are dealt to the 8 XCDs
+// round-robin) works on one contiguous range of logical tiles: neighbouring
+// tiles then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks)
+{
+    constexpr int64_t kXcd = 8;
+    const int64_t per = nblocks / kXcd;          // full rounds
+    const int64_t rem = nblocks - per * kXcd;    // XCDs that get one extra
+    const int64_t xcd = bid % kXcd;
+    const int64_t idx = bid / kXcd;
+    // XCD x owns logical tiles [start(x), start(x) + per + (x < rem))
+    const int64_t start = xcd * per + (xcd < rem ? xcd : rem);
+    return start + idx;
+}
+
+}  // namespace ct
