@@ -100,7 +100,11 @@ CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pa
  *
  * Implemented: k = 3, stride = 2, pad = 1, out_pad = 0, pool_k = 2,
  * pool_s = 2 (or 0, meaning pool_k), with (x_dtype, w_dtype) = (CT_F32,
- * CT_F32) or (CT_BF16, CT_BF16); accumulation and output are fp32.
+ * CT_F32) for Cin <= 128, or (CT_BF16, CT_BF16) for Cin <= 32, W a
+ * multiple of 8 up to 4096 and x 16-byte aligned (the kernel reads x in
+ * 16-byte pieces); accumulation and output are fp32.  The bf16 path represents the summed
+ * filter as a bf16 hi + lo pair, so its result matches an fp32 computation
+ * on the same bf16 inputs to ~2^-17 relative per term.
  * Other geometry -> CT_EUNSUPPORTED.  D, H or W equal to 1 gives an empty
  * output -> CT_EINVAL.
  */

@@ -97,6 +97,10 @@ def fused(**kw):
     (dict(out=FAKE + 64), ct.CT_EINVAL),            # out overlaps x
     (dict(out=FAKE2 + 4), ct.CT_EINVAL),            # out overlaps w
     (dict(Cin=129), ct.CT_EUNSUPPORTED),            # fp32 LDS limit
+    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, W=20), ct.CT_EUNSUPPORTED),   # bf16: W % 8
+    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, Cin=33), ct.CT_EUNSUPPORTED),
+    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, x=FAKE + 2), ct.CT_EUNSUPPORTED),  # bf16 x not 16B aligned
+    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, x=FAKE + 1), ct.CT_EINVAL),
     (dict(N=1 << 40), ct.CT_EUNSUPPORTED),          # beyond one launch's index range
     (dict(N=1 << 60), ct.CT_EINVAL),                # byte size overflows int64
 ])

@@ -140,6 +140,58 @@ def test_fused_f32_nan_propagates_locally(dev):
     assert np.array_equal(nan, exp)
 
 
+# ------------------------------------------------------------ fused bf16 ----
+FUSED_BF16 = [
+    # N, Cin, Cout, D, H, W   (W a multiple of 8, Cin <= 32)
+    (1, 8, 16, 2, 2, 8),
+    (2, 32, 64, 3, 5, 32),
+    (1, 5, 20, 4, 6, 16),      # Cin8 = 8
+    (1, 17, 70, 3, 4, 24),     # Cin8 = 24, two channel groups, ragged Cout
+    (2, 12, 64, 5, 3, 40),     # Cin8 = 16, three voxel blocks per row
+    (1, 32, 8, 2, 9, 64),
+]
+
+
+def bf16_round(a):
+    return synth.bf16_bits_to_f32(synth.to_bf16_bits(a)).reshape(a.shape)
+
+
+@pytest.mark.parametrize("shape", FUSED_BF16, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("with_cb", [False, True], ids=["nocb", "cb"])
+def test_fused_bf16_small(dev, shape, with_cb):
+    N, Cin, Cout, D, H, W = shape
+    log(f"fused bf16 {shape} cb={with_cb}")
+    seed = 4000 + sum(shape)
+    x = bf16_round(synth.normal(seed, 0, (N, Cin, D, H, W)))
+    bound = 1.0 / np.sqrt(Cin * 27)
+    w = bf16_round(synth.uniform(seed, 1, (Cin, Cout, 3, 3, 3), -bound, bound))
+    b = synth.normal(seed, 2, (Cout,))
+    cb = synth.normal(seed, 3, (Cout,)) if with_cb else None
+    got = run_fused(dev, x, w, cb, b, 0.5, 1.0, dtype="bf16")
+    ref = oracle.convT3d_scale_pool_bias(x, w, cb, b, 0.5, 1.0)
+    assert_close(got, ref, BF16_TOL, f"fused bf16 {shape}")
+    # the hi/lo filter split keeps the result far inside the bf16 tolerance
+    assert_close(got, ref, (1e-4, 1e-4), f"fused bf16 {shape} (tight)")
+
+
+def test_fused_bf16_c5_full_sampled(dev):
+    """Full-size bf16 [16,32,16,32,32] -> [16,64,15,31,31]; batch items 0, 9, 15
+    recomputed by the oracle from the same bf16 values, plus finiteness."""
+    wl = synth.WORKLOADS["c5"]
+    log(wl.description)
+    t = synth.make_inputs(wl)
+    xg = torch.from_numpy(t["x_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    wg = torch.from_numpy(t["w_bits"].view(np.int16)).to(dev).view(torch.bfloat16)
+    out = nan_like((16, 64, 15, 31, 31), dev)
+    ct.ct_convT3d_scale_pool_bias(xg, wg, None, torch.from_numpy(t["bias"]).to(dev),
+                                  0.5, 1.0, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    for n in (0, 9, 15):
+        ref = oracle.convT3d_scale_pool_bias(t["x"][n:n + 1], t["w"], None, t["bias"], 0.5, 1.0)
+        assert_close(out[n:n + 1].cpu().numpy(), ref, BF16_TOL, f"c5 n={n}")
+
+
 # ------------------------------------------------------------ avgpool3d ----
 POOL_SMALL = [
     (1, 1, 1, 1, 1),

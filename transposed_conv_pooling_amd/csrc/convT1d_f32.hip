@@ -131,7 +131,7 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int o = o0 + 64 * wave + 16 * b + col;
-                    if (o < Lo) __builtin_nontemporal_store(acc[m][b][r] + bv[m][r], yr + o);
+                    if (o < Lo) yr[o] = acc[m][b][r] + bv[m][r];
                 }
             }
     }

@@ -14,6 +14,7 @@
 
 namespace ct {
 size_t convT1d_f32_lds_bytes(int64_t Cin, int K, int dilation);
+size_t fused3d_bf16_lds_bytes(int64_t Cin, int64_t W);
 }
 
 namespace {
@@ -159,8 +160,12 @@ ct_status ct_convT3d_scale_pool_bias(
         return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: problem too large for one launch");
     if (x_dtype == CT_F32 && Cin > 128)
         return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: fp32 path supports Cin <= 128");
-    if (x_dtype == CT_BF16 && (Cin > 256))
-        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: bf16 path supports Cin <= 256");
+    if (x_dtype == CT_BF16) {
+        const size_t lb = ct::fused3d_bf16_lds_bytes(Cin, W);
+        if (Cin > 32 || W % 8 != 0 || !aligned(x, 16) || lb == 0 || lb > kLdsMax)
+            return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: bf16 path needs Cin <= 32, "
+                        "W a multiple of 8 (W <= 4096) and a 16-byte aligned x");
+    }
     if (overlap(out, no, x, nx) || overlap(out, no, w, nw) ||
         overlap(out, no, conv_bias, Cout * 4) || overlap(out, no, bias, Cout * 4))
         return fail(CT_EINVAL, "convT3d_scale_pool_bias: out overlaps an input");

@@ -138,7 +138,7 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
                     float v = acc[r] * 0.125f;
                     v = (v + cbv[r]) * s1;
                     v = (v + bv[r]) * s2;
-                    __builtin_nontemporal_store(v, on + (int64_t)co * pplane);
+                    on[(int64_t)co * pplane] = v;   // plain store: L2 merges the partial lines
                 }
             }
         }
