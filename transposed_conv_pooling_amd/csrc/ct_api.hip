@@ -155,7 +155,8 @@ ct_status ct_convT3d_scale_pool_bias(
     // kernel index limits
     const int64_t wblocks = (pd[2] + 15) / 16;
     int64_t nmb;
-    if (!prod({N, pd[0], pd[1], wblocks}, &nmb) || nmb > kI32Max / 8 || D * H * W > kI32Max ||
+    if (!prod({N, pd[0], pd[1], wblocks}, &nmb) || nmb > kI32Max / 8 || Cin * D * H * W > kI32Max ||
+        Cout * pd[0] * pd[1] * pd[2] > kI32Max ||
         Cout > 65535 * 16)
         return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: problem too large for one launch");
     if (x_dtype == CT_F32 && Cin > 128)

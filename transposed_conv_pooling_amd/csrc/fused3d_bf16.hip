@@ -6,7 +6,9 @@
 // is S/8 with S = sum_ci sum_{a,b,c in {0,1}} x[ci,d+a,h+b,w+c] *
 // Weff[ci,co,abc], Weff the per-tap sums of the 27 weights (passages on the
 // stride-2 parity rule and on grouping the 27 terms by input tap), then the
-// model's epilogue ((S/8 + conv_bias)*scale1 + bias)*scale2.
+// model's epilogue ((S/8 + conv_bias)*scale1 + bias)*scale2, evaluated in the
+// folded form S*(scale1*scale2/8) + (conv_bias*scale1 + bias)*scale2 the page
+// derives (one fma per output; within an ulp or two of the literal order).
 //
 // Precision.  Weff is summed in fp32 from the bf16 weights and split as
 // Weff = hi + lo with hi = bf16(Weff), lo = bf16(Weff - hi); both halves go
@@ -22,11 +24,13 @@
 // 8 kappas are 8 consecutive channels at one tap: with the input slab held
 // channels-last in LDS that is one 16-byte ds_read_b128.
 //  * Workgroup = 8 waves, persistent, one 64-channel output group
-//    (blockIdx.y).  Prologue: stage the raw weights into LDS (coalesced),
-//    form Weff and its hi/lo split once, write them in fragment order, and
-//    load each wave's fragments (2 output-channel blocks x all k-steps x
-//    hi/lo) into registers for the whole kernel.
-//  * Tile = (n, d, 2 pooled rows): the input slab x[n, :, d..d+1, h0..h0+2, :]
+//    (blockIdx.y).  Prologue: the raw weights come in with coalesced 16-byte
+//    loads (all chunks in flight at once) and are staged in LDS; every
+//    thread forms Weff and its hi/lo split for two (ci, co) pairs into a
+//    [half][tap][co][ci] table, from which each wave loads its fragments
+//    (2 output-channel blocks x all k-steps x hi/lo) into registers for the
+//    whole kernel.
+//  * Tile = (n, d, 4 pooled rows): the input slab x[n, :, d..d+1, h0..h0+4, :]
 //    is transposed to [plane][row][w][ci] in LDS; the next tile's slab is
 //    prefetched into registers while the current one is computed.
 //  * Wave = (voxel-block slot s = w%4, channel pair p = w/4): each B read
@@ -46,9 +50,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCoGroup = 64;          // output channels per workgroup
 constexpr int kCiChunk = 16;          // input channels staged per prologue pass
-constexpr int kTH = 2;                // pooled rows per tile
+constexpr int kTH = 4;                // pooled rows per tile
 constexpr int kRows = kTH + 1;        // input rows per plane in a slab
-constexpr int kPrefetch = 2;          // 16-byte slab pieces prefetched per thread
+constexpr int kPrefetch = 2;          // slab pieces (2 channels x 8 w) prefetched per thread
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b)
 {
@@ -64,9 +68,11 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f)
     return (unsigned short)(u >> 16);
 }
 
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Byte sizes of the LDS regions (shared with the launcher).
 __host__ __device__ inline int raw_bytes() { return kCiChunk * kCoGroup * 27 * 2; }
-__host__ __device__ inline int afrag_bytes(int ksteps) { return 4 * ksteps * 2 * 512 * 2; }
+__host__ __device__ inline int afrag_bytes(int ksteps) { return 2 * 8 * kCoGroup * (4 * ksteps + 2) * 2; }
 __host__ __device__ inline int slab_bytes(int W, int cs) { return 2 * kRows * W * cs * 2; }
 // The epilogue constants sit after the larger of the prologue regions and the
 // slab, so neither overwrites them.
@@ -93,36 +99,120 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     unsigned short *raw = lds;                                // prologue: raw weights
     unsigned short *afrag = lds + raw_bytes() / 2;            // prologue: fragments
     unsigned short *slab = lds;                               // main loop: input slab
+    float *epi = reinterpret_cast<float *>(lds_bytes + epi_offset(W, CS));   // [64]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = uniform(tid >> 6);
     const int g = lane >> 4;                 // lane group
     const int col = lane & 15;
     const int slot = wave & 3;               // voxel-block slot
     const int cp = wave >> 2;                // channel-block pair
     const int co0 = blockIdx.y * kCoGroup;
     const int ncog = min(kCoGroup, Cout - co0);
+    const int HW = H * W, DHW = D * HW;      // per-item sizes < 2^31 (checked by the shim)
+    const int64_t pplane = (int64_t)Dp * Hp * Wp;
 
-    // ---- prologue: Weff hi/lo in fragment order ------------------------
-    for (int c0 = 0; c0 < Cin8; c0 += kCiChunk) {
+    // ---- this workgroup's tiles, and the first slab's loads ---------------
+    const int t_begin = uniform(blockIdx.x * tiles_per_wg);
+    const int t_end = uniform(min(t_begin + tiles_per_wg, ntiles));
+    int hp, d, n;
+    {
+        int t = t_begin;
+        hp = uniform(t % hpairs); t /= hpairs;
+        d = uniform(t % Dp);
+        n = uniform(t / Dp);
+    }
+    // tile-invariant staging plan: piece q = ((a*kRows + row)*W8 + w8)*(Cin8/2) + cpair
+    // covers channels 2*cpair, 2*cpair+1 at x[.., d+a, h0+row, 8*w8 .. 8*w8+7]
+    const int W8 = W >> 3;
+    const int npieces = 2 * kRows * W8 * (Cin8 / 2);
+    int src_off[kPrefetch], dst_off[kPrefetch], prow[kPrefetch], pci[kPrefetch];
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) {
+        const int q = tid + i * kThreads;
+        const int cpair = q % (Cin8 / 2);
+        int t = q / (Cin8 / 2);
+        const int w8 = t % W8;
+        t /= W8;
+        const int row = t % kRows, a = t / kRows;
+        pci[i] = 2 * cpair;
+        src_off[i] = 2 * cpair * DHW + a * HW + row * W + 8 * w8;
+        dst_off[i] = ((a * kRows + row) * W + 8 * w8) * CS + 2 * cpair;
+        prow[i] = q < npieces ? row : 1 << 30;
+    }
+    u16x8 pre0[kPrefetch], pre1[kPrefetch];
+    auto fetch = [&](int n_, int d_, int hp_) {
+        const int h0 = kTH * hp_;
+        const unsigned short *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i) {
+            const bool rok = h0 + prow[i] < H;
+            pre0[i] = (rok && pci[i] < Cin) ? *reinterpret_cast<const u16x8 *>(xb + src_off[i])
+                                            : (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
+            pre1[i] = (rok && pci[i] + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(xb + src_off[i] + DHW)
+                                                : (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    };
+    auto put = [&](int off, u16x8 v0, u16x8 v1) {
+        unsigned *dst = reinterpret_cast<unsigned *>(slab + off);    // 2 channels per dword
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            dst[k * (CS / 2)] = (unsigned)v0[k] | ((unsigned)v1[k] << 16);
+    };
+    if (t_begin < t_end) fetch(n, d, hp);
+
+    // ---- prologue: Weff hi/lo -------------------------------------------
+    // raw weights of a 16-channel chunk: raw[cil][col][27]; weffT[h][tap][col][ci]
+    // (row stride Cin8 + 2 u16 = an odd number of dwords: conflict-free writes)
+    constexpr int WS = Cin8 + 2;
+    unsigned short *weffT = lds + raw_bytes() / 2;
+    constexpr int kChunks = (Cin8 + kCiChunk - 1) / kCiChunk;
+    constexpr int kVecPerThread = (kCiChunk * kCoGroup * 27 / 8 + kThreads - 1) / kThreads;
+    const bool vec_w = (Cout == kCoGroup) && (Cin % kCiChunk == 0) && ((((uintptr_t)w) & 15) == 0);
+    u16x8 wreg[kChunks][kVecPerThread];
+    if (vec_w) {              // both chunks' loads in flight at once
+#pragma unroll
+        for (int ch = 0; ch < kChunks; ++ch)
+#pragma unroll
+            for (int i = 0; i < kVecPerThread; ++i) {
+                const int e = tid + i * kThreads;
+                if (e < kCiChunk * kCoGroup * 27 / 8 && (ch + 1) * kCiChunk <= Cin)
+                    wreg[ch][i] = reinterpret_cast<const u16x8 *>(w + (int64_t)ch * kCiChunk * kCoGroup * 27)[e];
+            }
+    }
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+        const int c0 = ch * kCiChunk;
         const int nci = min(kCiChunk, Cin - c0);
-        __syncthreads();
-        for (int e = tid; e < kCiChunk * kCoGroup * 27; e += kThreads) {
-            const int pr = e / 27, k = e - pr * 27;
-            const int cil = pr / kCoGroup, col_ = pr - cil * kCoGroup;
-            raw[e] = (cil < nci && col_ < ncog)
-                ? w[((int64_t)(c0 + cil) * Cout + co0 + col_) * 27 + k] : (unsigned short)0;
+        __syncthreads();                               // previous chunk's raw consumed
+        if (vec_w) {
+#pragma unroll
+            for (int i = 0; i < kVecPerThread; ++i) {
+                const int e = tid + i * kThreads;
+                if (e < kCiChunk * kCoGroup * 27 / 8)
+                    reinterpret_cast<u16x8 *>(raw)[e] = wreg[ch][i];
+            }
+        } else {
+            const int run = ncog * 27;
+            for (int cil = 0; cil < kCiChunk; ++cil) {
+                unsigned short *rd = raw + cil * kCoGroup * 27;
+                const int64_t base = ((int64_t)(c0 + cil) * Cout + co0) * 27;
+                const int n_in = cil < nci ? run : 0;
+                for (int e = tid; e < kCoGroup * 27; e += kThreads)
+                    rd[e] = e < n_in ? w[base + e] : (unsigned short)0;
+            }
         }
         __syncthreads();
+        // pairs (cil, col), output channel fastest: raw reads 27 u16 apart
         for (int pr = tid; pr < kCiChunk * kCoGroup; pr += kThreads) {
-            const int cil = pr / kCoGroup, cl = pr - cil * kCoGroup;
+            const int cil = pr / kCoGroup, cl = pr % kCoGroup;
             const int ci = c0 + cil;
             if (ci >= Cin8) continue;
             float wv[27];
 #pragma unroll
             for (int k = 0; k < 27; ++k) wv[k] = bf16_to_f32(raw[pr * 27 + k]);
-            // offset 0 pairs with taps {1,2}, offset 1 with tap {0}, per axis
+            // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
             float s1w[9][2];
 #pragma unroll
             for (int r = 0; r < 9; ++r) {
@@ -142,17 +232,14 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                 const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
                 const float we = a ? s2w[0][b][c] : (s2w[1][b][c] + s2w[2][b][c]);
                 const unsigned short hi = f32_to_bf16(we);
-                const unsigned short lo = f32_to_bf16(we - bf16_to_f32(hi));
-                const int kap = tap * Cin8 + ci;
-                const int j = kap >> 5, gg = (kap >> 3) & 3, e8 = kap & 7;
-                const int cb = cl >> 4, l = gg * 16 + (cl & 15);
-                const int base = ((cb * KSTEPS + j) * 2) * 512 + l * 8 + e8;
-                afrag[base] = hi;
-                afrag[base + 512] = lo;
+                weffT[((0 * 8 + tap) * kCoGroup + cl) * WS + ci] = hi;
+                weffT[((1 * 8 + tap) * kCoGroup + cl) * WS + ci] = f32_to_bf16(we - bf16_to_f32(hi));
             }
         }
     }
     __syncthreads();
+    // A fragments: lane (g, l%16) of channel block cb, k-step j, half h holds
+    // Weff_h[ci0 .. ci0+7][co][tap] with kappa = 32j + 8g = tap*Cin8 + ci0
     bf16x8 A[2][KSTEPS][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -160,122 +247,103 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
         for (int j = 0; j < KSTEPS; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const int cb = 2 * cp + i;
-                const u16x8 v = *reinterpret_cast<const u16x8 *>(
-                    afrag + ((cb * KSTEPS + j) * 2 + h) * 512 + lane * 8);
+                const int cl = 16 * (2 * cp + i) + col;
+                const int kap = 32 * j + 8 * g;
+                const int tap = kap / Cin8, ci0 = kap % Cin8;
+                const unsigned *src = reinterpret_cast<const unsigned *>(
+                    weffT + ((h * 8 + tap) * kCoGroup + cl) * WS + ci0);
+                u16x8 v;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const unsigned u = src[q];
+                    v[2 * q] = (unsigned short)(u & 0xFFFFu);
+                    v[2 * q + 1] = (unsigned short)(u >> 16);
+                }
                 A[i][j][h] = __builtin_bit_cast(bf16x8, v);
             }
-    // epilogue constants of this workgroup's channels, kept in LDS
-    float *epi = reinterpret_cast<float *>(lds_bytes + epi_offset(W, CS));   // [2][64]
+    // folded epilogue ((S/8 + cb)*s1 + b)*s2 = S*alpha + beta[co]
+    const float alpha = 0.125f * s1 * s2;
     if (tid < kCoGroup) {
         const int co = co0 + tid;
-        epi[tid] = (conv_bias && co < Cout) ? conv_bias[co] : 0.0f;
-        epi[kCoGroup + tid] = (bias && co < Cout) ? bias[co] : 0.0f;
+        const float cbv = (conv_bias && co < Cout) ? conv_bias[co] : 0.0f;
+        const float bv = (bias && co < Cout) ? bias[co] : 0.0f;
+        epi[tid] = (cbv * s1 + bv) * s2;
+    }
+    // B-fragment slab offsets of this lane: kappa = 32j + 8g -> (tap, ci0)
+    int boff[KSTEPS];
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+        const int kap = 32 * j + 8 * g;
+        const int tap = kap / Cin8, ci0 = kap % Cin8;
+        boff[j] = (((tap >> 2) * kRows + ((tap >> 1) & 1)) * W + (tap & 1)) * CS + ci0;
     }
 
     // ---- main loop over tiles (n, d, pooled row pair) --------------------
-    const int64_t HW = (int64_t)H * W;
-    const int64_t DHW = (int64_t)D * HW;
-    const int64_t pplane = (int64_t)Dp * Hp * Wp;
-    const int W8 = W >> 3;                        // 8-element column groups (W % 8 == 0)
-    const int nq = Cin8 * 2 * kRows * W8;         // 16-byte slab pieces per tile
     const int wblocks = (Wp + 15) / 16;
     const int nvb = kTH * wblocks;                // voxel blocks per tile
-    const int t_begin = blockIdx.x * tiles_per_wg;
-    const int t_end = min(t_begin + tiles_per_wg, ntiles);
+    int vb_hh0 = 0, vb_wb0 = slot;               // first voxel block of this slot
+    while (vb_wb0 >= wblocks) { vb_wb0 -= wblocks; ++vb_hh0; }
 
-    // piece q = ((ci*2 + a)*kRows + row)*W8 + w8 covers x[n, ci, d+a, 2*hp+row, 8*w8 .. 8*w8+7]
-    auto piece_load = [&](int t, int q) -> u16x8 {
-        const int hp = t % hpairs;
-        const int nd = t / hpairs;
-        const int d = nd % Dp, n = nd / Dp;
-        const int w8 = q % W8;
-        int r = q / W8;
-        const int row = r % kRows;
-        r /= kRows;
-        const int a = r & 1, ci = r >> 1;
-        const int h = 2 * hp + row;
-        if (ci >= Cin || h >= H) return (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
-        return *reinterpret_cast<const u16x8 *>(
-            x + (int64_t)n * Cin * DHW + (int64_t)ci * DHW + (int64_t)(d + a) * HW +
-            (int64_t)h * W + 8 * w8);
-    };
-    auto piece_store = [&](int q, u16x8 v) {
-        const int w8 = q % W8;
-        int r = q / W8;
-        const int row = r % kRows;
-        r /= kRows;
-        const int a = r & 1, ci = r >> 1;
-        unsigned short *dst = slab + ((a * kRows + row) * W + 8 * w8) * CS + ci;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) dst[k * CS] = v[k];
-    };
-
-    u16x8 pre[kPrefetch];
-    if (t_begin < t_end) {
-#pragma unroll
-        for (int i = 0; i < kPrefetch; ++i) {
-            const int q = tid + i * kThreads;
-            if (q < nq) pre[i] = piece_load(t_begin, q);
-        }
-    }
     for (int t = t_begin; t < t_end; ++t) {
-        __syncthreads();                           // previous slab consumed
+        const int h0 = kTH * hp;
+        __syncthreads();                           // previous slab consumed (and fragments read)
 #pragma unroll
-        for (int i = 0; i < kPrefetch; ++i) {
-            const int q = tid + i * kThreads;
-            if (q < nq) piece_store(q, pre[i]);
+        for (int i = 0; i < kPrefetch; ++i)
+            if (prow[i] < (1 << 30)) put(dst_off[i], pre0[i], pre1[i]);
+        for (int q = tid + kPrefetch * kThreads; q < npieces; q += kThreads) {
+            const int cpair = q % (Cin8 / 2);
+            int tt = q / (Cin8 / 2);
+            const int w8 = tt % W8;
+            tt /= W8;
+            const int row = tt % kRows, a = tt / kRows;
+            const int ci = 2 * cpair;
+            const unsigned short *src = x + (int64_t)n * Cin * DHW + (int64_t)d * HW +
+                                        (int64_t)h0 * W + ci * DHW + a * HW + row * W + 8 * w8;
+            const bool rok = h0 + row < H;
+            const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+            const u16x8 v0 = (rok && ci < Cin) ? *reinterpret_cast<const u16x8 *>(src) : z;
+            const u16x8 v1 = (rok && ci + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(src + DHW) : z;
+            put(((a * kRows + row) * W + 8 * w8) * CS + ci, v0, v1);
         }
-        for (int q = tid + kPrefetch * kThreads; q < nq; q += kThreads)
-            piece_store(q, piece_load(t, q));
         __syncthreads();
-        if (t + 1 < t_end) {
-#pragma unroll
-            for (int i = 0; i < kPrefetch; ++i) {
-                const int q = tid + i * kThreads;
-                if (q < nq) pre[i] = piece_load(t + 1, q);
-            }
-        }
+        int hp2 = hp + 1, d2 = d, n2 = n;
+        if (hp2 == hpairs) { hp2 = 0; if (++d2 == Dp) { d2 = 0; ++n2; } }
+        if (t + 1 < t_end) fetch(n2, d2, hp2);
 
-        const int hp = t % hpairs;
-        const int nd = t / hpairs;
-        const int d = nd % Dp, n = nd / Dp;
+        float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
+        int hh = vb_hh0, wb = vb_wb0;
         for (int vb = slot; vb < nvb; vb += 4) {
-            const int hh = vb / wblocks, wb = vb - hh * wblocks;
-            const int h = 2 * hp + hh;
+            const int h = h0 + hh;
             const int wv = wb * 16 + col;
             const bool valid = (wv < Wp) && (h < Hp);
             const int wc = min(wv, Wp - 1);
-            v4f acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
+            const unsigned short *sb = slab + (hh * W + wc) * CS;
+            v4f a0h = {0.0f, 0.0f, 0.0f, 0.0f}, a1h = a0h, a0l = a0h, a1l = a0h;
 #pragma unroll
             for (int j = 0; j < KSTEPS; ++j) {
-                const int kap = 32 * j + 8 * g;
-                const int tap = kap / Cin8, ci0 = kap - tap * Cin8;
-                const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
-                const u16x8 bvv = *reinterpret_cast<const u16x8 *>(
-                    slab + ((a * kRows + hh + b) * W + wc + c) * CS + ci0);
-                const bf16x8 B = __builtin_bit_cast(bf16x8, bvv);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][0], B, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][0], B, acc1, 0, 0, 0);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][1], B, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][1], B, acc1, 0, 0, 0);
+                const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(sb + boff[j]));
+                a0h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][0], B, a0h, 0, 0, 0);
+                a1h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][0], B, a1h, 0, 0, 0);
+                a0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][1], B, a0l, 0, 0, 0);
+                a1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][1], B, a1l, 0, 0, 0);
             }
             if (valid) {
-                float *on = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h) * Wp + wv;
+                float *on = ob + hh * Wp + wv;        // per-item offsets fit in int32 (shim)
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int cl = 16 * (2 * cp + i) + 4 * g + r;
                         if (co0 + cl < Cout) {
-                            float v = (i ? acc1[r] : acc0[r]) * 0.125f;
-                            v = (v + epi[cl]) * s1;
-                            v = (v + epi[kCoGroup + cl]) * s2;
-                            on[(int64_t)(co0 + cl) * pplane] = v;
+                            const float sum = i ? (a1h[r] + a1l[r]) : (a0h[r] + a0l[r]);
+                            on[(co0 + cl) * (int)pplane] = __builtin_fmaf(sum, alpha, epi[cl]);
                         }
                     }
             }
+            wb += 4;
+            while (wb >= wblocks) { wb -= wblocks; ++hh; }
         }
+        hp = hp2; d = d2; n = n2;
     }
 }
 
