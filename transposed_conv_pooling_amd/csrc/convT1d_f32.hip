@@ -137,6 +137,132 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
     }
 }
 
+// Specialised path: Cin4, K and the dilation known at compile time, so every
+// LDS address is a per-lane base plus an immediate offset and the k-loop
+// carries no index arithmetic.  The input strip of the next tile is loaded
+// (16-byte loads, no divisions) into registers while the current tile
+// computes.  Requires L % 4 == 0 and dil*(K-1) % 4 == 0 (whole float4 pieces
+// are either inside or outside [0, L)) and 16-byte aligned x.
+template <int CIN4, int K, int DIL>
+struct FastGeom {
+    static constexpr int kKsteps = CIN4 * K / 4;
+    static constexpr int kHalo = DIL * (K - 1);
+    static constexpr int kTs = kTO + kHalo;
+    static constexpr int kStr = ((kTs + 63) / 64) * 64 + 16 - (((kTs + 63) / 64) * 64 + 16 - 64 >= kTs ? 64 : 0);
+    static constexpr int kQ = CIN4 * kTs / 4;                    // float4 pieces per strip
+    static constexpr int kQPerThread = (kQ + kThreads - 1) / kThreads;
+    static constexpr int kLdsFloats = 4 * kKsteps * 64 + CIN4 * kStr;
+};
+
+template <int CIN4, int K, int DIL>
+__global__ __launch_bounds__(kThreads, 2)
+void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restrict__ w,
+                             const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
+                             int tiles_per_n, int ntiles, float *__restrict__ y)
+{
+    typedef FastGeom<CIN4, K, DIL> G;
+    typedef float v4f_ __attribute__((ext_vector_type(4)));
+    extern __shared__ float lds[];
+    float *wfrag = lds;                           // [j][lane][m]: 4 m-blocks per 16 bytes
+    float *xs = lds + 4 * G::kKsteps * 64;        // [CIN4][kStr]
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cog = blockIdx.y;
+    const int kq = lane >> 4, col = lane & 15;
+
+    for (int e = threadIdx.x; e < 4 * G::kKsteps * 64; e += kThreads) {
+        const int m = e & 3, l = (e >> 2) & 63, j = e >> 8;
+        const int co = cog * kCO + 16 * m + (l & 15);
+        const int kap = 4 * j + (l >> 4);
+        const int k = kap / CIN4, ci = kap % CIN4;
+        wfrag[e] = (co < Cout && ci < Cin) ? w[((int64_t)ci * Cout + co) * K + k] : 0.0f;
+    }
+    float bv[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = cog * kCO + 16 * m + 4 * kq + r;
+            bv[m][r] = (bias && co < Cout) ? bias[co] : 0.0f;
+        }
+
+    // strip piece q = ci * (kTs/4) + t4 (compile-time divisor)
+    v4f_ pre[G::kQPerThread];
+    auto fetch = [&](int tile) {
+        const int n = tile / tiles_per_n;
+        const int o0 = (tile - n * tiles_per_n) * kTO;
+        const float *xb = x + (int64_t)n * Cin * L + (o0 - G::kHalo);
+#pragma unroll
+        for (int i = 0; i < G::kQPerThread; ++i) {
+            const int q = threadIdx.x + i * kThreads;
+            const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
+            const int pos = o0 - G::kHalo + 4 * t4;
+            pre[i] = (q < G::kQ && ci < Cin && pos >= 0 && pos < L)
+                ? *reinterpret_cast<const v4f_ *>(xb + ci * L + 4 * t4)
+                : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    if ((int)blockIdx.x < ntiles) fetch(blockIdx.x);
+
+    const float *xl = xs + kq * G::kStr + G::kHalo + 64 * wave + col;   // lane's B base
+    const float *al = wfrag + lane * 4;                                   // lane's A base
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int n = tile / tiles_per_n;
+        const int o0 = (tile - n * tiles_per_n) * kTO;
+        __syncthreads();          // previous strip consumed (and weights staged)
+#pragma unroll
+        for (int i = 0; i < G::kQPerThread; ++i) {
+            const int q = threadIdx.x + i * kThreads;
+            if (q < G::kQ) {
+                const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
+                *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * t4) = pre[i];
+            }
+        }
+        __syncthreads();
+        if (tile + (int)gridDim.x < ntiles) fetch(tile + gridDim.x);
+
+        v4f acc[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[m][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+        // kappa = k*CIN4 + ci: outer loop over taps k (one base per tap), inner
+        // over 4-channel groups with immediate LDS offsets
+#pragma unroll 1
+        for (int k = 0; k < K; ++k) {
+            const float *xk = xl - DIL * k;
+            const float *ak = al + k * (CIN4 / 4) * 256;
+#pragma unroll
+            for (int c = 0; c < CIN4 / 4; ++c) {
+                const v4f_ av = *reinterpret_cast<const v4f_ *>(ak + c * 256);
+                float bvv[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) bvv[b] = xk[4 * c * G::kStr + 16 * b];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bvv[b], acc[m][b], 0, 0, 0);
+            }
+        }
+
+        float *yn = y + (int64_t)n * Cout * Lo;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int co = cog * kCO + 16 * m + 4 * kq + r;
+                if (co >= Cout) continue;
+                float *yr = yn + (int64_t)co * Lo;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int o = o0 + 64 * wave + 16 * b + col;
+                    if (o < Lo) yr[o] = acc[m][b][r] + bv[m][r];
+                }
+            }
+    }
+}
+
 }  // namespace
 
 // LDS bytes the kernel needs for a geometry (weights + input strip).
@@ -161,6 +287,29 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
     const int64_t ts = kTO + (int64_t)dilation * (K - 1);
     int64_t str = ((ts + 63) / 64) * 64 + 16;
     if (str - 64 >= ts) str -= 64;
+    if (cin4 == 32 && Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 &&
+        (((uintptr_t)x) & 15) == 0) {
+        typedef FastGeom<32, 5, 3> G;
+        const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
+        hipError_t e = hipFuncSetAttribute((const void *)convT1d_f32_fast_kernel<32, 5, 3>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        int dev = 0, cus = 256, per_cu = 1;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 256;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)convT1d_f32_fast_kernel<32, 5, 3>,
+                                                         kThreads, lds) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
+        int64_t gx = (int64_t)cus * per_cu / gy;
+        if (gx < 1) gx = 1;
+        if (gx > ntiles) gx = ntiles;
+        hipLaunchKernelGGL((convT1d_f32_fast_kernel<32, 5, 3>), dim3((unsigned)gx, gy), dim3(kThreads),
+                           lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout, (int)Lo, tiles_per_n,
+                           (int)ntiles, out);
+        return hipGetLastError();
+    }
     const size_t lds = convT1d_f32_lds_bytes(Cin, K, dilation);
     hipError_t e = hipFuncSetAttribute((const void *)convT1d_f32_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
