@@ -30,9 +30,10 @@
 //    [half][tap][co][ci] table, from which each wave loads its fragments
 //    (2 output-channel blocks x all k-steps x hi/lo) into registers for the
 //    whole kernel.
-//  * Tile = (n, d, 4 pooled rows): the input slab x[n, :, d..d+1, h0..h0+4, :]
-//    is transposed to [plane][row][w][ci] in LDS; the next tile's slab is
-//    prefetched into registers while the current one is computed.
+//  * Tile = (n, d, 8 pooled rows): the input slab x[n, :, d..d+1, h0..h0+8, :]
+//    is transposed to [plane][row][w][ci] in a double-buffered LDS slab.  A
+//    tile's loads are issued two tiles ahead into registers and written to
+//    the spare buffer one tile ahead; one barrier per tile.
 //  * Wave = (voxel-block slot s = w%4, channel pair p = w/4): each B read
 //    feeds 4 MFMAs (2 channel blocks x hi/lo).
 //  * Each workgroup walks a contiguous range of tiles, so neighbouring tiles
@@ -50,9 +51,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCoGroup = 64;          // output channels per workgroup
 constexpr int kCiChunk = 16;          // input channels staged per prologue pass
-constexpr int kTH = 4;                // pooled rows per tile
-constexpr int kRows = kTH + 1;        // input rows per plane in a slab
-constexpr int kPrefetch = 2;          // slab pieces (2 channels x 8 w) prefetched per thread
+constexpr int kPrefetch = 3;          // slab pieces (2 channels x 8 w) prefetched per thread
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b)
 {
@@ -73,16 +72,17 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // Byte sizes of the LDS regions (shared with the launcher).
 __host__ __device__ inline int raw_bytes() { return kCiChunk * kCoGroup * 27 * 2; }
 __host__ __device__ inline int afrag_bytes(int ksteps) { return 2 * 8 * kCoGroup * (4 * ksteps + 2) * 2; }
-__host__ __device__ inline int slab_bytes(int W, int cs) { return 2 * kRows * W * cs * 2; }
+// one slab: 2 planes x (th + 1) rows x W positions x cs channels (u16)
+__host__ __device__ inline int slab_bytes(int th, int W, int cs) { return 2 * (th + 1) * W * cs * 2; }
 // The epilogue constants sit after the larger of the prologue regions and the
-// slab, so neither overwrites them.
-__host__ __device__ inline int epi_offset(int W, int cs)
+// two slabs, so neither overwrites them.
+__host__ __device__ inline int epi_offset(int th, int W, int cs)
 {
-    const int a = raw_bytes() + afrag_bytes(8), b = slab_bytes(W, cs);
+    const int a = raw_bytes() + afrag_bytes(8), b = 2 * slab_bytes(th, W, cs);
     return ((a > b ? a : b) + 15) & ~15;
 }
 
-template <int KSTEPS>
+template <int KSTEPS, int kTH>
 __global__ __launch_bounds__(kThreads)
 void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                          const unsigned short *__restrict__ w,
@@ -94,12 +94,13 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
 {
     constexpr int Cin8 = 4 * KSTEPS;
     constexpr int CS = Cin8 + 8;              // channel stride of a slab position (u16)
+    constexpr int kRows = kTH + 1;            // input rows per plane in a slab
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_bytes[];
     unsigned short *lds = reinterpret_cast<unsigned short *>(lds_bytes);
     unsigned short *raw = lds;                                // prologue: raw weights
     unsigned short *afrag = lds + raw_bytes() / 2;            // prologue: fragments
     unsigned short *slab = lds;                               // main loop: input slab
-    float *epi = reinterpret_cast<float *>(lds_bytes + epi_offset(W, CS));   // [64]
+    float *epi = reinterpret_cast<float *>(lds_bytes + epi_offset(kTH, W, CS));   // [64]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -142,20 +143,22 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
         prow[i] = q < npieces ? row : 1 << 30;
     }
     u16x8 pre0[kPrefetch], pre1[kPrefetch];
+    int pok[kPrefetch];
     auto fetch = [&](int n_, int d_, int hp_) {
         const int h0 = kTH * hp_;
         const unsigned short *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
+        // unconditional loads from valid addresses (x[0..] for masked pieces) so
+        // they all stay in flight; the zero fill happens in put()
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i) {
             const bool rok = h0 + prow[i] < H;
-            pre0[i] = (rok && pci[i] < Cin) ? *reinterpret_cast<const u16x8 *>(xb + src_off[i])
-                                            : (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
-            pre1[i] = (rok && pci[i] + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(xb + src_off[i] + DHW)
-                                                : (u16x8){0, 0, 0, 0, 0, 0, 0, 0};
+            pre0[i] = *reinterpret_cast<const u16x8 *>((rok && pci[i] < Cin) ? xb + src_off[i] : x);
+            pre1[i] = *reinterpret_cast<const u16x8 *>((rok && pci[i] + 1 < Cin) ? xb + src_off[i] + DHW : x);
+            pok[i] = (rok ? 1 : 0) | ((rok && pci[i] < Cin) ? 2 : 0) | ((rok && pci[i] + 1 < Cin) ? 4 : 0);
         }
     };
-    auto put = [&](int off, u16x8 v0, u16x8 v1) {
-        unsigned *dst = reinterpret_cast<unsigned *>(slab + off);    // 2 channels per dword
+    auto put = [&](unsigned short *buf, int off, u16x8 v0, u16x8 v1) {
+        unsigned *dst = reinterpret_cast<unsigned *>(buf + off);     // 2 channels per dword
 #pragma unroll
         for (int k = 0; k < 8; ++k)
             dst[k * (CS / 2)] = (unsigned)v0[k] | ((unsigned)v1[k] << 16);
@@ -284,12 +287,16 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     int vb_hh0 = 0, vb_wb0 = slot;               // first voxel block of this slot
     while (vb_wb0 >= wblocks) { vb_wb0 -= wblocks; ++vb_hh0; }
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int h0 = kTH * hp;
-        __syncthreads();                           // previous slab consumed (and fragments read)
+    // first tile's slab into buffer 0 (its loads were issued before the
+    // prologue), the second tile's loads into registers
+    const int slab_u16 = slab_bytes(kTH, W, CS) / 2;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto put_all = [&](unsigned short *buf, int n_, int d_, int hp_) {
+        const int h0 = kTH * hp_;
 #pragma unroll
         for (int i = 0; i < kPrefetch; ++i)
-            if (prow[i] < (1 << 30)) put(dst_off[i], pre0[i], pre1[i]);
+            if (prow[i] < (1 << 30))
+                put(buf, dst_off[i], (pok[i] & 2) ? pre0[i] : z8, (pok[i] & 4) ? pre1[i] : z8);
         for (int q = tid + kPrefetch * kThreads; q < npieces; q += kThreads) {
             const int cpair = q % (Cin8 / 2);
             int tt = q / (Cin8 / 2);
@@ -297,18 +304,35 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
             tt /= W8;
             const int row = tt % kRows, a = tt / kRows;
             const int ci = 2 * cpair;
-            const unsigned short *src = x + (int64_t)n * Cin * DHW + (int64_t)d * HW +
+            const unsigned short *src = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW +
                                         (int64_t)h0 * W + ci * DHW + a * HW + row * W + 8 * w8;
             const bool rok = h0 + row < H;
-            const u16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-            const u16x8 v0 = (rok && ci < Cin) ? *reinterpret_cast<const u16x8 *>(src) : z;
-            const u16x8 v1 = (rok && ci + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(src + DHW) : z;
-            put(((a * kRows + row) * W + 8 * w8) * CS + ci, v0, v1);
+            const u16x8 v0 = (rok && ci < Cin) ? *reinterpret_cast<const u16x8 *>(src) : z8;
+            const u16x8 v1 = (rok && ci + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(src + DHW) : z8;
+            put(buf, ((a * kRows + row) * W + 8 * w8) * CS + ci, v0, v1);
         }
-        __syncthreads();
-        int hp2 = hp + 1, d2 = d, n2 = n;
-        if (hp2 == hpairs) { hp2 = 0; if (++d2 == Dp) { d2 = 0; ++n2; } }
-        if (t + 1 < t_end) fetch(n2, d2, hp2);
+    };
+    auto next_pos = [&](int &n_, int &d_, int &hp_) {
+        if (++hp_ == hpairs) { hp_ = 0; if (++d_ == Dp) { d_ = 0; ++n_; } }
+    };
+    int n2 = n, d2 = d, hp2 = hp;
+    __syncthreads();              // every wave holds its fragments: the slabs may reuse that LDS
+    if (t_begin < t_end) {
+        put_all(slab, n, d, hp);
+        next_pos(n2, d2, hp2);
+        if (t_begin + 1 < t_end) fetch(n2, d2, hp2);
+    }
+    __syncthreads();
+
+    for (int t = t_begin; t < t_end; ++t) {
+        const int h0 = kTH * hp;
+        unsigned short *cur = slab + ((t - t_begin) & 1) * slab_u16;
+        if (t + 1 < t_end) {
+            // the spare buffer's last readers finished before the previous barrier
+            put_all(slab + (((t - t_begin) & 1) ^ 1) * slab_u16, n2, d2, hp2);
+            next_pos(n2, d2, hp2);
+            if (t + 2 < t_end) fetch(n2, d2, hp2);
+        }
 
         float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
         int hh = vb_hh0, wb = vb_wb0;
@@ -317,7 +341,7 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
             const int wv = wb * 16 + col;
             const bool valid = (wv < Wp) && (h < Hp);
             const int wc = min(wv, Wp - 1);
-            const unsigned short *sb = slab + (hh * W + wc) * CS;
+            const unsigned short *sb = cur + (hh * W + wc) * CS;
             v4f a0h = {0.0f, 0.0f, 0.0f, 0.0f}, a1h = a0h, a0l = a0h, a1l = a0h;
 #pragma unroll
             for (int j = 0; j < KSTEPS; ++j) {
@@ -343,21 +367,33 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
             wb += 4;
             while (wb >= wblocks) { wb -= wblocks; ++hh; }
         }
-        hp = hp2; d = d2; n = n2;
+        __syncthreads();                           // next slab written; this one consumed
+        next_pos(n, d, hp);
     }
 }
 
 }  // namespace
 
+// Pooled rows per tile for a geometry: 8 when the double-buffered slab fits
+// next to the prologue regions in LDS, else 2; 0 if nothing fits.
+static int pick_th(int cin8, int64_t W)
+{
+    for (int th : {8, 2}) {
+        const int64_t lds = (int64_t)epi_offset(th, (int)W, cin8 + 8) + kCoGroup * (int64_t)sizeof(float);
+        if (lds <= 160 * 1024) return th;
+    }
+    return 0;
+}
+
 // LDS bytes for a geometry; 0 if Cin or W is outside the implemented range
-// (Cin <= 32, W a multiple of 8).
+// (Cin <= 32, W a multiple of 8, slab fits).
 size_t fused3d_bf16_lds_bytes(int64_t Cin, int64_t W)
 {
     if (Cin < 1 || Cin > 32 || W % 8 != 0 || W > 4096) return 0;
     const int cin8 = (int)((Cin + 7) & ~int64_t(7));
-    const int ksteps = cin8 / 4;
-    (void)ksteps;
-    return (size_t)epi_offset((int)W, cin8 + 8) + 2 * kCoGroup * sizeof(float);
+    const int th = pick_th(cin8, W);
+    if (th == 0) return 0;
+    return (size_t)epi_offset(th, (int)W, cin8 + 8) + kCoGroup * sizeof(float);
 }
 
 hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w, const float *conv_bias,
@@ -366,13 +402,15 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w, const float
                                hipStream_t stream)
 {
     const int Dp = (int)(D - 1), Hp = (int)(H - 1), Wp = (int)(W - 1);
-    const int hpairs = (Hp + kTH - 1) / kTH;
-    const int64_t ntiles = N * Dp * (int64_t)hpairs;
     const int cin8 = (int)((Cin + 7) & ~int64_t(7));
     const int ksteps = cin8 / 4;
+    const int th = pick_th(cin8, W);
     const size_t lds = fused3d_bf16_lds_bytes(Cin, W);
+    if (th == 0 || lds == 0) return hipErrorInvalidValue;
+    const int hchunks = (Hp + th - 1) / th;
+    const int64_t ntiles = N * Dp * (int64_t)hchunks;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess &&
+    if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
     const unsigned gy = (unsigned)((Cout + kCoGroup - 1) / kCoGroup);
@@ -382,23 +420,28 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w, const float
     const int tpw = (int)((ntiles + gx - 1) / gx);
     gx = (ntiles + tpw - 1) / tpw;
 
-#define CT_LAUNCH_BF16(KS)                                                                   \
-    do {                                                                                     \
-        hipError_t e = hipFuncSetAttribute((const void *)fused3d_bf16_kernel<KS>,            \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,       \
-                                           (int)lds);                                        \
-        if (e != hipSuccess) return e;                                                       \
-        hipLaunchKernelGGL(fused3d_bf16_kernel<KS>, dim3((unsigned)gx, gy), dim3(kThreads),  \
-                           lds, stream, (const unsigned short *)x, (const unsigned short *)w, \
-                           conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H, (int)W,        \
-                           (int)Cout, Dp, Hp, Wp, hpairs, (int)ntiles, tpw, out);            \
+#define CT_LAUNCH_BF16(KS, TH)                                                                \
+    do {                                                                                      \
+        hipError_t e = hipFuncSetAttribute((const void *)fused3d_bf16_kernel<KS, TH>,         \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,        \
+                                           (int)lds);                                         \
+        if (e != hipSuccess) return e;                                                        \
+        hipLaunchKernelGGL((fused3d_bf16_kernel<KS, TH>), dim3((unsigned)gx, gy),             \
+                           dim3(kThreads), lds, stream, (const unsigned short *)x,            \
+                           (const unsigned short *)w, conv_bias, bias, s1, s2, (int)Cin,      \
+                           (int)D, (int)H, (int)W, (int)Cout, Dp, Hp, Wp, hchunks,            \
+                           (int)ntiles, tpw, out);                                            \
     } while (0)
 
-    switch (ksteps) {
-    case 2: CT_LAUNCH_BF16(2); break;
-    case 4: CT_LAUNCH_BF16(4); break;
-    case 6: CT_LAUNCH_BF16(6); break;
-    case 8: CT_LAUNCH_BF16(8); break;
+    switch (ksteps * 16 + th) {
+    case 2 * 16 + 8: CT_LAUNCH_BF16(2, 8); break;
+    case 4 * 16 + 8: CT_LAUNCH_BF16(4, 8); break;
+    case 6 * 16 + 8: CT_LAUNCH_BF16(6, 8); break;
+    case 8 * 16 + 8: CT_LAUNCH_BF16(8, 8); break;
+    case 2 * 16 + 2: CT_LAUNCH_BF16(2, 2); break;
+    case 4 * 16 + 2: CT_LAUNCH_BF16(4, 2); break;
+    case 6 * 16 + 2: CT_LAUNCH_BF16(6, 2); break;
+    case 8 * 16 + 2: CT_LAUNCH_BF16(8, 2); break;
     default: return hipErrorInvalidValue;
     }
 #undef CT_LAUNCH_BF16

@@ -64,24 +64,32 @@ __device__ __forceinline__ void build_wfrag(const float *__restrict__ w, int Cou
         const int j = e >> 6, l = e & 63;
         const int co = cob * 16 + (l & 15);
         const int kap = 4 * j + (l >> 4);
+        // all 8 candidate taps are loaded unconditionally from valid addresses
+        // (a conditional load would be waited on before the next one issues)
+        const int ci = kap >> 3, tap = kap & 7;
+        const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
+        const float *wp = w + ((int64_t)ci * Cout + min(co, Cout - 1)) * 27;
+        // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
+        const int kd0 = a ? 0 : 1, nkd = a ? 1 : 2;
+        const int kh0 = b ? 0 : 1, nkh = b ? 1 : 2;
+        const int kw0 = c ? 0 : 1, nkw = c ? 1 : 2;
+        float t8[8];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int k = 0; k < 2; ++k)
+                    t8[(i * 2 + jj) * 2 + k] = wp[(kd0 + i) * 9 + (kh0 + jj) * 3 + kw0 + k];
         float v = 0.0f;
-        if (co < Cout) {
-            const int ci = kap >> 3, tap = kap & 7;
-            const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
-            const float *wp = w + ((int64_t)ci * Cout + co) * 27;
-            // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
-            const int kd0 = a ? 0 : 1, nkd = a ? 1 : 2;
-            const int kh0 = b ? 0 : 1, nkh = b ? 1 : 2;
-            const int kw0 = c ? 0 : 1, nkw = c ? 1 : 2;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int k = 0; k < 2; ++k)
-                        if (i < nkd && jj < nkh && k < nkw)
-                            v += wp[(kd0 + i) * 9 + (kh0 + jj) * 3 + kw0 + k];
-        }
+                for (int k = 0; k < 2; ++k)
+                    if (i < nkd && jj < nkh && k < nkw) v += t8[(i * 2 + jj) * 2 + k];
+        if (co >= Cout) v = 0.0f;
         wfrag[e] = v;
     }
 }
@@ -209,9 +217,9 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
                 for (int jj = 0; jj < kChunk; ++jj) {
                     const int kap = 4 * (j0 + jj) + kq;
                     const int ci = kap >> 3, tap = kap & 7;
-                    xv[jj] = (j0 + jj < ksteps)
-                        ? xb[(int64_t)ci * DHW + (tap >> 2) * HW + ((tap >> 1) & 1) * W + (tap & 1)]
-                        : 0.0f;
+                    const int cic = min(ci, Cin - 1);          // valid address; masked below
+                    const float v = xb[(int64_t)cic * DHW + (tap >> 2) * HW + ((tap >> 1) & 1) * W + (tap & 1)];
+                    xv[jj] = (j0 + jj < ksteps) ? v : 0.0f;
                 }
 #pragma unroll
                 for (int jj = 0; jj < kChunk; ++jj)
@@ -237,10 +245,12 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 }
 
 // Main path for Cin <= 4: persistent workgroups walk contiguous ranges of
-// tasks (n, d, TH pooled rows); a task's input slab x[n, :, d..d+1,
-// h0..h0+TH, :] is loaded with coalesced VEC-wide loads into registers while
-// the previous task computes, then copied to LDS, where the B fragments are
-// read (16 consecutive w per lane group).
+// tasks (n, d, TH pooled rows).  A task's input slab x[n, :, d..d+1,
+// h0..h0+TH, :] is loaded two tasks ahead with coalesced VEC-wide loads into
+// registers, written into the spare half of a double-buffered LDS slab one
+// task ahead, and read from there as B fragments (16 consecutive w per lane
+// group); one barrier per task.  The first slab's loads are issued before
+// the filter build so the two latencies overlap.
 constexpr int kSlabPrefetch = 4;   // slab pieces each thread keeps in flight
 
 template <int VEC> struct Vec;
@@ -258,19 +268,29 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
 {
     typedef typename Vec<VEC>::T vec_t;
     extern __shared__ float lds[];
+    const int R = TH + 1;                      // input rows per plane in a slab
+    const int slab_floats = Cin * 2 * R * W;
     float *wfrag = lds;                        // [KS][64]
-    float *slab = lds + KS * 64;               // [Cin][2][TH+1][W]
+    float *slabs = lds + KS * 64;              // 2 x [Cin][2][R][W] (double buffer)
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int cob = blockIdx.y;
-    const int R = TH + 1;                      // input rows per plane in a slab
     const int HW = H * W, DHW = D * HW;        // per-item sizes < 2^31 (checked by the shim)
     const int64_t pplane = (int64_t)Dp * Hp * Wp;
     const int wblocks = (Wp + 15) / 16;
 
-    build_wfrag(w, Cout, cob, KS, wfrag);
+    // this workgroup's contiguous task range (n, d, hc), decoded once
+    const int t_begin = uniform((int)min<int64_t>(xcd_remap(blockIdx.x, gridDim.x) * tasks_per_wg, ntasks));
+    const int t_end = uniform(min(t_begin + tasks_per_wg, ntasks));
+    int hc, d, n;
+    {
+        int t = t_begin;
+        hc = uniform(t % hchunks); t /= hchunks;
+        d = uniform(t % Dp);
+        n = uniform(t / Dp);
+    }
 
     // tile-invariant staging plan: piece q = ((ci*2 + a)*R + r)*(W/VEC) + v
     const int WV = W / VEC;
@@ -286,13 +306,45 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         dst_off[i] = (ca * R + r) * W + v * VEC;
         prow[i] = q < npieces ? r : 1 << 30;   // rows past H (or no piece) load nothing
     }
-    __syncthreads();
+    vec_t pre[kSlabPrefetch];
+    // loads are unconditional (rows past H read x[0..], a valid address) so
+    // they all stay in flight; the zero fill is applied when they are stored
+    auto fetch = [&](int n_, int d_, int hc_) {
+        const int h0 = hc_ * TH;
+        const float *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
+#pragma unroll
+        for (int i = 0; i < kSlabPrefetch; ++i) {
+            const float *src = (h0 + prow[i] < H) ? xb + src_off[i] : x;
+            pre[i] = *reinterpret_cast<const vec_t *>(src);
+        }
+    };
+    // writes the prefetched slab (plus any pieces beyond the prefetch plan) into buf
+    auto put = [&](float *buf, int n_, int d_, int hc_) {
+        const int h0 = hc_ * TH;
+#pragma unroll
+        for (int i = 0; i < kSlabPrefetch; ++i)
+            if (prow[i] < (1 << 30))
+                *reinterpret_cast<vec_t *>(buf + dst_off[i]) = (h0 + prow[i] < H) ? pre[i] : vec_t{};
+        for (int q = threadIdx.x + kSlabPrefetch * kThreads; q < npieces; q += kThreads) {
+            const int v = q % WV, tt = q / WV;
+            const int r = tt % R, ca = tt / R;
+            vec_t val = vec_t{};
+            if (h0 + r < H)
+                val = *reinterpret_cast<const vec_t *>(
+                    x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W +
+                    (ca >> 1) * DHW + (ca & 1) * HW + r * W + v * VEC);
+            *reinterpret_cast<vec_t *>(buf + (ca * R + r) * W + v * VEC) = val;
+        }
+    };
+    // the first slab's loads fly while the filter is built
+    if (t_begin < t_end) fetch(n, d, hc);
+
+    build_wfrag(w, Cout, cob, KS, wfrag);
 
     float a[KS];
     int soff[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-        a[j] = wfrag[j * 64 + lane];
         const int kap = 4 * j + kq;
         const int ci = kap >> 3, tap = kap & 7;
         soff[j] = ((ci * 2 + (tap >> 2)) * R + ((tap >> 1) & 1)) * W + (tap & 1);
@@ -312,57 +364,37 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         co_off[r] = co * (int)pplane;
     }
 
-    const int t_begin = uniform((int)min<int64_t>(xcd_remap(blockIdx.x, gridDim.x) * tasks_per_wg, ntasks));
-    const int t_end = uniform(min(t_begin + tasks_per_wg, ntasks));
-    int hc, d, n;
-    {
-        int t = t_begin;
-        hc = uniform(t % hchunks); t /= hchunks;
-        d = uniform(t % Dp);
-        n = uniform(t / Dp);
-    }
-
-    vec_t pre[kSlabPrefetch];
-    auto fetch = [&](int n_, int d_, int hc_) {
-        const int h0 = hc_ * TH;
-        const float *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
+    // slab of the first task into buffer 0; then per task: put the next slab
+    // into the other buffer, fetch the one after, compute, one barrier
+    if (t_begin < t_end) put(slabs, n, d, hc);
+    __syncthreads();                           // filter and first slab visible
 #pragma unroll
-        for (int i = 0; i < kSlabPrefetch; ++i) {
-            if (h0 + prow[i] < H) pre[i] = *reinterpret_cast<const vec_t *>(xb + src_off[i]);
-            else pre[i] = vec_t{};
-        }
-    };
-    if (t_begin < t_end) fetch(n, d, hc);
+    for (int j = 0; j < KS; ++j) a[j] = wfrag[j * 64 + lane];
+    int hc2 = hc + 1, d2 = d, n2 = n;
+    if (hc2 == hchunks) { hc2 = 0; if (++d2 == Dp) { d2 = 0; ++n2; } }
+    if (t_begin + 1 < t_end) fetch(n2, d2, hc2);
 
     for (int t = t_begin; t < t_end; ++t) {
-        const int h0 = hc * TH;
-        __syncthreads();                      // previous slab consumed
-#pragma unroll
-        for (int i = 0; i < kSlabPrefetch; ++i)
-            if (prow[i] < (1 << 30)) *reinterpret_cast<vec_t *>(slab + dst_off[i]) = pre[i];
-        for (int q = threadIdx.x + kSlabPrefetch * kThreads; q < npieces; q += kThreads) {
-            const int v = q % WV, tt = q / WV;
-            const int r = tt % R, ca = tt / R;
-            vec_t val = vec_t{};
-            if (h0 + r < H)
-                val = *reinterpret_cast<const vec_t *>(
-                    x + (int64_t)n * Cin * DHW + (int64_t)d * HW + (int64_t)h0 * W +
-                    (ca >> 1) * DHW + (ca & 1) * HW + r * W + v * VEC);
-            *reinterpret_cast<vec_t *>(slab + (ca * R + r) * W + v * VEC) = val;
+        const int buf = (t - t_begin) & 1;
+        float *cur = slabs + buf * slab_floats;
+        // next task's slab into the other buffer (its last readers finished
+        // before the previous iteration's barrier), then the loads after it
+        if (t + 1 < t_end) {
+            put(slabs + (buf ^ 1) * slab_floats, n2, d2, hc2);
+            int hc3 = hc2 + 1, d3 = d2, n3 = n2;
+            if (hc3 == hchunks) { hc3 = 0; if (++d3 == Dp) { d3 = 0; ++n3; } }
+            if (t + 2 < t_end) fetch(n3, d3, hc3);
+            hc2 = hc3; d2 = d3; n2 = n3;
         }
-        __syncthreads();
-        // next task position; its slab loads fly while this one computes
-        int hc2 = hc + 1, d2 = d, n2 = n;
-        if (hc2 == hchunks) { hc2 = 0; if (++d2 == Dp) { d2 = 0; ++n2; } }
-        if (t + 1 < t_end) fetch(n2, d2, hc2);
 
+        const int h0 = hc * TH;
         const int rows = min(TH, Hp - h0);
         float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
         // each wave takes rows hh = wave, wave + 4, ...; a row's w-blocks go in
         // pairs, each block's K range split over two accumulators: four
         // independent MFMA chains in flight
         for (int hh = wave; hh < rows; hh += kWaves) {
-            const float *srow = slab + hh * W;
+            const float *srow = cur + hh * W;
             float *orow = ob + hh * Wp;
             for (int wb = 0; wb < wblocks; wb += 2) {
                 const int wv0 = wb * 16 + col, wv1 = wv0 + 16;
@@ -393,7 +425,8 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
                 }
             }
         }
-        hc = hc2; d = d2; n = n2;
+        __syncthreads();                       // next slab written; this one consumed
+        if (++hc == hchunks) { hc = 0; if (++d == Dp) { d = 0; ++n; } }
     }
 }
 
@@ -416,9 +449,9 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
     const unsigned gy = (unsigned)((Cout + 15) / 16);
 
     if constexpr (KS > 0) {
-        // pooled rows per task: up to 8, as many as the LDS budget allows
-        int TH = Hp < 8 ? Hp : 8;
-        auto slab_bytes = [&](int th) { return (size_t)(KS * 64 + Cin * 2 * (th + 1) * W) * sizeof(float); };
+        // pooled rows per task: up to 16, as many as the LDS budget allows
+        int TH = Hp < 16 ? Hp : 16;
+        auto slab_bytes = [&](int th) { return (size_t)(KS * 64 + 2 * Cin * 2 * (th + 1) * W) * sizeof(float); };
         while (TH > 1 && slab_bytes(TH) > kSlabLdsMax) --TH;
         if (slab_bytes(TH) <= kSlabLdsMax) {
             const size_t lds = slab_bytes(TH);
