@@ -98,15 +98,23 @@ CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pa
  *              pool_s, 0) (likewise H, W).  At k3 s2 p1 with a 2-pool,
  *              Dp = D - 1 for every D ([p50], passage on arbitrary sizes).
  *
- * Implemented: k = 3, stride = 2, pad = 1, out_pad = 0, pool_k = 2,
- * pool_s = 2 (or 0, meaning pool_k), with (x_dtype, w_dtype) = (CT_F32,
- * CT_F32) for Cin <= 128, or (CT_BF16, CT_BF16) for Cin <= 32, W a
- * multiple of 8 up to 4096 and x 16-byte aligned (the kernel reads x in
- * 16-byte pieces); accumulation and output are fp32.  The bf16 path represents the summed
- * filter as a bf16 hi + lo pair, so its result matches an fp32 computation
- * on the same bf16 inputs to ~2^-17 relative per term.
- * Other geometry -> CT_EUNSUPPORTED.  D, H or W equal to 1 gives an empty
- * output -> CT_EINVAL.
+ * Geometry: any k >= 1, stride >= 1, pad >= 0, 0 <= out_pad < stride
+ * (PyTorch's rule at dilation 1), pool_k >= 1, pool_s >= 1 (0 = pool_k);
+ * (x_dtype, w_dtype) = (CT_F32, CT_F32) or (CT_BF16, CT_BF16); accumulation
+ * and output are fp32.  Two implementations:
+ *   - k = 3, stride = 2, pad = 1, out_pad = 0, pool 2/2 (the page's
+ *     geometry): matrix-core kernels that contract the 8 input taps of a
+ *     pooled voxel with the grouped (summed) filter.  fp32 for Cin <= 128;
+ *     bf16 for Cin <= 32, W a multiple of 8 up to 4096 and x 16-byte
+ *     aligned.  The bf16 kernel represents the summed filter as a bf16
+ *     hi + lo pair, so its result matches an fp32 computation on the same
+ *     bf16 inputs to ~2^-17 relative per term.
+ *   - anything else: a general gather kernel on the vector ALUs (one thread
+ *     per pooled voxel summing the pool window of transposed-convolution
+ *     values), fp32 arithmetic on the (exactly widened) inputs.
+ * Mixed dtypes, lengths or Cin/Cout beyond 2^30, or k / pool_k beyond 1024
+ * -> CT_EUNSUPPORTED.  An empty output (e.g. D = 1 at the page's geometry)
+ * -> CT_EINVAL.
  */
 CT_API ct_status ct_convT3d_scale_pool_bias(
     const void *x, int x_dtype,
@@ -118,18 +126,47 @@ CT_API ct_status ct_convT3d_scale_pool_bias(
     float *out, void *stream);
 
 /*
+ * ConvTranspose3d alone, materialising its output ([p50], the model's first
+ * layer; the page's estimate of the traffic the fusion saves compares the
+ * fused chain with this layer followed by a separate pool):
+ *   y[n,co,od,oh,ow] = sum_ci sum_{kd,kh,kw} x[n,ci,id,ih,iw] * w[ci,co,kd,kh,kw]
+ *                      (+ bias[co])
+ * over the taps with od = id*stride - pad + kd (likewise h, w) inside the
+ * output, i.e. id = (od + pad - kd) / stride where that division is exact.
+ *
+ *   x     [N, Cin, D, H, W], dtype x_dtype
+ *   w     [Cin, Cout, k, k, k], dtype w_dtype (== x_dtype)
+ *   bias  [Cout] fp32, or NULL (= 0)
+ *   out   [N, Cout, Do, Ho, Wo] fp32, Do = ct_convT_out_len(D, k, stride,
+ *         pad, out_pad, 1) (likewise H, W)
+ *
+ * Geometry and limits as for ct_convT3d_scale_pool_bias.  Computed by the
+ * general gather kernel (one thread per output), fp32 arithmetic.
+ */
+CT_API ct_status ct_convT3d(const void *x, int x_dtype,
+                     const void *w, int w_dtype,
+                     const float *bias,
+                     int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout,
+                     int k, int stride, int pad, int out_pad,
+                     float *out, void *stream);
+
+/*
  * AvgPool3d over zero padding ([p46], opening passages):
  *   out[n,c,d,h,w] = (sum over kd,kh,kw < k of x[n,c, d*s - p + kd,
- *                     h*s - p + kh, w*s - p + kw]) / k^3
- * where taps outside the input read as 0 and the divisor is always k^3
- * (count_include_pad).
+ *                     h*s - p + kh, w*s - p + kw]) / divisor
+ * where taps outside the input read as 0.  The divisor is k^3 when
+ * count_include_pad = 1 (the page's case: 27 at k = 3) and the number of
+ * taps inside the input when count_include_pad = 0 ([p46], passage on the
+ * divisor of border windows).
  *
  *   x    [N, C, D, H, W] fp32
  *   out  [N, C, Do, Ho, Wo] fp32, Do = ct_pool_out_len(D, k, stride, pad)
  *
- * Implemented: k = 3, stride = 2 (or 0, meaning k), pad = 1,
- * count_include_pad = 1.  Other values -> CT_EUNSUPPORTED.  Any N, C, D, H,
- * W >= 1 (sizes per (n, c) slice below 2^31 elements).
+ * Geometry: k >= 1, stride >= 0 (0 = k), 0 <= pad <= k/2 (PyTorch's rule),
+ * floor mode.  k = 3, stride 2, pad 1 with count_include_pad = 1 runs on a
+ * separable streaming kernel (per-slice size below 2^31 elements); anything
+ * else on a general gather kernel (one thread per output; lengths and
+ * stride up to 2^30, k up to 1024, else CT_EUNSUPPORTED).
  */
 CT_API ct_status ct_avgpool3d(const float *x,
                        int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
@@ -150,13 +187,18 @@ CT_API ct_status ct_avgpool3d(const float *x,
  *   out   [N, Cout, L_out] fp32, L_out = ct_convT_out_len(L, K, stride, pad,
  *         out_pad, dilation)
  *
- * Implemented: stride = 1, pad = 0, out_pad = 0, any K >= 1 and
- * dilation >= 1, (x_dtype, w_dtype) = (CT_F32, CT_F32), as long as the
- * weights (64 * K * Cin4 floats, Cin4 = Cin rounded up to a multiple of 4)
- * and one input strip (Cin4 rows of 256 + dilation*(K-1) floats, padded)
- * fit the 160 KiB LDS of one gfx950 workgroup (Cin=32, K=5, dilation 3
- * needs 74 KiB).  Other values -> CT_EUNSUPPORTED.  Computed as an implicit GEMM on the
- * fp32 matrix cores (full fp32 products, fp32 accumulation).
+ * Geometry: K >= 1, stride >= 1, pad >= 0, dilation >= 1,
+ * 0 <= out_pad < max(stride, dilation) (PyTorch's rule);
+ * (x_dtype, w_dtype) = (CT_F32, CT_F32) or (CT_BF16, CT_BF16).
+ *   - fp32, stride 1, pad 0, out_pad 0 (the page's case): an implicit GEMM
+ *     on the fp32 matrix cores (full fp32 products and accumulation), as
+ *     long as the weights (64 * K * Cin4 floats, Cin4 = Cin rounded up to a
+ *     multiple of 4) and one input strip (Cin4 rows of 256 +
+ *     dilation*(K-1) floats, padded) fit the 160 KiB LDS of one gfx950
+ *     workgroup (Cin=32, K=5, dilation 3 needs 74 KiB).
+ *   - anything else: a general gather kernel (one thread per output), fp32
+ *     arithmetic on the exactly widened inputs; lengths, Cin, Cout, pad and
+ *     dilation*(K-1) up to 2^30, else CT_EUNSUPPORTED.
  */
 CT_API ct_status ct_convT1d(const void *x, int x_dtype,
                      const void *w, int w_dtype,

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = set(declared_functions())
-    for n in ["ct_convT3d_scale_pool_bias", "ct_avgpool3d", "ct_convT1d",
+    for n in ["ct_convT3d_scale_pool_bias", "ct_convT3d", "ct_avgpool3d", "ct_convT1d",
               "ct_convT_out_len", "ct_pool_out_len", "ct_status_str", "ct_last_error",
               "ct_version"]:
         assert n in names
@@ -84,24 +84,26 @@ def fused(**kw):
     (dict(D=1), ct.CT_EINVAL),              # pooled depth 0: empty output
     (dict(W=1), ct.CT_EINVAL),
     (dict(stride=0), ct.CT_EINVAL),
-    (dict(k=5), ct.CT_EUNSUPPORTED),
-    (dict(stride=1), ct.CT_EUNSUPPORTED),
-    (dict(pad=0), ct.CT_EUNSUPPORTED),
-    (dict(out_pad=1), ct.CT_EUNSUPPORTED),
-    (dict(pool_k=3), ct.CT_EUNSUPPORTED),
-    (dict(pool_s=1), ct.CT_EUNSUPPORTED),
+    (dict(out_pad=2), ct.CT_EINVAL),                # out_pad must be < stride
+    (dict(stride=1, out_pad=1), ct.CT_EINVAL),
+    (dict(pad=-1), ct.CT_EINVAL),
+    (dict(k=0), ct.CT_EINVAL),
+    (dict(pool_k=0), ct.CT_EINVAL),
+    (dict(pool_s=-1), ct.CT_EINVAL),
+    (dict(pool_k=16, D=8), ct.CT_EINVAL),           # pool window longer than depth 15
+    (dict(pad=9, D=8, k=3), ct.CT_EINVAL),          # conv output empty
     (dict(xd=ct.CT_BF16), ct.CT_EUNSUPPORTED),      # mixed dtypes
     (dict(x=FAKE + 2), ct.CT_EINVAL),               # fp32 x misaligned
     (dict(out=FAKE2 * 2 + 1), ct.CT_EINVAL),
     (dict(b=FAKE + 1), ct.CT_EINVAL),
     (dict(out=FAKE + 64), ct.CT_EINVAL),            # out overlaps x
     (dict(out=FAKE2 + 4), ct.CT_EINVAL),            # out overlaps w
-    (dict(Cin=129), ct.CT_EUNSUPPORTED),            # fp32 LDS limit
-    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, W=20), ct.CT_EUNSUPPORTED),   # bf16: W % 8
-    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, Cin=33), ct.CT_EUNSUPPORTED),
-    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, x=FAKE + 2), ct.CT_EUNSUPPORTED),  # bf16 x not 16B aligned
     (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, x=FAKE + 1), ct.CT_EINVAL),
-    (dict(N=1 << 40), ct.CT_EUNSUPPORTED),          # beyond one launch's index range
+    (dict(W=1 << 31), ct.CT_EUNSUPPORTED),          # beyond the kernels' index range
+    (dict(Cout=(1 << 30) + 1), ct.CT_EUNSUPPORTED),
+    (dict(k=1025, pad=600, D=600, H=600, W=600, N=1, Cin=1, Cout=1, out=1 << 44),
+     ct.CT_EUNSUPPORTED),
+    (dict(pool_k=1025, pool_s=1, D=600, H=600, W=600, out=1 << 44), ct.CT_EUNSUPPORTED),
     (dict(N=1 << 60), ct.CT_EINVAL),                # byte size overflows int64
 ])
 def test_fused_rejects(kw, status):
@@ -124,10 +126,11 @@ def pool(**kw):
     (dict(pad=2), ct.CT_EINVAL),                    # pad > k/2
     (dict(cip=2), ct.CT_EINVAL),
     (dict(k=5, pad=0, D=3, H=3, W=3), ct.CT_EINVAL),  # no window fits
-    (dict(cip=0), ct.CT_EUNSUPPORTED),
-    (dict(k=2, pad=1), ct.CT_EUNSUPPORTED),
-    (dict(stride=0), ct.CT_EUNSUPPORTED),           # stride = k = 3
-    (dict(stride=1), ct.CT_EUNSUPPORTED),
+    (dict(k=0), ct.CT_EINVAL),
+    (dict(stride=-1), ct.CT_EINVAL),
+    (dict(k=2, pad=0, N=1, C=1, D=2, H=2, W=(1 << 30) + 2, out=1 << 44),
+     ct.CT_EUNSUPPORTED),                           # general kernel's index range
+    (dict(k=1025, pad=0, N=1, C=1, D=2000, H=2000, W=2000, out=1 << 44), ct.CT_EUNSUPPORTED),
     (dict(x=FAKE + 1), ct.CT_EINVAL),
     (dict(out=FAKE + 4096), ct.CT_EINVAL),          # overlaps x
 ])
@@ -151,16 +154,47 @@ def conv1d(**kw):
     (dict(K=0), ct.CT_EINVAL),
     (dict(dil=0), ct.CT_EINVAL),
     (dict(pad=5, L=2, K=2, dil=1), ct.CT_EINVAL),   # empty output
-    (dict(stride=2), ct.CT_EUNSUPPORTED),
-    (dict(pad=1), ct.CT_EUNSUPPORTED),
-    (dict(out_pad=1), ct.CT_EUNSUPPORTED),
-    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16), ct.CT_EUNSUPPORTED),
-    (dict(Cin=1024, K=64), ct.CT_EUNSUPPORTED),     # exceeds LDS
+    (dict(stride=0), ct.CT_EINVAL),
+    (dict(pad=-1), ct.CT_EINVAL),
+    (dict(out_pad=3), ct.CT_EINVAL),                # out_pad must be < max(stride, dilation)
+    (dict(out_pad=4, stride=4, dil=1), ct.CT_EINVAL),
+    (dict(xd=ct.CT_BF16), ct.CT_EUNSUPPORTED),      # mixed dtypes
+    (dict(L=(1 << 30) + 1, stride=2, N=1, Cin=1, out=1 << 44),
+     ct.CT_EUNSUPPORTED),                           # general kernel's index range
+    (dict(dil=1 << 29, K=5), ct.CT_EUNSUPPORTED),
     (dict(x=FAKE + 2), ct.CT_EINVAL),
+    (dict(xd=ct.CT_BF16, wd=ct.CT_BF16, x=FAKE + 1), ct.CT_EINVAL),
     (dict(out=FAKE2 + 8), ct.CT_EINVAL),            # overlaps w
 ])
 def test_conv1d_rejects(kw, status):
     assert conv1d(**kw) == status
+
+
+def convT3d(**kw):
+    a = dict(x=FAKE, xd=ct.CT_F32, w=FAKE2, wd=ct.CT_F32, b=None, N=2, Cin=3, D=8, H=16, W=16,
+             Cout=16, k=3, stride=2, pad=1, out_pad=0, out=FAKE2 * 2, stream=None)
+    a.update(kw)
+    return ct.lib.ct_convT3d(a["x"], a["xd"], a["w"], a["wd"], a["b"], a["N"], a["Cin"], a["D"],
+                             a["H"], a["W"], a["Cout"], a["k"], a["stride"], a["pad"],
+                             a["out_pad"], a["out"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ct.CT_EINVAL),
+    (dict(out=None), ct.CT_EINVAL),
+    (dict(wd=9), ct.CT_EINVAL),
+    (dict(H=0), ct.CT_EINVAL),
+    (dict(stride=0), ct.CT_EINVAL),
+    (dict(out_pad=2), ct.CT_EINVAL),
+    (dict(pad=3, k=3, D=1), ct.CT_EINVAL),          # conv output empty
+    (dict(b=FAKE + 2), ct.CT_EINVAL),
+    (dict(out=FAKE + 128), ct.CT_EINVAL),           # overlaps x
+    (dict(wd=ct.CT_BF16), ct.CT_EUNSUPPORTED),      # mixed dtypes
+    (dict(D=1 << 31), ct.CT_EUNSUPPORTED),
+])
+def test_convT3d_rejects(kw, status):
+    assert convT3d(**kw) == status
+    assert ct.ct_last_error().startswith("convT3d")
 
 
 def test_python_binding_requires_gpu_tensors():

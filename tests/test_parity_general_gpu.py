@@ -1,0 +1,236 @@
+"""Parity of the general-geometry paths (everything outside the pages' own
+k3 s2 p1 / 2-pool, k3 s2 p1 / divisor-27 and stride-1 fp32 cases) with the
+fp64 CPU oracle, through the C ABI.
+
+Same tolerances as the specialised paths: fp32 inputs atol 1e-4, rtol 1e-5;
+bf16 inputs atol 1e-4, rtol 2e-2, with the oracle fed the identical
+bf16-rounded values.  Outputs are NaN-prefilled so an unwritten element fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+import transposed_conv_pooling_amd as ct  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = (1e-4, 1e-5)
+BF16_TOL = (1e-4, 2e-2)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def assert_close(got, ref, tol, what=""):
+    atol, rtol = tol
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    err = np.abs(got - ref)
+    ok = err <= atol + rtol * np.abs(ref)
+    if not ok.all():
+        idx = np.argwhere(~ok)
+        i0 = tuple(idx[0])
+        raise AssertionError(
+            f"{what}: {len(idx)} of {ok.size} elements out of tolerance; first at {i0}: "
+            f"gpu={got[i0]!r} oracle={ref[i0]!r}; max err {np.nanmax(err):.3g}")
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def bf16_round(a):
+    return synth.bf16_bits_to_f32(synth.to_bf16_bits(a)).reshape(a.shape)
+
+
+def to_dev(a, dev, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(synth.to_bf16_bits(a).reshape(a.shape).view(np.int16)).to(
+            dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def opt(a, dev):
+    return None if a is None else torch.from_numpy(a).to(dev)
+
+
+# ------------------------------------------------ fused, general geometry ----
+FUSED_GENERAL = [
+    # N, Cin, Cout, D, H, W, k, stride, pad, out_pad, pool_k, pool_s, dtype
+    (2, 3, 16, 5, 7, 9, 3, 2, 1, 1, 2, 2, "f32"),     # output_padding 1
+    (2, 3, 16, 5, 7, 9, 3, 2, 1, 1, 2, 2, "bf16"),
+    (1, 4, 6, 4, 5, 6, 4, 2, 1, 0, 2, 2, "f32"),      # even kernel
+    (1, 3, 5, 4, 6, 7, 3, 1, 0, 0, 3, 2, "f32"),      # stride 1, 3-pool with stride 2
+    (2, 2, 3, 3, 4, 5, 5, 3, 2, 2, 2, 1, "f32"),      # overlapping pool windows
+    (1, 5, 7, 3, 3, 4, 2, 2, 0, 0, 2, 2, "f32"),      # non-overlapping taps
+    (1, 2, 3, 4, 5, 6, 1, 1, 0, 0, 1, 1, "f32"),      # 1x1x1 conv, identity pool
+    (1, 3, 4, 3, 4, 5, 3, 2, 1, 0, 3, 3, "bf16"),
+    (1, 130, 4, 3, 3, 5, 3, 2, 1, 0, 2, 2, "f32"),    # page geometry, Cin beyond the MFMA path
+    (1, 40, 8, 3, 4, 8, 3, 2, 1, 0, 2, 2, "bf16"),    # page geometry, bf16 Cin > 32
+    (2, 3, 16, 4, 5, 13, 3, 2, 1, 0, 2, 2, "bf16"),   # page geometry, bf16 W % 8 != 0
+]
+
+
+@pytest.mark.parametrize("case", FUSED_GENERAL, ids=lambda c: "x".join(map(str, c)))
+def test_fused_general(dev, case):
+    N, Cin, Cout, D, H, W, k, s, p, op, pk, ps, dt = case
+    log(f"fused general {case}")
+    seed = 5000 + sum(c for c in case if isinstance(c, int))
+    x = synth.normal(seed, 0, (N, Cin, D, H, W))
+    bound = 1.0 / np.sqrt(Cin * k ** 3)
+    w = synth.uniform(seed, 1, (Cin, Cout, k, k, k), -bound, bound)
+    if dt == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    b = synth.normal(seed, 2, (Cout,))
+    cb = synth.normal(seed, 3, (Cout,))
+    ref = oracle.convT3d_scale_pool_bias(x, w, cb, b, 0.5, 1.25, stride=s, pad=p, out_pad=op,
+                                         pool_k=pk, pool_s=ps)
+    out = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT3d_scale_pool_bias(to_dev(x, dev, dt), to_dev(w, dev, dt), opt(cb, dev),
+                                  opt(b, dev), 0.5, 1.25, stride=s, pad=p, out_pad=op,
+                                  pool_k=pk, pool_s=ps, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, str(case))
+
+
+def test_fused_bf16_misaligned_x_takes_general_path(dev):
+    shape = (1, 8, 3, 4, 16)
+    x = bf16_round(synth.normal(71, 0, shape))
+    w = bf16_round(synth.uniform(71, 1, (8, 16, 3, 3, 3), -0.1, 0.1))
+    b = synth.normal(71, 2, (16,))
+    buf = torch.empty(x.size + 1, dtype=torch.bfloat16, device=dev)
+    buf[1:] = to_dev(x.reshape(-1), dev, "bf16")
+    xg = buf[1:].view(shape)                        # 2-byte but not 16-byte aligned
+    out = torch.full((1, 16, 2, 3, 15), float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT3d_scale_pool_bias(xg, to_dev(w, dev, "bf16"), None, opt(b, dev), 0.5, 1.0,
+                                  out=out)
+    torch.cuda.synchronize()
+    ref = oracle.convT3d_scale_pool_bias(x, w, None, b, 0.5, 1.0)
+    assert_close(out.cpu().numpy(), ref, BF16_TOL, "bf16 misaligned")
+
+
+# ------------------------------------------------- standalone ConvTranspose3d ----
+CONVT3D = [
+    # N, Cin, Cout, D, H, W, k, stride, pad, out_pad, bias, dtype
+    (2, 3, 16, 8, 16, 16, 3, 2, 1, 0, False, "f32"),  # the page's first layer at the small size
+    (1, 3, 5, 4, 5, 6, 3, 2, 1, 1, True, "f32"),
+    (1, 2, 3, 3, 4, 5, 4, 3, 1, 2, True, "f32"),
+    (1, 4, 4, 3, 3, 3, 2, 1, 0, 0, False, "f32"),
+    (2, 5, 6, 4, 4, 6, 3, 2, 1, 0, True, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", CONVT3D, ids=lambda c: "x".join(map(str, c)))
+def test_convT3d(dev, case):
+    N, Cin, Cout, D, H, W, k, s, p, op, with_bias, dt = case
+    log(f"convT3d {case}")
+    seed = 6000 + sum(c for c in case if isinstance(c, int))
+    x = synth.normal(seed, 0, (N, Cin, D, H, W))
+    bound = 1.0 / np.sqrt(Cin * k ** 3)
+    w = synth.uniform(seed, 1, (Cin, Cout, k, k, k), -bound, bound)
+    if dt == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    b = synth.normal(seed, 2, (Cout,)) if with_bias else None
+    ref = oracle.convT3d(x, w, b, stride=s, pad=p, out_pad=op)
+    out = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT3d(to_dev(x, dev, dt), to_dev(w, dev, dt), opt(b, dev), stride=s, pad=p,
+                  out_pad=op, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, str(case))
+
+
+def test_unfused_chain_c2_matches_fused(dev):
+    """The pages' unfused baseline at full size: ConvTranspose3d materialises
+    [128,16,31,63,63] (1.0 GB), then a 2-pool; the scaled, biased result equals
+    the fused kernel's.  Batch items 0 and 127 of the pre-pool tensor are also
+    recomputed by the oracle."""
+    wl = synth.WORKLOADS["c2"]
+    log(wl.description)
+    t = synth.make_inputs(wl)
+    xg, wg = torch.from_numpy(t["x"]).to(dev), torch.from_numpy(t["w"]).to(dev)
+    bg = torch.from_numpy(t["bias"]).to(dev)
+    y = torch.full((128, 16, 31, 63, 63), float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT3d(xg, wg, None, out=y)
+    pooled = torch.full((128, 16, 15, 31, 31), float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_avgpool3d(y, 2, 2, 0, True, out=pooled)
+    fused = ct.ct_convT3d_scale_pool_bias(xg, wg, None, bg, 0.5, 1.0)
+    torch.cuda.synchronize()
+    for n in (0, 127):
+        ref = oracle.convT3d(t["x"][n:n + 1], t["w"], None, stride=2, pad=1)
+        assert_close(y[n:n + 1].cpu().numpy(), ref, F32_TOL, f"c2 convT3d n={n}")
+    unfused = (pooled * 0.5 + bg.view(1, 16, 1, 1, 1)) * 1.0
+    assert_close(unfused.cpu().numpy(), fused.cpu().numpy().astype(np.float64), F32_TOL,
+                 "unfused vs fused")
+
+
+# ------------------------------------------------- pool, general geometry ----
+POOL_GENERAL = [
+    # shape, k, stride, pad, count_include_pad
+    ((2, 3, 9, 10, 13), 3, 2, 1, False),    # the page's window, valid-tap divisor
+    ((1, 2, 8, 9, 10), 2, 2, 0, True),      # the fused chain's pool, standalone
+    ((1, 2, 7, 6, 11), 3, 1, 1, True),
+    ((1, 1, 11, 12, 13), 5, 3, 2, False),
+    ((1, 1, 11, 12, 13), 5, 3, 2, True),
+    ((2, 1, 9, 8, 7), 4, 0, 2, False),      # stride 0 -> k
+    ((1, 1, 3, 4, 5), 1, 1, 0, True),       # identity
+    ((1, 1, 1, 1, 1), 1, 2, 0, False),
+    ((1, 2, 2, 3, 300), 2, 1, 1, False),
+]
+
+
+@pytest.mark.parametrize("case", POOL_GENERAL, ids=lambda c: "x".join(map(str, c[0])) +
+                         f"_k{c[1]}s{c[2]}p{c[3]}c{int(c[4])}")
+def test_pool_general(dev, case):
+    shape, k, s, p, cip = case
+    log(f"pool general {case}")
+    x = synth.normal(7000 + sum(shape) + k, 0, shape)
+    ref = oracle.avgpool3d(x, k, s if s else k, p, cip)
+    out = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_avgpool3d(torch.from_numpy(x).to(dev), k, s, p, cip, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, F32_TOL, str(case))
+
+
+def test_pool_valid_tap_divisor_border_values(dev):
+    """count_include_pad off: an all-ones input averages to exactly 1 everywhere."""
+    x = torch.ones((1, 1, 6, 7, 9), dtype=torch.float32, device=dev)
+    out = ct.ct_avgpool3d(x, 3, 2, 1, False)
+    torch.cuda.synchronize()
+    assert bool((out == 1.0).all())
+
+
+# ---------------------------------------------- convT1d, general geometry ----
+CONV1D_GENERAL = [
+    # N, Cin, Cout, L, K, stride, pad, dilation, out_pad, bias, dtype
+    (2, 32, 64, 300, 5, 1, 0, 3, 0, False, "bf16"),  # the page's geometry in bf16
+    (1, 4, 6, 37, 4, 2, 1, 1, 1, True, "f32"),
+    (2, 3, 5, 29, 5, 3, 2, 2, 1, True, "f32"),
+    (1, 5, 3, 40, 3, 1, 2, 3, 2, False, "f32"),      # out_pad < dilation
+    (1, 2, 2, 1, 1, 1, 0, 1, 0, True, "f32"),
+    (1, 8, 9, 50, 6, 4, 3, 2, 3, True, "bf16"),
+    (1, 300, 8, 20, 3, 1, 0, 1, 0, False, "f32"),    # weights beyond the LDS tile
+]
+
+
+@pytest.mark.parametrize("case", CONV1D_GENERAL, ids=lambda c: "x".join(map(str, c)))
+def test_conv1d_general(dev, case):
+    N, Cin, Cout, L, K, s, p, d, op, with_bias, dt = case
+    log(f"convT1d general {case}")
+    seed = 8000 + N + Cin + Cout + L + K
+    x = synth.normal(seed, 0, (N, Cin, L))
+    bnd = 1.0 / np.sqrt(Cin * K)
+    w = synth.uniform(seed, 1, (Cin, Cout, K), -bnd, bnd)
+    if dt == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    b = synth.normal(seed, 2, (Cout,)) if with_bias else None
+    ref = oracle.convT1d(x, w, b, s, p, d, op)
+    out = torch.full(ref.shape, float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT1d(to_dev(x, dev, dt), to_dev(w, dev, dt), opt(b, dev), s, p, d, op, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, str(case))

@@ -14,6 +14,7 @@ There is no CPU fallback: importing this package without a built
 Operations (POPCORNBENCH pages, one problem each):
   [p50] "Kimi-K2.6 l2_p50" -- fused ConvTranspose3d -> scale -> AvgPool3d ->
         bias -> scale (``ct_convT3d_scale_pool_bias``)
+        and the unfused first layer alone (``ct_convT3d``)
   [p46] "Kimi-K2.6 l1_p46" -- AvgPool3d(k3, s2, p1), divisor 27
         (``ct_avgpool3d``)
   [p74] "Kimi-K2.6 l1_p74" -- dilated ConvTranspose1d (``ct_convT1d``)
@@ -51,6 +52,8 @@ def _load():
     lib.ct_convT3d_scale_pool_bias.restype = _int
     lib.ct_convT3d_scale_pool_bias.argtypes = (
         [_ptr, _int, _ptr, _int, _ptr, _ptr, _f32, _f32] + [_i64] * 6 + [_int] * 6 + [_ptr, _ptr])
+    lib.ct_convT3d.restype = _int
+    lib.ct_convT3d.argtypes = [_ptr, _int, _ptr, _int, _ptr] + [_i64] * 6 + [_int] * 4 + [_ptr, _ptr]
     lib.ct_avgpool3d.restype = _int
     lib.ct_avgpool3d.argtypes = [_ptr] + [_i64] * 5 + [_int] * 4 + [_ptr, _ptr]
     lib.ct_convT1d.restype = _int
@@ -170,6 +173,30 @@ def ct_convT3d_scale_pool_bias(x, w, conv_bias=None, bias=None, scale1: float = 
     return out
 
 
+def ct_convT3d(x, w, bias=None, stride: int = 2, pad: int = 1, out_pad: int = 0, out=None,
+               stream=None):
+    """ConvTranspose3d; x [N,Cin,D,H,W], w [Cin,Cout,k,k,k] (both float32 or both
+    bfloat16), bias float32 [Cout] or None -> float32 [N,Cout,Do,Ho,Wo]."""
+    torch = _torch()
+    N, Cin, D, H, W = x.shape
+    Cin2, Cout, k = w.shape[0], w.shape[1], w.shape[2]
+    if Cin2 != Cin or tuple(w.shape[2:]) != (k, k, k):
+        raise ValueError(f"weight shape {tuple(w.shape)} does not match input {tuple(x.shape)}")
+    dims = [ct_convT_out_len(n, k, stride, pad, out_pad, 1) for n in (D, H, W)]
+    if out is None:
+        out = torch.empty((N, Cout, *[max(d, 0) for d in dims]), dtype=torch.float32,
+                          device=x.device)
+    elif tuple(out.shape) != (N, Cout, *dims) or out.dtype != torch.float32:
+        raise ValueError(f"out must be float32 {(N, Cout, *dims)}")
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Cout):
+        raise ValueError(f"bias must be float32 with {Cout} elements")
+    st = lib.ct_convT3d(_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
+                        _dev_ptr(bias, "bias", False), N, Cin, D, H, W, Cout, k, stride, pad,
+                        out_pad, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    _check(st)
+    return out
+
+
 def ct_avgpool3d(x, k: int = 3, stride: int = 2, pad: int = 1, count_include_pad: bool = True,
                  out=None, stream=None):
     """AvgPool3d over zero padding; x [N,C,D,H,W] float32 -> float32."""
@@ -192,7 +219,8 @@ def ct_avgpool3d(x, k: int = 3, stride: int = 2, pad: int = 1, count_include_pad
 
 def ct_convT1d(x, w, bias=None, stride: int = 1, pad: int = 0, dilation: int = 1,
                out_pad: int = 0, out=None, stream=None):
-    """Transposed 1D convolution; x [N,Cin,L], w [Cin,Cout,K] float32 -> [N,Cout,L_out]."""
+    """Transposed 1D convolution; x [N,Cin,L], w [Cin,Cout,K] (both float32 or both
+    bfloat16), bias float32 [Cout] or None -> float32 [N,Cout,L_out]."""
     torch = _torch()
     N, Cin, L = x.shape
     Cin2, Cout, K = w.shape
@@ -214,6 +242,6 @@ def ct_convT1d(x, w, bias=None, stride: int = 1, pad: int = 0, dilation: int = 1
 
 __all__ = [
     "CtError", "CT_OK", "CT_EINVAL", "CT_EUNSUPPORTED", "CT_EHIP", "CT_F32", "CT_BF16",
-    "ct_convT3d_scale_pool_bias", "ct_avgpool3d", "ct_convT1d", "ct_convT_out_len",
+    "ct_convT3d_scale_pool_bias", "ct_convT3d", "ct_avgpool3d", "ct_convT1d", "ct_convT_out_len",
     "ct_pool_out_len", "ct_status_str", "ct_last_error", "ct_version", "lib", "LIB_PATH",
 ]

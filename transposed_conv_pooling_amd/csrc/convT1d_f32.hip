@@ -103,7 +103,6 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 
         // B row base for this lane: xs[ci][halo - dil*k + 64*wave + 16b + col]
         const int obase = halo + 64 * wave + col;
-#pragma unroll 2
         for (int j = 0; j < ksteps; ++j) {
             const int kap = 4 * j + kq;
             const int k = kap / Cin4, ci = kap - k * Cin4;
@@ -315,8 +314,9 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess)
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
     const int per_cu = lds <= 80 * 1024 ? 2 : 1;
     int64_t gx = (int64_t)cus * per_cu;
     if (gx > ntiles) gx = ntiles;

@@ -81,6 +81,54 @@ ct_status hip_status(hipError_t e, const char *what)
     return fail(CT_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+
+// Limits of the general-geometry kernels: they index one axis in 32-bit
+// arithmetic (o + pad - k, i * stride), so every length, pad and stride stays
+// below 2^30 and the kernel / pool size below 2^10 (a window already holds
+// 2^30 taps there).
+constexpr int64_t kGenericMaxLen = int64_t(1) << 30;
+constexpr int kGenericMaxTap = 1024;
+
+// Checks shared by the fused chain and the standalone ConvTranspose3d:
+// pointers, dtypes, sizes, PyTorch's rule out_pad < stride (dilation 1),
+// non-empty convolution output (od[]), alignment of x, w and out, and the
+// general kernel's index range.
+ct_status check_convT3d(const char *fn, const void *x, int x_dtype, const void *w, int w_dtype,
+                        int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout,
+                        int k, int stride, int pad, int out_pad, const float *out, int *xs,
+                        int *ws, int64_t od[3])
+{
+    if (!x || !w || !out) return fail(CT_EINVAL, "%s: x, w and out must be non-null", fn);
+    *xs = dtype_size(x_dtype);
+    *ws = dtype_size(w_dtype);
+    if (!*xs || !*ws) return fail(CT_EINVAL, "%s: unknown dtype (%d, %d)", fn, x_dtype, w_dtype);
+    if (N < 1 || Cin < 1 || D < 1 || H < 1 || W < 1 || Cout < 1)
+        return fail(CT_EINVAL, "%s: sizes must be >= 1 (N=%lld Cin=%lld D=%lld H=%lld W=%lld Cout=%lld)",
+                    fn, (long long)N, (long long)Cin, (long long)D, (long long)H, (long long)W,
+                    (long long)Cout);
+    if (k < 1 || stride < 1 || pad < 0 || out_pad < 0 || out_pad >= stride)
+        return fail(CT_EINVAL, "%s: invalid geometry k=%d stride=%d pad=%d out_pad=%d "
+                    "(out_pad must be < stride)", fn, k, stride, pad, out_pad);
+    const int64_t in[3] = {D, H, W};
+    for (int i = 0; i < 3; ++i) {
+        od[i] = ct_convT_out_len(in[i], k, stride, pad, out_pad, 1);
+        if (od[i] <= 0)
+            return fail(CT_EINVAL, "%s: empty output along axis %d (input %lld -> conv %lld)", fn, i,
+                        (long long)in[i], (long long)od[i]);
+    }
+    if (!aligned(x, *xs) || !aligned(w, *ws) || !aligned(out, 4))
+        return fail(CT_EINVAL, "%s: misaligned pointer", fn);
+    for (int i = 0; i < 3; ++i)
+        if (in[i] > kGenericMaxLen || od[i] > kGenericMaxLen)
+            return fail(CT_EUNSUPPORTED, "%s: lengths beyond %lld are not implemented", fn,
+                        (long long)kGenericMaxLen);
+    if (Cin > kGenericMaxLen || Cout > kGenericMaxLen || pad > kGenericMaxLen ||
+        k > kGenericMaxTap)
+        return fail(CT_EUNSUPPORTED, "%s: Cin, Cout or pad beyond %lld, or k beyond %d, is not "
+                    "implemented", fn, (long long)kGenericMaxLen, kGenericMaxTap);
+    return CT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,66 +168,93 @@ ct_status ct_convT3d_scale_pool_bias(
     int k, int stride, int pad, int out_pad, int pool_k, int pool_s,
     float *out, void *stream)
 {
-    if (!x || !w || !out)
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: x, w and out must be non-null");
-    const int xs = dtype_size(x_dtype), ws = dtype_size(w_dtype);
-    if (!xs || !ws)
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: unknown dtype (%d, %d)", x_dtype, w_dtype);
-    if (N < 1 || Cin < 1 || D < 1 || H < 1 || W < 1 || Cout < 1)
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: sizes must be >= 1 (N=%lld Cin=%lld D=%lld H=%lld W=%lld Cout=%lld)",
-                    (long long)N, (long long)Cin, (long long)D, (long long)H, (long long)W, (long long)Cout);
-    if (k < 1 || stride < 1 || pad < 0 || out_pad < 0 || pool_k < 1 || pool_s < 0)
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: invalid geometry k=%d stride=%d pad=%d out_pad=%d pool_k=%d pool_s=%d",
-                    k, stride, pad, out_pad, pool_k, pool_s);
+    const char *fn = "convT3d_scale_pool_bias";
+    int xs, ws;
+    int64_t od[3];
+    ct_status st = check_convT3d(fn, x, x_dtype, w, w_dtype, N, Cin, D, H, W, Cout, k, stride,
+                                 pad, out_pad, out, &xs, &ws, od);
+    if (st != CT_OK) return st;
+    if (pool_k < 1 || pool_s < 0)
+        return fail(CT_EINVAL, "%s: invalid pool geometry pool_k=%d pool_s=%d", fn, pool_k, pool_s);
     const int ps = pool_s == 0 ? pool_k : pool_s;
-    int64_t od[3], pd[3];
-    const int64_t in[3] = {D, H, W};
+    int64_t pd[3];
     for (int i = 0; i < 3; ++i) {
-        od[i] = ct_convT_out_len(in[i], k, stride, pad, out_pad, 1);
-        pd[i] = od[i] > 0 ? ct_pool_out_len(od[i], pool_k, ps, 0) : 0;
+        pd[i] = ct_pool_out_len(od[i], pool_k, ps, 0);
         if (pd[i] <= 0)
-            return fail(CT_EINVAL, "convT3d_scale_pool_bias: empty output along axis %d (input %lld -> conv %lld -> pool %lld)",
-                        i, (long long)in[i], (long long)od[i], (long long)pd[i]);
+            return fail(CT_EINVAL, "%s: empty output along axis %d (conv %lld -> pool %lld)", fn, i,
+                        (long long)od[i], (long long)pd[i]);
     }
-    if (k != 3 || stride != 2 || pad != 1 || out_pad != 0 || pool_k != 2 || ps != 2)
-        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: only k=3 stride=2 pad=1 out_pad=0 pool 2/2 is implemented");
-    if (x_dtype != w_dtype)
-        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: x and w dtypes must match");
-    if (!aligned(x, xs) || !aligned(w, ws) || !aligned(out, 4) ||
-        (conv_bias && !aligned(conv_bias, 4)) || (bias && !aligned(bias, 4)))
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: misaligned pointer");
+    if ((conv_bias && !aligned(conv_bias, 4)) || (bias && !aligned(bias, 4)))
+        return fail(CT_EINVAL, "%s: misaligned pointer", fn);
     int64_t nx, nw, no;
-    if (!prod({N, Cin, D, H, W, (int64_t)xs}, &nx) || !prod({Cin, Cout, 27, (int64_t)ws}, &nw) ||
+    if (!prod({N, Cin, D, H, W, (int64_t)xs}, &nx) ||
+        !prod({Cin, Cout, (int64_t)k, (int64_t)k, (int64_t)k, (int64_t)ws}, &nw) ||
         !prod({N, Cout, pd[0], pd[1], pd[2], 4}, &no))
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: tensor size overflows");
-    // kernel index limits
-    const int64_t wblocks = (pd[2] + 15) / 16;
-    int64_t nmb;
-    if (!prod({N, pd[0], pd[1], wblocks}, &nmb) || nmb > kI32Max / 8 || Cin * D * H * W > kI32Max ||
-        Cout * pd[0] * pd[1] * pd[2] > kI32Max ||
-        Cout > 65535 * 16)
-        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: problem too large for one launch");
-    if (x_dtype == CT_F32 && Cin > 128)
-        return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: fp32 path supports Cin <= 128");
-    if (x_dtype == CT_BF16) {
-        const size_t lb = ct::fused3d_bf16_lds_bytes(Cin, W);
-        if (Cin > 32 || W % 8 != 0 || !aligned(x, 16) || lb == 0 || lb > kLdsMax)
-            return fail(CT_EUNSUPPORTED, "convT3d_scale_pool_bias: bf16 path needs Cin <= 32, "
-                        "W a multiple of 8 (W <= 4096) and a 16-byte aligned x");
-    }
+        return fail(CT_EINVAL, "%s: tensor size overflows", fn);
     if (overlap(out, no, x, nx) || overlap(out, no, w, nw) ||
         overlap(out, no, conv_bias, Cout * 4) || overlap(out, no, bias, Cout * 4))
-        return fail(CT_EINVAL, "convT3d_scale_pool_bias: out overlaps an input");
+        return fail(CT_EINVAL, "%s: out overlaps an input", fn);
+    if (x_dtype != w_dtype)
+        return fail(CT_EUNSUPPORTED, "%s: x and w dtypes must match", fn);
 
+    // The pages' geometry (k3 s2 p1, 2-pool) runs on the matrix-core kernels
+    // when their own limits hold; everything else on the general kernel.
+    bool fast = k == 3 && stride == 2 && pad == 1 && out_pad == 0 && pool_k == 2 && ps == 2;
+    if (fast) {
+        const int64_t wblocks = (pd[2] + 15) / 16;
+        int64_t nmb, xitem, oitem;
+        fast = prod({N, pd[0], pd[1], wblocks}, &nmb) && nmb <= kI32Max / 8 &&
+               prod({Cin, D, H, W}, &xitem) && xitem <= kI32Max &&
+               prod({Cout, pd[0], pd[1], pd[2]}, &oitem) && oitem <= kI32Max &&
+               Cout <= 65535 * 16;
+        if (x_dtype == CT_F32) {
+            fast = fast && Cin <= 128;
+        } else {
+            const size_t lb = ct::fused3d_bf16_lds_bytes(Cin, W);
+            fast = fast && Cin <= 32 && W % 8 == 0 && aligned(x, 16) && lb != 0 && lb <= kLdsMax;
+        }
+    }
     hipError_t e;
-    if (x_dtype == CT_F32)
+    if (fast && x_dtype == CT_F32) {
         e = ct::launch_fused3d_f32((const float *)x, (const float *)w, conv_bias, bias, scale1,
                                    scale2, N, Cin, D, H, W, Cout, out, (hipStream_t)stream);
-    else
+    } else if (fast) {
         e = ct::launch_fused3d_bf16((const uint16_t *)x, (const uint16_t *)w, conv_bias, bias,
                                     scale1, scale2, N, Cin, D, H, W, Cout, out,
                                     (hipStream_t)stream);
+    } else {
+        if (pool_k > kGenericMaxTap)
+            return fail(CT_EUNSUPPORTED, "%s: pool_k > %d is not implemented", fn, kGenericMaxTap);
+        e = ct::launch_fused3d_generic(x, w, x_dtype == CT_BF16, conv_bias, bias, scale1, scale2,
+                                       N, Cin, D, H, W, Cout, k, stride, pad, out_pad, pool_k, ps,
+                                       out, (hipStream_t)stream);
+    }
     return hip_status(e, "convT3d_scale_pool_bias launch");
+}
+
+ct_status ct_convT3d(const void *x, int x_dtype, const void *w, int w_dtype, const float *bias,
+                     int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W, int64_t Cout,
+                     int k, int stride, int pad, int out_pad, float *out, void *stream)
+{
+    const char *fn = "convT3d";
+    int xs, ws;
+    int64_t od[3];
+    ct_status st = check_convT3d(fn, x, x_dtype, w, w_dtype, N, Cin, D, H, W, Cout, k, stride,
+                                 pad, out_pad, out, &xs, &ws, od);
+    if (st != CT_OK) return st;
+    if (bias && !aligned(bias, 4)) return fail(CT_EINVAL, "%s: misaligned pointer", fn);
+    int64_t nx, nw, no;
+    if (!prod({N, Cin, D, H, W, (int64_t)xs}, &nx) ||
+        !prod({Cin, Cout, (int64_t)k, (int64_t)k, (int64_t)k, (int64_t)ws}, &nw) ||
+        !prod({N, Cout, od[0], od[1], od[2], 4}, &no))
+        return fail(CT_EINVAL, "%s: tensor size overflows", fn);
+    if (overlap(out, no, x, nx) || overlap(out, no, w, nw) || overlap(out, no, bias, Cout * 4))
+        return fail(CT_EINVAL, "%s: out overlaps an input", fn);
+    if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "%s: x and w dtypes must match", fn);
+    hipError_t e = ct::launch_convT3d_generic(x, w, x_dtype == CT_BF16, bias, N, Cin, D, H, W,
+                                              Cout, k, stride, pad, out_pad, out,
+                                              (hipStream_t)stream);
+    return hip_status(e, "convT3d launch");
 }
 
 ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
@@ -189,7 +264,7 @@ ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t 
     if (!x || !out) return fail(CT_EINVAL, "avgpool3d: x and out must be non-null");
     if (N < 1 || C < 1 || D < 1 || H < 1 || W < 1)
         return fail(CT_EINVAL, "avgpool3d: sizes must be >= 1");
-    if (k < 1 || stride < 0 || pad < 0 || 2 * pad > k ||
+    if (k < 1 || stride < 0 || pad < 0 || 2 * (int64_t)pad > k ||
         (count_include_pad != 0 && count_include_pad != 1))
         return fail(CT_EINVAL, "avgpool3d: invalid geometry k=%d stride=%d pad=%d count_include_pad=%d "
                     "(pad must be <= k/2)", k, stride, pad, count_include_pad);
@@ -201,19 +276,32 @@ ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t 
         if (o[i] <= 0)
             return fail(CT_EINVAL, "avgpool3d: empty output along axis %d", i);
     }
-    if (k != 3 || s != 2 || pad != 1 || count_include_pad != 1)
-        return fail(CT_EUNSUPPORTED, "avgpool3d: only k=3 stride=2 pad=1 count_include_pad=1 is implemented");
     if (!aligned(x, 4) || !aligned(out, 4)) return fail(CT_EINVAL, "avgpool3d: misaligned pointer");
     int64_t nx, no, slice;
     if (!prod({N, C, D, H, W, 4}, &nx) || !prod({N, C, o[0], o[1], o[2], 4}, &no) ||
         !prod({D, H, W}, &slice))
         return fail(CT_EINVAL, "avgpool3d: tensor size overflows");
-    const int64_t hgroups = (o[1] + 15) / 16, dchunks = (o[0] + 15) / 16, wchunks = (o[2] + 127) / 128;
-    int64_t nwg;
-    if (slice > kI32Max || !prod({N, C, hgroups, dchunks, wchunks}, &nwg) || nwg > kI32Max)
-        return fail(CT_EUNSUPPORTED, "avgpool3d: problem too large for one launch");
     if (overlap(out, no, x, nx)) return fail(CT_EINVAL, "avgpool3d: out overlaps x");
-    hipError_t e = ct::launch_avgpool3d_k3s2p1(x, N * C, D, H, W, out, (hipStream_t)stream);
+
+    bool fast = k == 3 && s == 2 && pad == 1 && count_include_pad == 1;
+    if (fast) {
+        const int64_t hgroups = (o[1] + 15) / 16, dchunks = (o[0] + 15) / 16,
+                      wchunks = (o[2] + 127) / 128;
+        int64_t nwg;
+        fast = slice <= kI32Max && prod({N, C, hgroups, dchunks, wchunks}, &nwg) && nwg <= kI32Max;
+    }
+    hipError_t e;
+    if (fast) {
+        e = ct::launch_avgpool3d_k3s2p1(x, N * C, D, H, W, out, (hipStream_t)stream);
+    } else {
+        if (D > kGenericMaxLen || H > kGenericMaxLen || W > kGenericMaxLen || k > kGenericMaxTap ||
+            s > kGenericMaxLen)
+            return fail(CT_EUNSUPPORTED, "avgpool3d: sizes beyond the general kernel's index range "
+                        "(lengths and stride <= %lld, k <= %d)", (long long)kGenericMaxLen,
+                        kGenericMaxTap);
+        e = ct::launch_avgpool3d_generic(x, N * C, D, H, W, k, s, pad, count_include_pad, out,
+                                         (hipStream_t)stream);
+    }
     return hip_status(e, "avgpool3d launch");
 }
 
@@ -225,34 +313,46 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
     const int xs = dtype_size(x_dtype), ws = dtype_size(w_dtype);
     if (!xs || !ws) return fail(CT_EINVAL, "convT1d: unknown dtype (%d, %d)", x_dtype, w_dtype);
     if (N < 1 || Cin < 1 || L < 1 || Cout < 1) return fail(CT_EINVAL, "convT1d: sizes must be >= 1");
-    if (K < 1 || stride < 1 || pad < 0 || dilation < 1 || out_pad < 0)
-        return fail(CT_EINVAL, "convT1d: invalid geometry K=%d stride=%d pad=%d dilation=%d out_pad=%d",
-                    K, stride, pad, dilation, out_pad);
+    if (K < 1 || stride < 1 || pad < 0 || dilation < 1 || out_pad < 0 ||
+        out_pad >= (stride > dilation ? stride : dilation))
+        return fail(CT_EINVAL, "convT1d: invalid geometry K=%d stride=%d pad=%d dilation=%d out_pad=%d "
+                    "(out_pad must be < max(stride, dilation))", K, stride, pad, dilation, out_pad);
     const int64_t Lo = ct_convT_out_len(L, K, stride, pad, out_pad, dilation);
     if (Lo <= 0) return fail(CT_EINVAL, "convT1d: empty output (L_out=%lld)", (long long)Lo);
-    if (stride != 1 || pad != 0 || out_pad != 0)
-        return fail(CT_EUNSUPPORTED, "convT1d: only stride=1 pad=0 out_pad=0 is implemented");
-    if (x_dtype != CT_F32 || w_dtype != CT_F32)
-        return fail(CT_EUNSUPPORTED, "convT1d: only fp32 x and w are implemented");
-    if (!aligned(x, 4) || !aligned(w, 4) || !aligned(out, 4) || (bias && !aligned(bias, 4)))
+    if (!aligned(x, xs) || !aligned(w, ws) || !aligned(out, 4) || (bias && !aligned(bias, 4)))
         return fail(CT_EINVAL, "convT1d: misaligned pointer");
     int64_t nx, nw, no;
-    if (!prod({N, Cin, L, 4}, &nx) || !prod({Cin, Cout, (int64_t)K, 4}, &nw) ||
+    if (!prod({N, Cin, L, (int64_t)xs}, &nx) || !prod({Cin, Cout, (int64_t)K, (int64_t)ws}, &nw) ||
         !prod({N, Cout, Lo, 4}, &no))
         return fail(CT_EINVAL, "convT1d: tensor size overflows");
-    const int64_t tiles = (Lo + 255) / 256;
-    int64_t ntiles;
-    if (Lo > kI32Max - 256 || !prod({N, tiles}, &ntiles) || ntiles > kI32Max ||
-        (Cout + 63) / 64 > 65535 || Cin > 4096 || K > 4096 ||
-        (int64_t)dilation * (K - 1) > 65536)
-        return fail(CT_EUNSUPPORTED, "convT1d: problem too large for one launch");
-    if (ct::convT1d_f32_lds_bytes(Cin, K, dilation) > kLdsMax)
-        return fail(CT_EUNSUPPORTED, "convT1d: Cin*K and dilation*(K-1) too large for LDS "
-                    "(needs %zu bytes)", ct::convT1d_f32_lds_bytes(Cin, K, dilation));
     if (overlap(out, no, x, nx) || overlap(out, no, w, nw) || overlap(out, no, bias, Cout * 4))
         return fail(CT_EINVAL, "convT1d: out overlaps an input");
-    hipError_t e = ct::launch_convT1d_f32((const float *)x, (const float *)w, bias, N, Cin, L,
-                                          Cout, K, dilation, out, (hipStream_t)stream);
+    if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "convT1d: x and w dtypes must match");
+
+    // Stride 1, pad 0 in fp32 runs on the matrix-core kernel when its tiles
+    // fit; everything else on the general kernel.
+    bool fast = x_dtype == CT_F32 && stride == 1 && pad == 0 && out_pad == 0;
+    if (fast) {
+        const int64_t tiles = (Lo + 255) / 256;
+        int64_t ntiles;
+        fast = Lo <= kI32Max - 256 && prod({N, tiles}, &ntiles) && ntiles <= kI32Max &&
+               (Cout + 63) / 64 <= 65535 && Cin <= 4096 && K <= 4096 &&
+               (int64_t)dilation * (K - 1) <= 65536 &&
+               ct::convT1d_f32_lds_bytes(Cin, K, dilation) <= kLdsMax;
+    }
+    hipError_t e;
+    if (fast) {
+        e = ct::launch_convT1d_f32((const float *)x, (const float *)w, bias, N, Cin, L, Cout, K,
+                                   dilation, out, (hipStream_t)stream);
+    } else {
+        if (Lo > kGenericMaxLen || L > kGenericMaxLen || Cin > kGenericMaxLen ||
+            Cout > kGenericMaxLen || pad > kGenericMaxLen ||
+            (int64_t)dilation * (K - 1) > kGenericMaxLen)
+            return fail(CT_EUNSUPPORTED, "convT1d: sizes beyond the general kernel's index range "
+                        "(lengths, pad and dilation*(K-1) <= %lld)", (long long)kGenericMaxLen);
+        e = ct::launch_convT1d_generic(x, w, x_dtype == CT_BF16, bias, N, Cin, L, Cout, K, stride,
+                                       pad, dilation, out_pad, out, (hipStream_t)stream);
+    }
     return hip_status(e, "convT1d launch");
 }
 

@@ -36,6 +36,24 @@ hipError_t launch_convT1d_f32(const float *x, const float *w,
                               int64_t L, int64_t Cout, int K, int dilation,
                               float *out, hipStream_t stream);
 
+// General-geometry kernels (generic.hip): one thread per output element,
+// fp32 or bf16 (bf16 = true) x and w, fp32 accumulation and output.
+hipError_t launch_fused3d_generic(const void *x, const void *w, bool bf16,
+                                  const float *conv_bias, const float *bias, float s1, float s2,
+                                  int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                  int64_t Cout, int k, int s, int p, int op, int pk, int ps,
+                                  float *out, hipStream_t stream);
+hipError_t launch_convT3d_generic(const void *x, const void *w, bool bf16, const float *bias,
+                                  int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                                  int64_t Cout, int k, int s, int p, int op, float *y,
+                                  hipStream_t stream);
+hipError_t launch_avgpool3d_generic(const float *x, int64_t NC, int64_t D, int64_t H, int64_t W,
+                                    int k, int s, int p, int include_pad, float *out,
+                                    hipStream_t stream);
+hipError_t launch_convT1d_generic(const void *x, const void *w, bool bf16, const float *bias,
+                                  int64_t N, int64_t Cin, int64_t L, int64_t Cout, int K, int s,
+                                  int p, int dil, int op, float *y, hipStream_t stream);
+
 // Workgroup index remapped so that each XCD (blocks are dealt to the 8 XCDs
 // round-robin) works on one contiguous range of logical tiles: neighbouring
 // tiles then share that XCD's L2.

@@ -98,7 +98,6 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_bytes[];
     unsigned short *lds = reinterpret_cast<unsigned short *>(lds_bytes);
     unsigned short *raw = lds;                                // prologue: raw weights
-    unsigned short *afrag = lds + raw_bytes() / 2;            // prologue: fragments
     unsigned short *slab = lds;                               // main loop: input slab
     float *epi = reinterpret_cast<float *>(lds_bytes + epi_offset(kTH, W, CS));   // [64]
 
