@@ -16,6 +16,8 @@ timed on a bounded sample of the same workloads.
 
   python bench.py [--steps K] [--warmup W] [--ops a,b] [--no-cpu-baseline]
   python bench.py --ops copy        # plain 1 GiB device copy (counter calibration)
+  python bench.py --ops fused3d_f32,unfused3d_f32   # fusion vs materialising the
+                                    # [128,16,31,63,63] pre-pool tensor, then a 2-pool
 """
 from __future__ import annotations
 
@@ -41,6 +43,7 @@ OP_SOURCES = {
     "avgpool3d": "avgpool3d.hip",
     "convT1d": "convT1d_f32.hip",
     "fused3d_bf16": "fused3d_bf16.hip",
+    "unfused3d_f32": "generic.hip",
 }
 
 
@@ -169,6 +172,32 @@ def make_ops(names, dev):
 
         ops.append(Op("fused3d_bf16", run, nbytes(x, w, b, out), 2 * out.numel() * 32 * 8,
                       "hbm", HBM_PEAK_GBS, [wl.description], sample))
+
+    if "unfused3d_f32" in names:
+        # The chain without fusion: ConvTranspose3d writes the full pre-pool
+        # tensor, a separate 2-pool reads it back.  (The scale / bias steps
+        # would add further passes over the pooled tensor; they are left out,
+        # so this is a lower bound on the unfused chain's time.)
+        wl = synth.WORKLOADS["c2"]
+        log(f"inputs: {wl.description} (unfused)")
+        t = synth.make_inputs(wl)
+        x, w = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w"))
+        y = torch.empty((128, 16, 31, 63, 63), dtype=torch.float32, device=dev)
+        out = torch.empty((128, 16, 15, 31, 31), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, y=y, out=out):
+            ct.ct_convT3d(x, w, None, 2, 1, 0, out=y)
+            ct.ct_avgpool3d(y, 2, 2, 0, True, out=out)
+
+        def sample(t=t):
+            import oracle
+            n = 8
+            t0 = time.perf_counter()
+            oracle.avgpool3d(oracle.convT3d(t["x"][:n], t["w"], None, 2, 1, 0), 2, 2, 0, True)
+            return time.perf_counter() - t0, n / 128.0, f"{n} of 128 batch items"
+
+        ops.append(Op("unfused3d_f32", run, nbytes(x, w, y, y, out), 2 * y.numel() * 3 * 27 // 8,
+                      "hbm", HBM_PEAK_GBS, [wl.description + ", unfused"], sample))
 
     if "copy" in names:
         n = 1 << 28                      # 1 GiB of fp32

@@ -14,13 +14,40 @@
 //    ((S/pk^3 + conv_bias)*scale1 + bias)*scale2 (the conv bias passes
 //    through the window mean unchanged).
 // One thread per output element, consecutive threads along the innermost
-// output axis (coalesced stores); grid-stride over 64-bit element counts.
+// output axis (coalesced stores), grid-stride.  Element indices are 32-bit
+// when the output has fewer than 2^31 elements, and every division by a
+// runtime size (index decode, stride) is then a multiply-high by a
+// precomputed reciprocal instead of a software division loop.
 #include "ct_internal.h"
 
 namespace ct {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Unsigned division by a run-time constant d (1 <= d < 2^32), after
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication" (PLDI 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (umulhi(m, n) + n) >> l for
+// every 32-bit n (the sum is formed in 64 bits).  64-bit dividends use the
+// ordinary division.
+struct Div {
+    uint32_t d, m, l;
+    __device__ __forceinline__ uint32_t q(uint32_t n) const
+    {
+        const uint32_t t = __umulhi(m, n);
+        return (uint32_t)(((uint64_t)t + n) >> l);
+    }
+    __device__ __forceinline__ uint64_t q(uint64_t n) const { return n / d; }
+};
+
+Div make_div(uint32_t d)
+{
+    uint32_t l = 0;
+    while (l < 32 && (uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return {d, (uint32_t)m, l};
+}
 
 template <typename T> __device__ __forceinline__ float ld(const T *p, int64_t i);
 template <> __device__ __forceinline__ float ld<float>(const float *p, int64_t i) { return p[i]; }
@@ -29,57 +56,51 @@ template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, int
     return __uint_as_float(((unsigned)p[i]) << 16);   // bf16 -> fp32, exact
 }
 
-// Input index feeding output position o through tap k of a dilated 1D
-// transposed convolution, or -1 when the division is inexact or the index
-// falls outside [0, in).
-__device__ __forceinline__ int in_index(int o, int k, int stride, int pad, int dil, int in)
-{
-    const int t = o + pad - dil * k;
-    if (t < 0 || t % stride) return -1;
-    const int i = t / stride;
-    return i < in ? i : -1;
-}
+// Geometry of a 3D transposed convolution (dilation 1) and the pool after it.
+struct Geo3 {
+    int Cin, D, H, W, Cout, k, s, p, pk, ps;
+};
 
-// Taps of one axis of a dilation-1 transposed convolution that feed output
-// position o: tap k reaches o from input (o + pad - k) / stride when that
-// division is exact, so the valid taps are k0, k0 + stride, ... with
-// k0 = (o + pad) mod stride, and their inputs i0, i0 - 1, ...  The range is
-// clipped to taps below k and inputs inside [0, in); n <= 0 means none.
+// Taps of one axis that feed output position o: tap k reaches o from input
+// (o + pad - k) / stride when that division is exact, so the valid taps are
+// k0, k0 + stride, ... with k0 = (o + pad) mod stride, and their inputs
+// i0, i0 - 1, ...  The range is clipped to taps below k and inputs inside
+// [0, in); n <= 0 means none.
 struct Taps {
     int k0, i0, n;
 };
 
-__device__ __forceinline__ Taps axis_taps(int o, int k, int stride, int pad, int in)
+__device__ __forceinline__ Taps axis_taps(int o, int k, const Div &ds, int pad, int in)
 {
-    const int t = o + pad;
-    const int k0 = t % stride, i0 = t / stride;
-    const int jlo = i0 - (in - 1) > 0 ? i0 - (in - 1) : 0;   // input <= in - 1
-    int jhi = k0 < k ? (k - 1 - k0) / stride : -1;          // tap < k
-    if (jhi > i0) jhi = i0;                                 // input >= 0
-    return {k0 + jlo * stride, i0 - jlo, jhi - jlo + 1};
+    const uint32_t t = (uint32_t)(o + pad);
+    const int i0 = (int)ds.q(t), k0 = (int)(t - (uint32_t)i0 * ds.d);
+    const int jlo = i0 - (in - 1) > 0 ? i0 - (in - 1) : 0;          // input <= in - 1
+    int jhi = k0 < k ? (int)ds.q((uint32_t)(k - 1 - k0)) : -1;      // tap < k
+    if (jhi > i0) jhi = i0;                                         // input >= 0
+    return {k0 + jlo * (int)ds.d, i0 - jlo, jhi - jlo + 1};
 }
 
 // ConvTranspose3d value (without bias) at output (co, od, oh, ow) of one batch
 // item; xn points at that item's [Cin][D][H][W] block.
 template <typename T>
-__device__ float convT3d_point(const T *__restrict__ xn, const T *__restrict__ w, int Cin,
-                               int D, int H, int W, int Cout, int k, int s, int p, int co,
-                               int od, int oh, int ow)
+__device__ float convT3d_point(const T *__restrict__ xn, const T *__restrict__ w, const Geo3 &g,
+                               const Div &ds, int co, int od, int oh, int ow)
 {
     float acc = 0.0f;
-    const int64_t HW = (int64_t)H * W, DHW = (int64_t)D * HW, k3 = (int64_t)k * k * k;
-    const int64_t wstride = (int64_t)Cout * k3;   // between input channels
-    const Taps td = axis_taps(od, k, s, p, D), th = axis_taps(oh, k, s, p, H),
-               tw = axis_taps(ow, k, s, p, W);
+    const int k = g.k, s = g.s;
+    const int64_t HW = (int64_t)g.H * g.W, DHW = (int64_t)g.D * HW, k3 = (int64_t)k * k * k;
+    const int64_t wstride = (int64_t)g.Cout * k3;   // between input channels
+    const Taps td = axis_taps(od, k, ds, g.p, g.D), th = axis_taps(oh, k, ds, g.p, g.H),
+               tw = axis_taps(ow, k, ds, g.p, g.W);
     for (int a = 0; a < td.n; ++a) {
         const int kd = td.k0 + a * s, id = td.i0 - a;
         for (int b = 0; b < th.n; ++b) {
             const int kh = th.k0 + b * s, ih = th.i0 - b;
             for (int c = 0; c < tw.n; ++c) {
                 const int kw = tw.k0 + c * s, iw = tw.i0 - c;
-                const int64_t xo = (int64_t)id * HW + (int64_t)ih * W + iw;
+                const int64_t xo = (int64_t)id * HW + (int64_t)ih * g.W + iw;
                 const int64_t wo = (int64_t)co * k3 + ((int64_t)kd * k + kh) * k + kw;
-                for (int ci = 0; ci < Cin; ++ci)
+                for (int ci = 0; ci < g.Cin; ++ci)
                     acc = __builtin_fmaf(ld(xn, ci * DHW + xo), ld(w, ci * wstride + wo), acc);
             }
         }
@@ -87,29 +108,34 @@ __device__ float convT3d_point(const T *__restrict__ xn, const T *__restrict__ w
     return acc;
 }
 
-template <typename T>
+// Splits a flat index into (rest, coordinate) for one axis of size d.
+template <typename I>
+__device__ __forceinline__ int peel(I &e, const Div &dv)
+{
+    const I q = dv.q(e);
+    const int c = (int)(e - q * (I)dv.d);
+    e = q;
+    return c;
+}
+
+template <typename T, typename I>
 __global__ __launch_bounds__(kThreads)
 void fused3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
                             const float *__restrict__ conv_bias, const float *__restrict__ bias,
-                            float s1, float s2, float inv, int Cin, int D, int H, int W,
-                            int Cout, int k, int s, int p, int pk, int ps, int Dp, int Hp,
-                            int Wp, int64_t total, float *__restrict__ out)
+                            float s1, float s2, float inv, Geo3 g, Div dWp, Div dHp, Div dDp,
+                            Div dCout, Div ds, I total, float *__restrict__ out)
 {
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * kThreads) {
-        int64_t t = e;
-        const int wp = (int)(t % Wp); t /= Wp;
-        const int hp = (int)(t % Hp); t /= Hp;
-        const int dp = (int)(t % Dp); t /= Dp;
-        const int co = (int)(t % Cout);
-        const int64_t n = t / Cout;
-        const T *xn = x + n * Cin * (int64_t)D * H * W;
+    const int64_t xitem = (int64_t)g.Cin * g.D * g.H * g.W;
+    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+        I t = e;
+        const int wp = peel(t, dWp), hp = peel(t, dHp), dp = peel(t, dDp), co = peel(t, dCout);
+        const T *xn = x + (int64_t)t * xitem;
         float S = 0.0f;
-        for (int a = 0; a < pk; ++a)
-            for (int b = 0; b < pk; ++b)
-                for (int c = 0; c < pk; ++c)
-                    S += convT3d_point(xn, w, Cin, D, H, W, Cout, k, s, p, co,
-                                       dp * ps + a, hp * ps + b, wp * ps + c);
+        for (int a = 0; a < g.pk; ++a)
+            for (int b = 0; b < g.pk; ++b)
+                for (int c = 0; c < g.pk; ++c)
+                    S += convT3d_point(xn, w, g, ds, co, dp * g.ps + a, hp * g.ps + b,
+                                       wp * g.ps + c);
         float v = S * inv;
         v = (v + (conv_bias ? conv_bias[co] : 0.0f)) * s1;
         v = (v + (bias ? bias[co] : 0.0f)) * s2;
@@ -117,40 +143,31 @@ void fused3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
     }
 }
 
-template <typename T>
+template <typename T, typename I>
 __global__ __launch_bounds__(kThreads)
 void convT3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
-                            const float *__restrict__ bias, int Cin, int D, int H, int W,
-                            int Cout, int k, int s, int p, int Do, int Ho, int Wo, int64_t total,
-                            float *__restrict__ y)
+                            const float *__restrict__ bias, Geo3 g, Div dWo, Div dHo, Div dDo,
+                            Div dCout, Div ds, I total, float *__restrict__ y)
 {
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * kThreads) {
-        int64_t t = e;
-        const int ow = (int)(t % Wo); t /= Wo;
-        const int oh = (int)(t % Ho); t /= Ho;
-        const int od = (int)(t % Do); t /= Do;
-        const int co = (int)(t % Cout);
-        const int64_t n = t / Cout;
-        const T *xn = x + n * Cin * (int64_t)D * H * W;
-        y[e] = convT3d_point(xn, w, Cin, D, H, W, Cout, k, s, p, co, od, oh, ow) +
-               (bias ? bias[co] : 0.0f);
+    const int64_t xitem = (int64_t)g.Cin * g.D * g.H * g.W;
+    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+        I t = e;
+        const int ow = peel(t, dWo), oh = peel(t, dHo), od = peel(t, dDo), co = peel(t, dCout);
+        const T *xn = x + (int64_t)t * xitem;
+        y[e] = convT3d_point(xn, w, g, ds, co, od, oh, ow) + (bias ? bias[co] : 0.0f);
     }
 }
 
+template <typename I>
 __global__ __launch_bounds__(kThreads)
 void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, int k, int s,
-                              int p, int include_pad, float kvol, int Do, int Ho, int Wo,
-                              int64_t total, float *__restrict__ out)
+                              int p, int include_pad, float kvol, Div dWo, Div dHo, Div dDo,
+                              I total, float *__restrict__ out)
 {
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * kThreads) {
-        int64_t t = e;
-        const int ow = (int)(t % Wo); t /= Wo;
-        const int oh = (int)(t % Ho); t /= Ho;
-        const int od = (int)(t % Do);
-        const int64_t sl = t / Do;
-        const float *xs = x + sl * (int64_t)D * H * W;
+    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+        I t = e;
+        const int ow = peel(t, dWo), oh = peel(t, dHo), od = peel(t, dDo);
+        const float *xs = x + (int64_t)t * D * H * W;
         float sum = 0.0f;
         int cnt = 0;
         for (int kd = 0; kd < k; ++kd) {
@@ -171,23 +188,24 @@ void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, 
     }
 }
 
-template <typename T>
+template <typename T, typename I>
 __global__ __launch_bounds__(kThreads)
 void convT1d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
                             const float *__restrict__ bias, int Cin, int L, int Cout, int K,
-                            int s, int p, int dil, int Lo, int64_t total, float *__restrict__ y)
+                            int p, int dil, Div dLo, Div dCout, Div ds, I total,
+                            float *__restrict__ y)
 {
-    for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * kThreads) {
-        const int o = (int)(e % Lo);
-        int64_t t = e / Lo;
-        const int co = (int)(t % Cout);
-        const int64_t n = t / Cout;
-        const T *xn = x + n * Cin * (int64_t)L;
+    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+        I t = e;
+        const int o = peel(t, dLo), co = peel(t, dCout);
+        const T *xn = x + (int64_t)t * Cin * L;
         float acc = 0.0f;
         for (int kk = 0; kk < K; ++kk) {
-            const int i = in_index(o, kk, s, p, dil, L);
-            if (i < 0) continue;
+            // input (o + pad - dil*k) / stride when exact and inside [0, L)
+            const int tt = o + p - dil * kk;
+            if (tt < 0) break;                      // later taps only go lower
+            const int i = (int)ds.q((uint32_t)tt);
+            if (i * (int)ds.d != tt || i >= L) continue;
             for (int ci = 0; ci < Cin; ++ci)
                 acc = __builtin_fmaf(ld(xn, (int64_t)ci * L + i),
                                      ld(w, ((int64_t)ci * Cout + co) * K + kk), acc);
@@ -205,6 +223,9 @@ unsigned grid_for(int64_t total)
     return (unsigned)(blocks < kMaxBlocks ? blocks : kMaxBlocks);
 }
 
+// 32-bit element indices when the grid-stride loop cannot wrap.
+bool small_index(int64_t total) { return total < (int64_t(1) << 31); }
+
 }  // namespace
 
 hipError_t launch_fused3d_generic(const void *x, const void *w, bool bf16,
@@ -218,16 +239,19 @@ hipError_t launch_fused3d_generic(const void *x, const void *w, bool bf16,
     const int64_t Dp = (Do - pk) / ps + 1, Hp = (Ho - pk) / ps + 1, Wp = (Wo - pk) / ps + 1;
     const int64_t total = N * Cout * Dp * Hp * Wp;
     const float inv = (float)(1.0 / ((double)pk * pk * pk));
-    if (bf16)
-        hipLaunchKernelGGL(fused3d_generic_kernel<uint16_t>, dim3(grid_for(total)), dim3(kThreads), 0,
-                           stream, (const uint16_t *)x, (const uint16_t *)w, conv_bias, bias, s1, s2,
-                           inv, (int)Cin, (int)D, (int)H, (int)W, (int)Cout, k, s, p, pk, ps,
-                           (int)Dp, (int)Hp, (int)Wp, total, out);
-    else
-        hipLaunchKernelGGL(fused3d_generic_kernel<float>, dim3(grid_for(total)), dim3(kThreads), 0,
-                           stream, (const float *)x, (const float *)w, conv_bias, bias, s1, s2,
-                           inv, (int)Cin, (int)D, (int)H, (int)W, (int)Cout, k, s, p, pk, ps,
-                           (int)Dp, (int)Hp, (int)Wp, total, out);
+    const Geo3 g{(int)Cin, (int)D, (int)H, (int)W, (int)Cout, k, s, p, pk, ps};
+    const Div dW = make_div((uint32_t)Wp), dH = make_div((uint32_t)Hp), dD = make_div((uint32_t)Dp),
+              dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s);
+    const dim3 grid(grid_for(total)), block(kThreads);
+#define CT_FUSED(T, I)                                                                          \
+    hipLaunchKernelGGL((fused3d_generic_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
+                       (const T *)w, conv_bias, bias, s1, s2, inv, g, dW, dH, dD, dC, dS,       \
+                       (I)total, out)
+    if (bf16 && small_index(total)) CT_FUSED(uint16_t, uint32_t);
+    else if (bf16) CT_FUSED(uint16_t, uint64_t);
+    else if (small_index(total)) CT_FUSED(float, uint32_t);
+    else CT_FUSED(float, uint64_t);
+#undef CT_FUSED
     return hipGetLastError();
 }
 
@@ -239,14 +263,18 @@ hipError_t launch_convT3d_generic(const void *x, const void *w, bool bf16, const
     const int64_t Do = (D - 1) * s - 2 * p + k + op, Ho = (H - 1) * s - 2 * p + k + op,
                   Wo = (W - 1) * s - 2 * p + k + op;
     const int64_t total = N * Cout * Do * Ho * Wo;
-    if (bf16)
-        hipLaunchKernelGGL(convT3d_generic_kernel<uint16_t>, dim3(grid_for(total)), dim3(kThreads), 0,
-                           stream, (const uint16_t *)x, (const uint16_t *)w, bias, (int)Cin, (int)D,
-                           (int)H, (int)W, (int)Cout, k, s, p, (int)Do, (int)Ho, (int)Wo, total, y);
-    else
-        hipLaunchKernelGGL(convT3d_generic_kernel<float>, dim3(grid_for(total)), dim3(kThreads), 0,
-                           stream, (const float *)x, (const float *)w, bias, (int)Cin, (int)D,
-                           (int)H, (int)W, (int)Cout, k, s, p, (int)Do, (int)Ho, (int)Wo, total, y);
+    const Geo3 g{(int)Cin, (int)D, (int)H, (int)W, (int)Cout, k, s, p, 1, 1};
+    const Div dW = make_div((uint32_t)Wo), dH = make_div((uint32_t)Ho), dD = make_div((uint32_t)Do),
+              dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s);
+    const dim3 grid(grid_for(total)), block(kThreads);
+#define CT_CONV(T, I)                                                                           \
+    hipLaunchKernelGGL((convT3d_generic_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
+                       (const T *)w, bias, g, dW, dH, dD, dC, dS, (I)total, y)
+    if (bf16 && small_index(total)) CT_CONV(uint16_t, uint32_t);
+    else if (bf16) CT_CONV(uint16_t, uint64_t);
+    else if (small_index(total)) CT_CONV(float, uint32_t);
+    else CT_CONV(float, uint64_t);
+#undef CT_CONV
     return hipGetLastError();
 }
 
@@ -257,9 +285,17 @@ hipError_t launch_avgpool3d_generic(const float *x, int64_t NC, int64_t D, int64
     const int64_t Do = (D + 2 * p - k) / s + 1, Ho = (H + 2 * p - k) / s + 1,
                   Wo = (W + 2 * p - k) / s + 1;
     const int64_t total = NC * Do * Ho * Wo;
-    hipLaunchKernelGGL(avgpool3d_generic_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
-                       x, (int)D, (int)H, (int)W, k, s, p, include_pad, (float)k * k * k, (int)Do,
-                       (int)Ho, (int)Wo, total, out);
+    const Div dW = make_div((uint32_t)Wo), dH = make_div((uint32_t)Ho), dD = make_div((uint32_t)Do);
+    const float kvol = (float)k * k * k;
+    const dim3 grid(grid_for(total)), block(kThreads);
+    if (small_index(total))
+        hipLaunchKernelGGL((avgpool3d_generic_kernel<uint32_t>), grid, block, 0, stream, x, (int)D,
+                           (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, dD,
+                           (uint32_t)total, out);
+    else
+        hipLaunchKernelGGL((avgpool3d_generic_kernel<uint64_t>), grid, block, 0, stream, x, (int)D,
+                           (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, dD,
+                           (uint64_t)total, out);
     return hipGetLastError();
 }
 
@@ -267,16 +303,19 @@ hipError_t launch_convT1d_generic(const void *x, const void *w, bool bf16, const
                                   int64_t N, int64_t Cin, int64_t L, int64_t Cout, int K, int s,
                                   int p, int dil, int op, float *y, hipStream_t stream)
 {
-    const int64_t Lo = (L - 1) * s - 2 * p + dil * (K - 1) + op + 1;
+    const int64_t Lo = (L - 1) * s - 2 * p + (int64_t)dil * (K - 1) + op + 1;
     const int64_t total = N * Cout * Lo;
-    if (bf16)
-        hipLaunchKernelGGL(convT1d_generic_kernel<uint16_t>, dim3(grid_for(total)), dim3(kThreads), 0,
-                           stream, (const uint16_t *)x, (const uint16_t *)w, bias, (int)Cin, (int)L,
-                           (int)Cout, K, s, p, dil, (int)Lo, total, y);
-    else
-        hipLaunchKernelGGL(convT1d_generic_kernel<float>, dim3(grid_for(total)), dim3(kThreads), 0,
-                           stream, (const float *)x, (const float *)w, bias, (int)Cin, (int)L,
-                           (int)Cout, K, s, p, dil, (int)Lo, total, y);
+    const Div dL = make_div((uint32_t)Lo), dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s);
+    const dim3 grid(grid_for(total)), block(kThreads);
+#define CT_C1D(T, I)                                                                            \
+    hipLaunchKernelGGL((convT1d_generic_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
+                       (const T *)w, bias, (int)Cin, (int)L, (int)Cout, K, p, dil, dL, dC, dS,  \
+                       (I)total, y)
+    if (bf16 && small_index(total)) CT_C1D(uint16_t, uint32_t);
+    else if (bf16) CT_C1D(uint16_t, uint64_t);
+    else if (small_index(total)) CT_C1D(float, uint32_t);
+    else CT_C1D(float, uint64_t);
+#undef CT_C1D
     return hipGetLastError();
 }
 
