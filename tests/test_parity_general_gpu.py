@@ -123,6 +123,13 @@ CONVT3D = [
     (1, 2, 3, 3, 4, 5, 4, 3, 1, 2, True, "f32"),
     (1, 4, 4, 3, 3, 3, 2, 1, 0, 0, False, "f32"),
     (2, 5, 6, 4, 4, 6, 3, 2, 1, 0, True, "bf16"),
+    # the k3 s2 p1 parity kernel (Cin <= 8), both output paddings, edges
+    (2, 3, 16, 5, 7, 9, 3, 2, 1, 1, True, "f32"),
+    (1, 8, 5, 3, 4, 70, 3, 2, 1, 0, False, "f32"),
+    (1, 1, 1, 1, 1, 1, 3, 2, 1, 0, False, "f32"),
+    (1, 2, 3, 1, 2, 1, 3, 2, 1, 1, True, "f32"),
+    (2, 7, 4, 3, 5, 6, 3, 2, 1, 1, True, "bf16"),
+    (1, 9, 4, 3, 3, 4, 3, 2, 1, 0, True, "f32"),      # Cin 9: general kernel
 ]
 
 

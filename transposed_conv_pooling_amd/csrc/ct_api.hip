@@ -251,9 +251,18 @@ ct_status ct_convT3d(const void *x, int x_dtype, const void *w, int w_dtype, con
     if (overlap(out, no, x, nx) || overlap(out, no, w, nw) || overlap(out, no, bias, Cout * 4))
         return fail(CT_EINVAL, "%s: out overlaps an input", fn);
     if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "%s: x and w dtypes must match", fn);
-    hipError_t e = ct::launch_convT3d_generic(x, w, x_dtype == CT_BF16, bias, N, Cin, D, H, W,
-                                              Cout, k, stride, pad, out_pad, out,
-                                              (hipStream_t)stream);
+    // The pages' k3 s2 p1 layer with few input channels runs on the parity
+    // kernel (grid of one thread per input voxel); the rest on the general one.
+    int64_t nvox;
+    const bool parity = k == 3 && stride == 2 && pad == 1 && Cin <= 8 &&
+                        prod({N, D, H, W}, &nvox) && nvox <= kI32Max * 64;
+    hipError_t e;
+    if (parity)
+        e = ct::launch_convT3d_s2(x, w, x_dtype == CT_BF16, bias, N, Cin, D, H, W, Cout, out_pad,
+                                  out, (hipStream_t)stream);
+    else
+        e = ct::launch_convT3d_generic(x, w, x_dtype == CT_BF16, bias, N, Cin, D, H, W, Cout, k,
+                                       stride, pad, out_pad, out, (hipStream_t)stream);
     return hip_status(e, "convT3d launch");
 }
 

@@ -36,6 +36,13 @@ hipError_t launch_convT1d_f32(const float *x, const float *w,
                               int64_t L, int64_t Cout, int K, int dilation,
                               float *out, hipStream_t stream);
 
+// ConvTranspose3d(k3, s2, p1), output_padding 0 or 1, 1 <= Cin <= 8, output
+// [N, Cout, 2D-1+op, 2H-1+op, 2W-1+op] materialised; x, w fp32 or bf16.
+// Requires N*D*H*W < 2^31 * 256 and each output length below 2^31.
+hipError_t launch_convT3d_s2(const void *x, const void *w, bool bf16, const float *bias,
+                             int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
+                             int64_t Cout, int op, float *y, hipStream_t stream);
+
 // General-geometry kernels (generic.hip): one thread per output element,
 // fp32 or bf16 (bf16 = true) x and w, fp32 accumulation and output.
 hipError_t launch_fused3d_generic(const void *x, const void *w, bool bf16,

@@ -158,7 +158,10 @@ void convT3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
     }
 }
 
-template <typename I>
+// KC > 0: window size known at compile time; every tap is loaded from a
+// clamped (always valid) address and masked, so that all KC^3 loads are in
+// flight together.  KC == 0: run-time k, taps outside the input skipped.
+template <int KC, typename I>
 __global__ __launch_bounds__(kThreads)
 void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, int k, int s,
                               int p, int include_pad, float kvol, Div dWo, Div dHo, Div dDo,
@@ -170,17 +173,43 @@ void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, 
         const float *xs = x + (int64_t)t * D * H * W;
         float sum = 0.0f;
         int cnt = 0;
-        for (int kd = 0; kd < k; ++kd) {
-            const int id = od * s - p + kd;
-            if (id < 0 || id >= D) continue;
-            for (int kh = 0; kh < k; ++kh) {
-                const int ih = oh * s - p + kh;
-                if (ih < 0 || ih >= H) continue;
-                for (int kw = 0; kw < k; ++kw) {
-                    const int iw = ow * s - p + kw;
-                    if (iw < 0 || iw >= W) continue;
-                    sum += xs[((int64_t)id * H + ih) * W + iw];
-                    ++cnt;
+        if constexpr (KC > 0) {
+            int id[KC], ih[KC], iw[KC];
+            bool vd[KC], vh[KC], vw[KC];
+#pragma unroll
+            for (int j = 0; j < KC; ++j) {
+                const int d = od * s - p + j, h = oh * s - p + j, w = ow * s - p + j;
+                vd[j] = d >= 0 && d < D;
+                vh[j] = h >= 0 && h < H;
+                vw[j] = w >= 0 && w < W;
+                id[j] = vd[j] ? d : 0;
+                ih[j] = vh[j] ? h : 0;
+                iw[j] = vw[j] ? w : 0;
+            }
+#pragma unroll
+            for (int a = 0; a < KC; ++a)
+#pragma unroll
+                for (int b = 0; b < KC; ++b)
+#pragma unroll
+                    for (int c = 0; c < KC; ++c) {
+                        const float v = xs[((int64_t)id[a] * H + ih[b]) * W + iw[c]];
+                        const bool in = vd[a] && vh[b] && vw[c];
+                        sum += in ? v : 0.0f;
+                        cnt += in;
+                    }
+        } else {
+            for (int kd = 0; kd < k; ++kd) {
+                const int id = od * s - p + kd;
+                if (id < 0 || id >= D) continue;
+                for (int kh = 0; kh < k; ++kh) {
+                    const int ih = oh * s - p + kh;
+                    if (ih < 0 || ih >= H) continue;
+                    for (int kw = 0; kw < k; ++kw) {
+                        const int iw = ow * s - p + kw;
+                        if (iw < 0 || iw >= W) continue;
+                        sum += xs[((int64_t)id * H + ih) * W + iw];
+                        ++cnt;
+                    }
                 }
             }
         }
@@ -288,14 +317,15 @@ hipError_t launch_avgpool3d_generic(const float *x, int64_t NC, int64_t D, int64
     const Div dW = make_div((uint32_t)Wo), dH = make_div((uint32_t)Ho), dD = make_div((uint32_t)Do);
     const float kvol = (float)k * k * k;
     const dim3 grid(grid_for(total)), block(kThreads);
-    if (small_index(total))
-        hipLaunchKernelGGL((avgpool3d_generic_kernel<uint32_t>), grid, block, 0, stream, x, (int)D,
-                           (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, dD,
-                           (uint32_t)total, out);
-    else
-        hipLaunchKernelGGL((avgpool3d_generic_kernel<uint64_t>), grid, block, 0, stream, x, (int)D,
-                           (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, dD,
-                           (uint64_t)total, out);
+#define CT_POOL(KC, I)                                                                          \
+    hipLaunchKernelGGL((avgpool3d_generic_kernel<KC, I>), grid, block, 0, stream, x, (int)D,    \
+                       (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, dD, (I)total, out)
+    const bool small = small_index(total);
+    if (k == 2 && small) CT_POOL(2, uint32_t);
+    else if (k == 3 && small) CT_POOL(3, uint32_t);
+    else if (small) CT_POOL(0, uint32_t);
+    else CT_POOL(0, uint64_t);
+#undef CT_POOL
     return hipGetLastError();
 }
 
