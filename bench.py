@@ -44,6 +44,7 @@ OP_SOURCES = {
     "convT1d": "convT1d_f32.hip",
     "fused3d_bf16": "fused3d_bf16.hip",
     "unfused3d_f32": "generic.hip",
+    "convT1d_bf16": "convT1d_bf16.hip",
 }
 
 
@@ -172,6 +173,32 @@ def make_ops(names, dev):
 
         ops.append(Op("fused3d_bf16", run, nbytes(x, w, b, out), 2 * out.numel() * 32 * 8,
                       "hbm", HBM_PEAK_GBS, [wl.description], sample))
+
+    if "convT1d_bf16" in names:
+        # the same dilated ConvTranspose1d with bf16 x and w (fp32 output)
+        wl = synth.WORKLOADS["c4"]
+        log(f"inputs: {wl.description} in bf16")
+        t = synth.make_inputs(wl)
+        xb, wb = synth.to_bf16_bits(t["x"]), synth.to_bf16_bits(t["w"])
+        x = torch.from_numpy(xb.reshape(t["x"].shape).view(np.int16)).to(dev).view(torch.bfloat16)
+        w = torch.from_numpy(wb.reshape(t["w"].shape).view(np.int16)).to(dev).view(torch.bfloat16)
+        out = torch.empty((32, 64, 131084), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, out=out):
+            ct.ct_convT1d(x, w, None, 1, 0, 3, out=out)
+
+        def sample(xb=xb, wb=wb, shape=t["x"].shape, wshape=t["w"].shape):
+            import oracle
+            n = 8
+            xf = synth.bf16_bits_to_f32(xb).reshape(shape)
+            wf = synth.bf16_bits_to_f32(wb).reshape(wshape)
+            t0 = time.perf_counter()
+            oracle.convT1d(xf[:n], wf, None, 1, 0, 3)
+            return time.perf_counter() - t0, n / 32.0, f"{n} of 32 batch items"
+
+        flops = 2 * 32 * 32 * 131072 * 5 * 64
+        ops.append(Op("convT1d_bf16", run, nbytes(x, w, out), flops, "hbm", HBM_PEAK_GBS,
+                      [wl.description + " in bf16"], sample))
 
     if "unfused3d_f32" in names:
         # The chain without fusion: ConvTranspose3d writes the full pre-pool

@@ -222,6 +222,11 @@ CONV1D_GENERAL = [
     (1, 2, 2, 1, 1, 1, 0, 1, 0, True, "f32"),
     (1, 8, 9, 50, 6, 4, 3, 2, 3, True, "bf16"),
     (1, 300, 8, 20, 3, 1, 0, 1, 0, False, "f32"),    # weights beyond the LDS tile
+    # the bf16 matrix-core kernel (Cin 32, K 5, dilation 3, L % 8 == 0)
+    (2, 32, 64, 296, 5, 1, 0, 3, 0, False, "bf16"),
+    (1, 32, 70, 520, 5, 1, 0, 3, 0, True, "bf16"),    # two output-channel groups, ragged
+    (1, 32, 16, 8, 5, 1, 0, 3, 0, True, "bf16"),      # shortest input
+    (3, 32, 64, 1024, 5, 1, 0, 3, 0, True, "bf16"),   # several tiles per item
 ]
 
 
@@ -241,3 +246,31 @@ def test_conv1d_general(dev, case):
     ct.ct_convT1d(to_dev(x, dev, dt), to_dev(w, dev, dt), opt(b, dev), s, p, d, op, out=out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, str(case))
+
+
+def test_conv1d_bf16_c4_shape_sampled(dev):
+    """The [32,32,131072] workload with bf16 inputs and weights on the bf16
+    matrix-core kernel; batch items 0, 13 and 31 recomputed by the oracle from
+    the same bf16 values, plus finiteness."""
+    wl = synth.WORKLOADS["c4"]
+    log(wl.description + " in bf16")
+    t = synth.make_inputs(wl)
+    xb, wb = bf16_round(t["x"]), bf16_round(t["w"])
+    out = torch.full((32, 64, 131084), float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT1d(to_dev(xb, dev, "bf16"), to_dev(wb, dev, "bf16"), None, 1, 0, 3, out=out)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    for n in (0, 13, 31):
+        ref = oracle.convT1d(xb[n:n + 1], wb, None, 1, 0, 3)
+        assert_close(out[n:n + 1].cpu().numpy(), ref, F32_TOL, f"c4 bf16 n={n}")
+
+
+def test_conv1d_bf16_misaligned_x_takes_general_path(dev):
+    x = bf16_round(synth.normal(91, 0, (1, 32, 64)))
+    w = bf16_round(synth.uniform(91, 1, (32, 8, 5), -0.1, 0.1))
+    buf = torch.empty(x.size + 1, dtype=torch.bfloat16, device=dev)
+    buf[1:] = to_dev(x.reshape(-1), dev, "bf16")
+    out = torch.full((1, 8, 76), float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT1d(buf[1:].view(1, 32, 64), to_dev(w, dev, "bf16"), None, 1, 0, 3, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), oracle.convT1d(x, w, None, 1, 0, 3), F32_TOL, "misaligned")

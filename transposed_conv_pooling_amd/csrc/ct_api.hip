@@ -338,8 +338,8 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
         return fail(CT_EINVAL, "convT1d: out overlaps an input");
     if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "convT1d: x and w dtypes must match");
 
-    // Stride 1, pad 0 in fp32 runs on the matrix-core kernel when its tiles
-    // fit; everything else on the general kernel.
+    // Stride 1, pad 0 in fp32 runs on the fp32 matrix-core kernel when its
+    // tiles fit; everything else not caught below on the general kernel.
     bool fast = x_dtype == CT_F32 && stride == 1 && pad == 0 && out_pad == 0;
     if (fast) {
         const int64_t tiles = (Lo + 255) / 256;
@@ -349,10 +349,22 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
                (int64_t)dilation * (K - 1) <= 65536 &&
                ct::convT1d_f32_lds_bytes(Cin, K, dilation) <= kLdsMax;
     }
+    // bf16 at the page's geometry runs on the bf16 matrix-core kernel.
+    bool fast_bf16 = x_dtype == CT_BF16 && stride == 1 && pad == 0 && out_pad == 0 &&
+                     ct::convT1d_bf16_supported(Cin, K, dilation, L, x);
+    if (fast_bf16) {
+        const int64_t tiles = (Lo + 28 + 255) / 256;
+        int64_t ntiles;
+        fast_bf16 = Lo <= kI32Max - 512 && prod({N, tiles}, &ntiles) && ntiles <= kI32Max &&
+                    (Cout + 63) / 64 <= 65535;
+    }
     hipError_t e;
     if (fast) {
         e = ct::launch_convT1d_f32((const float *)x, (const float *)w, bias, N, Cin, L, Cout, K,
                                    dilation, out, (hipStream_t)stream);
+    } else if (fast_bf16) {
+        e = ct::launch_convT1d_bf16((const uint16_t *)x, (const uint16_t *)w, bias, N, L, Cout, K,
+                                    dilation, out, (hipStream_t)stream);
     } else {
         if (Lo > kGenericMaxLen || L > kGenericMaxLen || Cin > kGenericMaxLen ||
             Cout > kGenericMaxLen || pad > kGenericMaxLen ||

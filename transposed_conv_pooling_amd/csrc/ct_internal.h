@@ -36,6 +36,15 @@ hipError_t launch_convT1d_f32(const float *x, const float *w,
                               int64_t L, int64_t Cout, int K, int dilation,
                               float *out, hipStream_t stream);
 
+// ConvTranspose1d, stride 1, pad 0, bf16 x and w (fp32 accumulation and
+// output) on the bf16 matrix cores, for the geometries where
+// convT1d_bf16_supported() holds (Cin 32, K 5, dilation 3, L a multiple of 8,
+// x 16-byte aligned).
+bool convT1d_bf16_supported(int64_t Cin, int K, int dilation, int64_t L, const void *x);
+hipError_t launch_convT1d_bf16(const uint16_t *x, const uint16_t *w, const float *bias,
+                               int64_t N, int64_t L, int64_t Cout, int K, int dilation,
+                               float *out, hipStream_t stream);
+
 // ConvTranspose3d(k3, s2, p1), output_padding 0 or 1, 1 <= Cin <= 8, output
 // [N, Cout, 2D-1+op, 2H-1+op, 2W-1+op] materialised; x, w fp32 or bf16.
 // Requires N*D*H*W < 2^31 * 256 and each output length below 2^31.
