@@ -39,6 +39,7 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -167,13 +168,19 @@ void convT1d_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
         // line, so no partly written line goes to memory.  The computed range
         // [o0 - kLead, o0 + 256) covers every such segment.
         float *yn = y + (int64_t)n * Cout * Lo;
+        // vector stores go through a buffer resource over this item's output
+        // (word 3 0x00020000: 32-bit data format, as gfx9-family raw buffers
+        // need); the hardware drops a store whose offset lies past the range,
+        // so masked lanes need no branch and the wait for the next strip's
+        // loads does not cover these stores
+        const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(yn, 0, Cout * Lo * 4, 0x00020000);
         const int ow = o0 - kLead + 16 * kOB * wave + 4 * g;   // lane's first output
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int co = cog * kCO + 16 * cb + col;
-            if (co >= Cout) continue;
             float *yr = yn + (int64_t)co * Lo;
             int lo = o0, hi = o0 + kTO;
+            if (co >= Cout) hi = lo;
             if (VEC_OUT) {
                 const int sh = (int)((ybase + ((int64_t)n * Cout + co) * Lo) & 31);
                 lo -= sh;
@@ -186,7 +193,8 @@ void convT1d_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
                 const int o = ow + 16 * ob;
                 const v4f v = acc[ob][cb] + bv[cb];
                 if (VEC_OUT) {                            // o and Lo multiples of 4
-                    if (o >= lo && o < hi) *reinterpret_cast<v4f *>(yr + o) = v;
+                    const int off = (o >= lo && o < hi) ? (co * Lo + o) * 4 : 0x7ffffff0;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yrs, off, 0, 0);
                 } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)

@@ -186,7 +186,13 @@ void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restric
         }
 
     // strip piece q = ci * (kTs/4) + t4 (compile-time divisor)
+    // Loads are unconditional, from the piece's address when it lies inside
+    // [0, L) (L % 4 == 0: a piece is wholly inside or outside) and from x
+    // otherwise, and masked when stored: every load of a fetch is then in
+    // flight together, and the wait for them before the next put() need not
+    // cover the stores issued after them.
     v4f_ pre[G::kQPerThread];
+    bool pok[G::kQPerThread];
     auto fetch = [&](int tile) {
         const int n = tile / tiles_per_n;
         const int o0 = (tile - n * tiles_per_n) * kTO;
@@ -196,9 +202,9 @@ void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restric
             const int q = threadIdx.x + i * kThreads;
             const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
             const int pos = o0 - G::kHalo + 4 * t4;
-            pre[i] = (q < G::kQ && ci < Cin && pos >= 0 && pos < L)
-                ? *reinterpret_cast<const v4f_ *>(xb + ci * L + 4 * t4)
-                : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
+            const bool ok = q < G::kQ && ci < Cin && pos >= 0 && pos < L;
+            pre[i] = *reinterpret_cast<const v4f_ *>(ok ? xb + ci * L + 4 * t4 : x);
+            pok[i] = ok;
         }
     };
     if ((int)blockIdx.x < ntiles) fetch(blockIdx.x);
@@ -214,7 +220,8 @@ void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restric
             const int q = threadIdx.x + i * kThreads;
             if (q < G::kQ) {
                 const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
-                *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * t4) = pre[i];
+                *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * t4) =
+                    pok[i] ? pre[i] : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
         __syncthreads();
@@ -245,18 +252,24 @@ void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restric
             }
         }
 
-        float *yn = y + (int64_t)n * Cout * Lo;
+        // Stores go through a buffer resource over this batch item's output
+        // (word 3 0x00020000: 32-bit data format, as gfx9-family raw buffers
+        // need); the hardware drops a store whose offset lies beyond the range,
+        // so masked lanes need no branch.  With neither loads nor stores
+        // behind branches, the wait for the next strip's loads at the next
+        // put() does not have to cover this tile's stores.
+        const __amdgpu_buffer_rsrc_t yr =
+            __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * Cout * Lo, 0, Cout * Lo * 4, 0x00020000);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int co = cog * kCO + 16 * m + 4 * kq + r;
-                if (co >= Cout) continue;
-                float *yr = yn + (int64_t)co * Lo;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int o = o0 + 64 * wave + 16 * b + col;
-                    if (o < Lo) yr[o] = acc[m][b][r] + bv[m][r];
+                    const int off = (co < Cout && o < Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;   // past the range
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc[m][b][r] + bv[m][r]), yr, off, 0, 0);
                 }
             }
     }

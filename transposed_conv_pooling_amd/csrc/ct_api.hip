@@ -348,6 +348,8 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
                (Cout + 63) / 64 <= 65535 && Cin <= 4096 && K <= 4096 &&
                (int64_t)dilation * (K - 1) <= 65536 &&
                ct::convT1d_f32_lds_bytes(Cin, K, dilation) <= kLdsMax;
+        int64_t item;           // one batch item's output within a 2 GiB buffer range
+        fast = fast && prod({Cout, Lo, 4}, &item) && item < (int64_t(1) << 31) - 64;
     }
     // bf16 at the page's geometry runs on the bf16 matrix-core kernel.
     bool fast_bf16 = x_dtype == CT_BF16 && stride == 1 && pad == 0 && out_pad == 0 &&
@@ -355,8 +357,10 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
     if (fast_bf16) {
         const int64_t tiles = (Lo + 28 + 255) / 256;
         int64_t ntiles;
+        int64_t item;           // one batch item's output within a 2 GiB buffer range
         fast_bf16 = Lo <= kI32Max - 512 && prod({N, tiles}, &ntiles) && ntiles <= kI32Max &&
-                    (Cout + 63) / 64 <= 65535;
+                    (Cout + 63) / 64 <= 65535 && prod({Cout, Lo, 4}, &item) &&
+                    item < (int64_t(1) << 31) - 64;
     }
     hipError_t e;
     if (fast) {
