@@ -18,17 +18,19 @@
 //      D (16x16): lane l holds D[co = 4*(l/16) + r][o = l%16]
 //    kappa runs k-major with ci padded to a multiple of 4 (Cin4), so the 4
 //    kappas of one MFMA share one tap k.
-//  * A workgroup (4 waves) owns a 64-channel x 256-output tile; each wave
+//  * General kernel (any Cin, K, dilation within the LDS limit): a
+//    workgroup (4 waves) owns a 64-channel x 256-output tile; each wave
 //    computes 64 channels x 64 outputs = 16 MFMA accumulators.  Workgroups
 //    are persistent: they stage the weights once into LDS in fragment order
-//    (lane-consecutive, conflict-free) and then walk tiles.
-//  * Per tile the input strip x[n, :, o0-halo .. o0+255] (halo =
-//    dil*(K-1), zero outside [0,L)) is staged in LDS once; the K shifted
-//    views of the gather are different LDS offsets into that strip, read
-//    at a row stride of 16 mod 64 words so the four 16-lane groups of a
+//    (lane-consecutive, conflict-free) and then walk tiles; per tile the
+//    input strip x[n, :, o0-halo .. o0+255] (halo = dil*(K-1), zero outside
+//    [0,L)) is staged in LDS once behind a workgroup barrier, and the K
+//    shifted views of the gather are different LDS offsets into that strip,
+//    read at a row stride of 16 mod 64 words so the four 16-lane groups of a
 //    fragment read hit disjoint banks.
-//  * Outputs are written with non-temporal stores, 16 consecutive outputs
-//    (64 bytes) per lane group.
+//  * Page's geometry (Cin 32, K 5, dilation 3): the same MFMA tiling with
+//    everything known at compile time, but each wave owns its tiles and a
+//    private strip, so no tile waits at a barrier (convT1d_f32_wave_kernel).
 #include "ct_internal.h"
 
 namespace ct {
@@ -136,104 +138,127 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
     }
 }
 
-// Specialised path: Cin4, K and the dilation known at compile time, so every
-// LDS address is a per-lane base plus an immediate offset and the k-loop
-// carries no index arithmetic.  The input strip of the next tile is loaded
-// (16-byte loads, no divisions) into registers while the current tile
-// computes.  Requires L % 4 == 0 and dil*(K-1) % 4 == 0 (whole float4 pieces
-// are either inside or outside [0, L)) and 16-byte aligned x.
-template <int CIN4, int K, int DIL>
-struct FastGeom {
+// Specialised path for the page's geometry: Cin4, K and the dilation known
+// at compile time, so every LDS address is a per-lane base plus an immediate
+// offset and the k-loop carries no index arithmetic.  Requires L % 4 == 0 and
+// dil*(K-1) % 4 == 0 (whole float4 pieces are either inside or outside
+// [0, L)) and 16-byte aligned x.
+// Wave-independent path for the same specialised geometry: a workgroup of
+// WW waves shares one copy of the weight fragments (40 KiB of LDS, staged
+// once behind the kernel's only barrier); each wave then walks its own
+// contiguous range of 16*NB-output tiles with a wave-private input strip
+// (positions o0 - halo .. o0 + 16*NB - 1), so no tile ever waits at a
+// workgroup barrier.  Several waves per SIMD, out of phase with each other,
+// keep the matrix pipe busy while any one of them stages its next strip or
+// issues its stores.  Neighbouring tiles both read the strip halo.
+template <int CIN4, int K, int DIL, int NB, int WW>
+struct WaveGeom {
+    static constexpr int kThreads = 64 * WW;
+    static constexpr int kTW = 16 * NB;                             // outputs per wave tile
     static constexpr int kKsteps = CIN4 * K / 4;
     static constexpr int kHalo = DIL * (K - 1);
-    static constexpr int kTs = kTO + kHalo;
-    static constexpr int kStr = ((kTs + 63) / 64) * 64 + 16 - (((kTs + 63) / 64) * 64 + 16 - 64 >= kTs ? 64 : 0);
-    static constexpr int kQ = CIN4 * kTs / 4;                    // float4 pieces per strip
-    static constexpr int kQPerThread = (kQ + kThreads - 1) / kThreads;
-    static constexpr int kLdsFloats = 4 * kKsteps * 64 + CIN4 * kStr;
+    static constexpr int kTs = kTW + kHalo;                         // strip positions
+    // row stride >= kTs with stride mod 64 in {16, 48} words: the four
+    // 16-lane groups of a B-fragment read (rows kq = 0..3) hit disjoint banks
+    static constexpr int kStr16 = kTs <= 16 ? 16 : (kTs - 16 + 63) / 64 * 64 + 16;
+    static constexpr int kStr48 = kTs <= 48 ? 48 : (kTs - 48 + 63) / 64 * 64 + 48;
+    static constexpr int kStr = kStr16 < kStr48 ? kStr16 : kStr48;
+    static constexpr int kQ = CIN4 * kTs / 4;                       // float4 pieces per strip
+    static constexpr int kQPerLane = (kQ + 63) / 64;
+    static constexpr int kWfrag = 4 * kKsteps * 64;                 // floats
+    static constexpr int kLdsFloats = kWfrag + kCO + WW * CIN4 * kStr;
 };
 
-template <int CIN4, int K, int DIL>
-__global__ __launch_bounds__(kThreads, 2)
-void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restrict__ w,
+template <int CIN4, int K, int DIL, int NB, int WW>
+__global__ __launch_bounds__(64 * WW, 1)
+void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
                              int tiles_per_n, int ntiles, float *__restrict__ y)
 {
-    typedef FastGeom<CIN4, K, DIL> G;
+    typedef WaveGeom<CIN4, K, DIL, NB, WW> G;
+    static_assert(G::kStr >= G::kTs && (G::kStr % 64 == 16 || G::kStr % 64 == 48), "strip row stride");
+    static_assert(G::kHalo % 4 == 0, "halo in whole float4 pieces");
+    static_assert(G::kQPerLane <= 32, "piece mask");
+    static_assert(G::kLdsFloats * 4 <= 160 * 1024, "LDS of one workgroup");
     typedef float v4f_ __attribute__((ext_vector_type(4)));
     extern __shared__ float lds[];
-    float *wfrag = lds;                           // [j][lane][m]: 4 m-blocks per 16 bytes
-    float *xs = lds + 4 * G::kKsteps * 64;        // [CIN4][kStr]
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float *wfrag = lds;                                      // [j][lane][m]
+    float *bsh = lds + G::kWfrag;                            // [64] bias of the channel block
+    float *xs = bsh + kCO + wave * CIN4 * G::kStr;           // this wave's [CIN4][kStr]
     const int cog = blockIdx.y;
     const int kq = lane >> 4, col = lane & 15;
 
-    for (int e = threadIdx.x; e < 4 * G::kKsteps * 64; e += kThreads) {
+    for (int e = threadIdx.x; e < G::kWfrag; e += G::kThreads) {
         const int m = e & 3, l = (e >> 2) & 63, j = e >> 8;
         const int co = cog * kCO + 16 * m + (l & 15);
         const int kap = 4 * j + (l >> 4);
         const int k = kap / CIN4, ci = kap % CIN4;
         wfrag[e] = (co < Cout && ci < Cin) ? w[((int64_t)ci * Cout + co) * K + k] : 0.0f;
     }
-    float bv[4][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = cog * kCO + 16 * m + 4 * kq + r;
-            bv[m][r] = (bias && co < Cout) ? bias[co] : 0.0f;
-        }
+    if (threadIdx.x < kCO) {
+        const int co = cog * kCO + threadIdx.x;
+        bsh[threadIdx.x] = (bias && co < Cout) ? bias[co] : 0.0f;
+    }
 
-    // strip piece q = ci * (kTs/4) + t4 (compile-time divisor)
-    // Loads are unconditional, from the piece's address when it lies inside
-    // [0, L) (L % 4 == 0: a piece is wholly inside or outside) and from x
-    // otherwise, and masked when stored: every load of a fetch is then in
-    // flight together, and the wait for them before the next put() need not
-    // cover the stores issued after them.
-    v4f_ pre[G::kQPerThread];
-    bool pok[G::kQPerThread];
+    // this wave's contiguous tile range (workgroups in XCD-aware order)
+    const int64_t gw = xcd_remap(blockIdx.x, gridDim.x) * WW + wave;
+    const int64_t nw = (int64_t)gridDim.x * WW;
+    const int per = (int)(ntiles / nw), rem = (int)(ntiles % nw);
+    const int t_begin = (int)(gw * per + (gw < rem ? gw : rem));
+    const int t_end = t_begin + per + (gw < rem ? 1 : 0);
+
+    // strip piece q = ci * (kTs/4) + t4; unconditional loads from clamped
+    // addresses (L % 4 == 0: a piece is wholly inside or outside [0, L)),
+    // masked when written
+    v4f_ pre[G::kQPerLane];
+    unsigned pok = 0;                                        // bit i: piece i inside [0, L)
     auto fetch = [&](int tile) {
         const int n = tile / tiles_per_n;
-        const int o0 = (tile - n * tiles_per_n) * kTO;
+        const int o0 = (tile - n * tiles_per_n) * G::kTW;
         const float *xb = x + (int64_t)n * Cin * L + (o0 - G::kHalo);
 #pragma unroll
-        for (int i = 0; i < G::kQPerThread; ++i) {
-            const int q = threadIdx.x + i * kThreads;
+        for (int i = 0; i < G::kQPerLane; ++i) {
+            const int q = lane + 64 * i;
             const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
             const int pos = o0 - G::kHalo + 4 * t4;
             const bool ok = q < G::kQ && ci < Cin && pos >= 0 && pos < L;
             pre[i] = *reinterpret_cast<const v4f_ *>(ok ? xb + ci * L + 4 * t4 : x);
-            pok[i] = ok;
+            pok = ok ? pok | (1u << i) : pok & ~(1u << i);
         }
     };
-    if ((int)blockIdx.x < ntiles) fetch(blockIdx.x);
+    if (t_begin < t_end) fetch(t_begin);
+    __syncthreads();                                         // weights and bias staged
 
-    const float *xl = xs + kq * G::kStr + G::kHalo + 64 * wave + col;   // lane's B base
-    const float *al = wfrag + lane * 4;                                   // lane's A base
-    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const float *xl = xs + kq * G::kStr + G::kHalo + col;   // lane's B base
+    const float *al = wfrag + lane * 4;                      // lane's A base
+    for (int tile = t_begin; tile < t_end; ++tile) {
         const int n = tile / tiles_per_n;
-        const int o0 = (tile - n * tiles_per_n) * kTO;
-        __syncthreads();          // previous strip consumed (and weights staged)
+        const int o0 = (tile - n * tiles_per_n) * G::kTW;
+        // this wave alone reads and writes its strip, and a wave's LDS
+        // operations complete in order: compiler-only fences suffice
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int i = 0; i < G::kQPerThread; ++i) {
-            const int q = threadIdx.x + i * kThreads;
+        for (int i = 0; i < G::kQPerLane; ++i) {
+            const int q = lane + 64 * i;
             if (q < G::kQ) {
                 const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
                 *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * t4) =
-                    pok[i] ? pre[i] : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
+                    ((pok >> i) & 1) ? pre[i] : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
-        __syncthreads();
-        if (tile + (int)gridDim.x < ntiles) fetch(tile + gridDim.x);
+        __builtin_amdgcn_wave_barrier();
+        if (tile + 1 < t_end) fetch(tile + 1);
 
-        v4f acc[4][4];
+        // accumulators start at the bias of their channels (D rows 4kq .. +3)
+        v4f acc[4][NB];
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) {
+            const v4f b4 = *reinterpret_cast<const v4f *>(bsh + 16 * m + 4 * kq);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[m][b] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-        // kappa = k*CIN4 + ci: outer loop over taps k (one base per tap), inner
-        // over 4-channel groups with immediate LDS offsets
+            for (int b = 0; b < NB; ++b) acc[m][b] = b4;
+        }
 #pragma unroll 1
         for (int k = 0; k < K; ++k) {
             const float *xk = xl - DIL * k;
@@ -241,23 +266,20 @@ void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restric
 #pragma unroll
             for (int c = 0; c < CIN4 / 4; ++c) {
                 const v4f_ av = *reinterpret_cast<const v4f_ *>(ak + c * 256);
-                float bvv[4];
+                float bvv[NB];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) bvv[b] = xk[4 * c * G::kStr + 16 * b];
+                for (int b = 0; b < NB; ++b) bvv[b] = xk[4 * c * G::kStr + 16 * b];
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
+                    for (int b = 0; b < NB; ++b)
                         acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bvv[b], acc[m][b], 0, 0, 0);
             }
         }
 
-        // Stores go through a buffer resource over this batch item's output
-        // (word 3 0x00020000: 32-bit data format, as gfx9-family raw buffers
-        // need); the hardware drops a store whose offset lies beyond the range,
-        // so masked lanes need no branch.  With neither loads nor stores
-        // behind branches, the wait for the next strip's loads at the next
-        // put() does not have to cover this tile's stores.
+        // buffer stores over this batch item's output (word 3 0x00020000:
+        // 32-bit data format); masked lanes store past the range, which the
+        // hardware drops, so no store sits behind a branch
         const __amdgpu_buffer_rsrc_t yr =
             __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * Cout * Lo, 0, Cout * Lo * 4, 0x00020000);
 #pragma unroll
@@ -266,14 +288,23 @@ void convT1d_f32_fast_kernel(const float *__restrict__ x, const float *__restric
             for (int r = 0; r < 4; ++r) {
                 const int co = cog * kCO + 16 * m + 4 * kq + r;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int o = o0 + 64 * wave + 16 * b + col;
+                for (int b = 0; b < NB; ++b) {
+                    const int o = o0 + 16 * b + col;
                     const int off = (co < Cout && o < Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;   // past the range
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, acc[m][b][r] + bv[m][r]), yr, off, 0, 0);
+                    // (__float_as_uint: a bit_cast of the vector element
+                    // lvalue acc[m][b][r] read element 0 for every r)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][b][r]), yr, off, 0, 0);
                 }
             }
     }
 }
+
+// The configuration the launcher uses for Cin 32, K 5, dilation 3: 64-output
+// wave tiles, 8 waves (2 per SIMD) per workgroup.  Measured at the
+// [32,32,131072] workload: 710 us, against 720 for 32-output tiles with 12
+// or 16 waves and 743 for 256-output workgroup tiles behind barriers.
+constexpr int kWaveNB = 4;
+constexpr int kWaveWW = 8;
 
 }  // namespace
 
@@ -301,25 +332,26 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
     if (str - 64 >= ts) str -= 64;
     if (cin4 == 32 && Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 &&
         (((uintptr_t)x) & 15) == 0) {
-        typedef FastGeom<32, 5, 3> G;
+        typedef WaveGeom<32, 5, 3, kWaveNB, kWaveWW> G;
+        const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW>;
         const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
-        hipError_t e = hipFuncSetAttribute((const void *)convT1d_f32_fast_kernel<32, 5, 3>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         int dev = 0, cus = 256, per_cu = 1;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)convT1d_f32_fast_kernel<32, 5, 3>,
-                                                         kThreads, lds) != hipSuccess || per_cu < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, G::kThreads, lds) != hipSuccess ||
+            per_cu < 1)
             per_cu = 1;
+        const int wtiles_per_n = (int)((Lo + G::kTW - 1) / G::kTW);
+        const int64_t wtiles = N * wtiles_per_n;
         const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
         int64_t gx = (int64_t)cus * per_cu / gy;
         if (gx < 1) gx = 1;
-        if (gx > ntiles) gx = ntiles;
-        hipLaunchKernelGGL((convT1d_f32_fast_kernel<32, 5, 3>), dim3((unsigned)gx, gy), dim3(kThreads),
-                           lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout, (int)Lo, tiles_per_n,
-                           (int)ntiles, out);
+        hipLaunchKernelGGL((convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW>), dim3((unsigned)gx, gy),
+                           dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
+                           (int)Lo, wtiles_per_n, (int)wtiles, out);
         return hipGetLastError();
     }
     const size_t lds = convT1d_f32_lds_bytes(Cin, K, dilation);
