@@ -268,6 +268,10 @@ CONV1D_SMALL = [
     (1, 4, 16, 5, 5, 3, False),          # L shorter than the halo
     (1, 36, 64, 513, 5, 3, False),
     (3, 32, 64, 256, 5, 3, True),
+    (1, 32, 70, 520, 5, 3, True),        # two output-channel groups, ragged
+    (2, 32, 16, 8, 5, 3, False),         # one tile per item, most waves idle
+    (1, 32, 64, 4, 5, 3, True),          # shortest fast-path input
+    (5, 32, 64, 1028, 5, 3, False),      # tiles straddling batch items
 ]
 
 
