@@ -390,38 +390,50 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         const int h0 = hc * TH;
         const int rows = min(TH, Hp - h0);
         float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
-        // each wave takes rows hh = wave, wave + 4, ...; a row's w-blocks go in
-        // pairs, each block's K range split over two accumulators: four
-        // independent MFMA chains in flight
-        for (int hh = wave; hh < rows; hh += kWaves) {
-            const float *srow = cur + hh * W;
-            float *orow = ob + hh * Wp;
+        // each wave takes rows hh = wave, wave + 4, ... two at a time (hh and
+        // hh + 4); a row's w-blocks go in pairs, each block's K range split
+        // over two accumulators: eight independent MFMA chains in flight, with
+        // all their LDS reads issued first
+        auto store_block = [&](float *orow, int wv, const v4f &p, const v4f &q) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (co_ok[r]) orow[co_off[r] + wv] = __builtin_fmaf(p[r] + q[r], alpha, beta[r]);
+        };
+        for (int hh = wave; hh < rows; hh += 2 * kWaves) {
+            const int hh2 = hh + kWaves;
+            const bool two = hh2 < rows;           // wave-uniform
+            const float *srowA = cur + hh * W, *srowB = cur + (two ? hh2 : hh) * W;
+            float *orowA = ob + hh * Wp, *orowB = ob + hh2 * Wp;
             for (int wb = 0; wb < wblocks; wb += 2) {
                 const int wv0 = wb * 16 + col, wv1 = wv0 + 16;
                 const int wc0 = min(wv0, Wp - 1), wc1 = min(wv1, Wp - 1);
-                float b0[KS], b1[KS];
+                float a0[KS], a1[KS], b0[KS], b1[KS];
 #pragma unroll
                 for (int j = 0; j < KS; ++j) {
-                    b0[j] = srow[wc0 + soff[j]];
-                    b1[j] = srow[wc1 + soff[j]];
+                    a0[j] = srowA[wc0 + soff[j]];
+                    a1[j] = srowA[wc1 + soff[j]];
+                    b0[j] = srowB[wc0 + soff[j]];
+                    b1[j] = srowB[wc1 + soff[j]];
                 }
-                v4f p0 = {0.0f, 0.0f, 0.0f, 0.0f}, q0 = p0, p1 = p0, q1 = p0;
+                v4f pA0 = {0.0f, 0.0f, 0.0f, 0.0f}, qA0 = pA0, pA1 = pA0, qA1 = pA0;
+                v4f pB0 = pA0, qB0 = pA0, pB1 = pA0, qB1 = pA0;
 #pragma unroll
                 for (int j = 0; j < KS; j += 2) {
-                    p0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b0[j], p0, 0, 0, 0);
-                    p1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b1[j], p1, 0, 0, 0);
-                    q0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b0[j + 1], q0, 0, 0, 0);
-                    q1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b1[j + 1], q1, 0, 0, 0);
+                    pA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a0[j], pA0, 0, 0, 0);
+                    pA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a1[j], pA1, 0, 0, 0);
+                    pB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b0[j], pB0, 0, 0, 0);
+                    pB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b1[j], pB1, 0, 0, 0);
+                    qA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a0[j + 1], qA0, 0, 0, 0);
+                    qA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a1[j + 1], qA1, 0, 0, 0);
+                    qB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b0[j + 1], qB0, 0, 0, 0);
+                    qB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b1[j + 1], qB1, 0, 0, 0);
                 }
-                if (wv0 < Wp) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (co_ok[r]) orow[co_off[r] + wv0] = __builtin_fmaf(p0[r] + q0[r], alpha, beta[r]);
-                }
-                if (wb + 1 < wblocks && wv1 < Wp) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (co_ok[r]) orow[co_off[r] + wv1] = __builtin_fmaf(p1[r] + q1[r], alpha, beta[r]);
+                const bool w1 = wb + 1 < wblocks && wv1 < Wp;
+                if (wv0 < Wp) store_block(orowA, wv0, pA0, qA0);
+                if (w1) store_block(orowA, wv1, pA1, qA1);
+                if (two) {
+                    if (wv0 < Wp) store_block(orowB, wv0, pB0, qB0);
+                    if (w1) store_block(orowB, wv1, pB1, qB1);
                 }
             }
         }
