@@ -79,6 +79,12 @@ FUSED_SMALL = [
     (1, 5, 7, 6, 5, 18),
     (1, 32, 64, 3, 5, 33),
     (1, 7, 3, 2, 3, 49),
+    # several tasks per workgroup: staged rows carried across row chunks,
+    # planes and batch items, ragged last chunks, W % 4 != 0, ragged Cout
+    (5, 3, 16, 7, 20, 24),
+    (3, 4, 40, 5, 19, 13),
+    (9, 1, 16, 4, 33, 32),
+    (2, 2, 17, 3, 70, 9),
 ]
 
 

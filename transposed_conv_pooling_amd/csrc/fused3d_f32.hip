@@ -249,16 +249,52 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // h0..h0+TH, :] is loaded two tasks ahead with coalesced VEC-wide loads into
 // registers, written into the spare half of a double-buffered LDS slab one
 // task ahead, and read from there as B fragments (16 consecutive w per lane
-// group); one barrier per task.  The first slab's loads are issued before
-// the filter build so the two latencies overlap.
-constexpr int kSlabPrefetch = 4;   // slab pieces each thread keeps in flight
+// group).  The first slab's loads are issued before the filter build so the
+// two latencies overlap.
+//
+// Output.  For one (n, co) the pooled outputs of all (d, h, w) form one
+// contiguous stream of Dp*Hp*Wp floats, and consecutive tasks of a workgroup
+// continue each of their 16 streams.  A task's results go to a staging row
+// per channel in LDS, placed so that staging position p is the float at
+// address line_base + 4p (line_base = the 128-byte line holding the task's
+// first output of that stream).  The store phase then writes every complete
+// 128-byte line with non-temporal 16-byte stores, and hands the unfinished
+// last line (fewer than 32 floats) to the next task's staging row instead of
+// writing it, so HBM sees whole lines; only a stream's first and last
+// partial lines in a workgroup are written with plain stores (for L2 to
+// merge with the neighbour's part).  Staging is double-buffered as well:
+// one barrier per task separates a task's compute from its store phase.
+constexpr int kSlabPrefetch = 8;   // slab pieces each loader lane keeps in flight
+constexpr int kLine = 32;          // floats per 128-byte line
+// 4 compute waves, 2 loader waves, 2 store waves.  vmcnt counts a wave's
+// loads and stores together and retires them in order, so a wave that both
+// stores and prefetches would wait for its earlier stores before each slab;
+// here only the loader waves load and only the store waves store.
+constexpr int kLoadWaves = 2;
+constexpr int kStoreWaves = 2;
+constexpr int kLoadThreads = 64 * kLoadWaves;
+constexpr int kSlabThreads = 64 * (kWaves + kLoadWaves + kStoreWaves);
 
 template <int VEC> struct Vec;
 template <> struct Vec<4> { typedef float4 T; };
 template <> struct Vec<1> { typedef float T; };
 
+// LDS layout sizes in floats (int64 so the host can size any geometry)
+__host__ __device__ inline int64_t slab_floats(int64_t cin, int64_t th, int64_t w) { return cin * 2 * (th + 1) * w; }
+// staging row stride: a leading partial line plus TH rows, a multiple of 4
+// floats (16-byte aligned rows) plus 4 to spread the channels over banks
+__host__ __device__ inline int64_t stage_stride(int64_t th, int64_t wp) { return ((kLine + th * wp + 3) & ~int64_t(3)) + 4; }
+__host__ __device__ inline int64_t stage_offset(int64_t ks, int64_t cin, int64_t th, int64_t w)
+{
+    return (ks * 64 + 2 * slab_floats(cin, th, w) + 3) & ~int64_t(3);
+}
+__host__ __device__ inline int64_t slab_lds_floats(int64_t ks, int64_t cin, int64_t th, int64_t w, int64_t wp)
+{
+    return stage_offset(ks, cin, th, w) + 2 * 16 * stage_stride(th, wp);
+}
+
 template <int KS, int VEC>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kSlabThreads)
 void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ conv_bias,
                              const float *__restrict__ bias, float s1, float s2,
@@ -267,23 +303,22 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
                              int tasks_per_wg, float *__restrict__ out)
 {
     typedef typename Vec<VEC>::T vec_t;
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];
     const int R = TH + 1;                      // input rows per plane in a slab
-    const int slab_floats = Cin * 2 * R * W;
+    const int sfl = (int)slab_floats(Cin, TH, W);
+    const int STR = (int)stage_stride(TH, Wp);
     float *wfrag = lds;                        // [KS][64]
     float *slabs = lds + KS * 64;              // 2 x [Cin][2][R][W] (double buffer)
+    float *stage = lds + stage_offset(KS, Cin, TH, W);   // 2 x [16][STR]
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
-    const int col = lane & 15;
-    const int kq = lane >> 4;
     const int cob = blockIdx.y;
     const int HW = H * W, DHW = D * HW;        // per-item sizes < 2^31 (checked by the shim)
     const int64_t pplane = (int64_t)Dp * Hp * Wp;
-    const int wblocks = (Wp + 15) / 16;
 
     // this workgroup's contiguous task range (n, d, hc), decoded once
     const int t_begin = uniform((int)min<int64_t>(xcd_remap(blockIdx.x, gridDim.x) * tasks_per_wg, ntasks));
-    const int t_end = uniform(min(t_begin + tasks_per_wg, ntasks));
+    const int ntask = uniform(min(t_begin + tasks_per_wg, ntasks) - t_begin);
     int hc, d, n;
     {
         int t = t_begin;
@@ -291,57 +326,161 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         d = uniform(t % Dp);
         n = uniform(t / Dp);
     }
+    auto next = [&](int &n_, int &d_, int &hc_) {
+        if (++hc_ == hchunks) { hc_ = 0; if (++d_ == Dp) { d_ = 0; ++n_; } }
+    };
 
-    // tile-invariant staging plan: piece q = ((ci*2 + a)*R + r)*(W/VEC) + v
-    const int WV = W / VEC;
-    const int npieces = Cin * 2 * R * WV;
-    int src_off[kSlabPrefetch], dst_off[kSlabPrefetch], prow[kSlabPrefetch];
-#pragma unroll
-    for (int i = 0; i < kSlabPrefetch; ++i) {
-        const int q = threadIdx.x + i * kThreads;
-        const int v = q % WV, t = q / WV;
-        const int r = t % R, ca = t / R;
-        const int a = ca & 1, ci = ca >> 1;
-        src_off[i] = ci * DHW + a * HW + r * W + v * VEC;
-        dst_off[i] = (ca * R + r) * W + v * VEC;
-        prow[i] = q < npieces ? r : 1 << 30;   // rows past H (or no piece) load nothing
-    }
-    vec_t pre[kSlabPrefetch];
-    // loads are unconditional (rows past H read x[0..], a valid address) so
-    // they all stay in flight; the zero fill is applied when they are stored
-    auto fetch = [&](int n_, int d_, int hc_) {
-        const int h0 = hc_ * TH;
-        const float *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
+    // Three roles, one pipeline stage per task, one barrier per stage (after
+    // a first barrier that publishes the filter and the first slab).  In
+    // stage s the loader waves put slab s+1 into LDS, the compute waves turn
+    // slab s into staging row set s, and the store waves write staging set
+    // s-1 to memory.  Each role runs its own loop over the same barriers, so
+    // no role's registers are live in another's code.
+    if (wave >= kWaves && wave < kWaves + kLoadWaves) {
+        // ---- loader: slab pieces q = ((ci*2 + a)*R + r)*(W/VEC) + v --------
+        const int ll = threadIdx.x - kThreads;  // 0 .. kLoadThreads-1
+        const int WV = W / VEC;
+        const int npieces = Cin * 2 * R * WV;
+        // per piece: source offset, and destination offset * 256 + slab row
+        // (a slab fits the LDS budget, so offsets are < 2^23, and R <= 9);
+        // -1 marks "no piece"
+        int src_off[kSlabPrefetch], dst_row[kSlabPrefetch];
 #pragma unroll
         for (int i = 0; i < kSlabPrefetch; ++i) {
-            const float *src = (h0 + prow[i] < H) ? xb + src_off[i] : x;
-            pre[i] = *reinterpret_cast<const vec_t *>(src);
+            const int q = ll + i * kLoadThreads;
+            const int v = q % WV, t = q / WV;
+            const int r = t % R, ca = t / R;
+            const int a = ca & 1, ci = ca >> 1;
+            src_off[i] = ci * DHW + a * HW + r * W + v * VEC;
+            dst_row[i] = q < npieces ? (((ca * R + r) * W + v * VEC) << 8) | r : -1;
         }
-    };
-    // writes the prefetched slab (plus any pieces beyond the prefetch plan) into buf
-    auto put = [&](float *buf, int n_, int d_, int hc_) {
-        const int h0 = hc_ * TH;
+        // Every fetch issues exactly kSlabPrefetch loads, all from valid
+        // addresses (x[0..] for no piece, a row past H or a task past the
+        // range), so the count of loads in flight is the same on every path
+        // and each put waits only for its own batch.
+        auto fetch = [&](vec_t *pre, int n_, int d_, int hc_, bool real) {
+            const int h0 = hc_ * TH;
+            const float *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
 #pragma unroll
-        for (int i = 0; i < kSlabPrefetch; ++i)
-            if (prow[i] < (1 << 30))
-                *reinterpret_cast<vec_t *>(buf + dst_off[i]) = (h0 + prow[i] < H) ? pre[i] : vec_t{};
-        for (int q = threadIdx.x + kSlabPrefetch * kThreads; q < npieces; q += kThreads) {
-            const int v = q % WV, tt = q / WV;
-            const int r = tt % R, ca = tt / R;
-            vec_t val = vec_t{};
-            if (h0 + r < H)
-                val = *reinterpret_cast<const vec_t *>(
-                    x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W +
-                    (ca >> 1) * DHW + (ca & 1) * HW + r * W + v * VEC);
-            *reinterpret_cast<vec_t *>(buf + (ca * R + r) * W + v * VEC) = val;
+            for (int i = 0; i < kSlabPrefetch; ++i) {
+                const bool ok = real && dst_row[i] >= 0 && h0 + (dst_row[i] & 255) < H;
+                pre[i] = *reinterpret_cast<const vec_t *>(ok ? xb + src_off[i] : x);
+            }
+        };
+        // writes a fetched slab (plus any pieces beyond the prefetch plan) into buf
+        auto put = [&](float *buf, const vec_t *pre, int n_, int d_, int hc_) {
+            const int h0 = hc_ * TH;
+#pragma unroll
+            for (int i = 0; i < kSlabPrefetch; ++i)
+                if (dst_row[i] >= 0)
+                    *reinterpret_cast<vec_t *>(buf + (dst_row[i] >> 8)) =
+                        (h0 + (dst_row[i] & 255) < H) ? pre[i] : vec_t{};
+            for (int q = ll + kSlabPrefetch * kLoadThreads; q < npieces; q += kLoadThreads) {
+                const int v = q % WV, tt = q / WV;
+                const int r = tt % R, ca = tt / R;
+                vec_t val = vec_t{};
+                if (h0 + r < H)
+                    val = *reinterpret_cast<const vec_t *>(
+                        x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W +
+                        (ca >> 1) * DHW + (ca & 1) * HW + r * W + v * VEC);
+                *reinterpret_cast<vec_t *>(buf + (ca * R + r) * W + v * VEC) = val;
+            }
+        };
+        vec_t pa[kSlabPrefetch], pb[kSlabPrefetch];
+        // slab 0 now; slabs 1 and 2 in flight in registers
+        int n1 = n, d1 = d, h1 = hc;
+        fetch(pa, n1, d1, h1, ntask > 0);
+        put(slabs, pa, n1, d1, h1);
+        next(n1, d1, h1);
+        fetch(pa, n1, d1, h1, ntask > 1);
+        int n2 = n1, d2 = d1, h2 = h1;
+        next(n2, d2, h2);
+        fetch(pb, n2, d2, h2, ntask > 2);
+        __syncthreads();
+        // stage s: put slab s+1 (held in pa for even s, pb for odd s) into
+        // buffer (s+1)&1, refill that register set with slab s+3
+        for (int s = 0; s <= ntask; s += 2) {
+            if (s + 1 < ntask) put(slabs + sfl, pa, n1, d1, h1);
+            next(n1, d1, h1); next(n1, d1, h1);
+            fetch(pa, n1, d1, h1, s + 3 < ntask);
+            __syncthreads();
+            if (s + 1 > ntask) break;
+            if (s + 2 < ntask) put(slabs, pb, n2, d2, h2);
+            next(n2, d2, h2); next(n2, d2, h2);
+            fetch(pb, n2, d2, h2, s + 4 < ntask);
+            __syncthreads();
         }
-    };
-    // the first slab's loads fly while the filter is built
-    if (t_begin < t_end) fetch(n, d, hc);
+        return;
+    }
 
+    if (wave >= kWaves + kLoadWaves) {
+        // ---- store waves: store wave k owns staging rows k*8 .. k*8+7; lane
+        // l serves row k*8 + l/8 with column j = l%8, so one store
+        // instruction writes a whole 128-byte line of each of the 8 rows and
+        // every per-row bound is a per-lane value.  `cont` says the lane's row
+        // starts with a carried line head.  Task s-1 is stored in stage s.
+        const int j = lane & 7;
+        const int sc = (wave - kWaves - kLoadWaves) * 8 + (lane >> 3);
+        const bool row_ok = cob * 16 + sc < Cout;
+        const int64_t row_off = (int64_t)(cob * 16 + sc) * pplane;
+        const int kmax = (kLine - 1 + TH * Wp) / kLine;   // most whole lines in a row
+        bool cont = false;
+        __syncthreads();
+        __syncthreads();                       // stage 0: nothing to store yet
+        int ns = n, ds = d, hs = hc;
+        for (int s = 1; s <= ntask; ++s) {
+            int nn = ns, dn = ds, hn = hs;
+            next(nn, dn, hn);
+            const bool next_same_n = s < ntask && nn == ns;  // task s continues the streams
+            const int buf = (s - 1) & 1;
+            const float *sr = stage + buf * 16 * STR + sc * STR;
+            float *sn = stage + (buf ^ 1) * 16 * STR + sc * STR;
+            const int h0 = hs * TH;
+            const int len = min(TH, Hp - h0) * Wp;
+            float *first = out + (int64_t)ns * Cout * pplane + row_off + ((int64_t)ds * Hp + h0) * Wp;
+            // staging positions [start, end) hold task s-1's outputs (and, if
+            // continued, the carried line head [0, c0)); whole lines [lo, hi)
+            // go out with non-temporal 16-byte stores, the partial head
+            // [start, lo) with plain stores, the tail [hi, end) to the next
+            // staging set or, where the stream ends here, to memory
+            const int c0 = (int)(((uintptr_t)first >> 2) & (kLine - 1));
+            float *gl = first - c0;                                   // 128-byte aligned
+            const int end = c0 + len;
+            const int start = cont ? 0 : c0;
+            const int lo = min((start + kLine - 1) & ~(kLine - 1), end);
+            const int hi = max(lo, end & ~(kLine - 1));
+            const int nl = row_ok ? (hi - lo) / kLine : 0;
+            for (int k0 = 0; k0 < kmax; k0 += 4) {
+                v4f v[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)   // lo is a line boundary whenever nl > 0
+                    v[u] = *reinterpret_cast<const v4f *>(sr + min((lo & ~3) + (k0 + u) * kLine + 4 * j, STR - 4));
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (k0 + u < nl)
+                        __builtin_nontemporal_store(v[u], reinterpret_cast<v4f *>(gl + lo + (k0 + u) * kLine + 4 * j));
+            }
+            if (row_ok)
+                for (int p = start + j; p < lo; p += 8) gl[p] = sr[p];       // head: partial line
+            if (next_same_n) {                                               // tail: carried
+                for (int p = hi + j; p < end; p += 8) sn[p - hi] = sr[p];
+            } else if (row_ok) {                                             // tail: partial line
+                for (int p = hi + j; p < end; p += 8) gl[p] = sr[p];
+            }
+            // the next task's row starts with a carried line unless this
+            // task's last line was written as a head
+            cont = next_same_n && (hi < end || (end & (kLine - 1)) == 0);
+            __syncthreads();
+            ns = nn; ds = dn; hs = hn;
+        }
+        return;
+    }
+
+    // ---- compute waves: task s in stage s, MFMA into staging set s&1 ------
+    const int col = lane & 15;
+    const int kq = lane >> 4;
+    const int wblocks = (Wp + 15) / 16;
     build_wfrag(w, Cout, cob, KS, wfrag);
-
-    float a[KS];
     int soff[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
@@ -363,88 +502,80 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         beta[r] = (cbv * s1 + bv) * s2;
         co_off[r] = co * (int)pplane;
     }
-
-    // slab of the first task into buffer 0; then per task: put the next slab
-    // into the other buffer, fetch the one after, compute, one barrier
-    if (t_begin < t_end) put(slabs, n, d, hc);
     __syncthreads();                           // filter and first slab visible
+    float a[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) a[j] = wfrag[j * 64 + lane];
-    int hc2 = hc + 1, d2 = d, n2 = n;
-    if (hc2 == hchunks) { hc2 = 0; if (++d2 == Dp) { d2 = 0; ++n2; } }
-    if (t_begin + 1 < t_end) fetch(n2, d2, hc2);
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        float *cur = slabs + buf * slab_floats;
-        // next task's slab into the other buffer (its last readers finished
-        // before the previous iteration's barrier), then the loads after it
-        if (t + 1 < t_end) {
-            put(slabs + (buf ^ 1) * slab_floats, n2, d2, hc2);
-            int hc3 = hc2 + 1, d3 = d2, n3 = n2;
-            if (hc3 == hchunks) { hc3 = 0; if (++d3 == Dp) { d3 = 0; ++n3; } }
-            if (t + 2 < t_end) fetch(n3, d3, hc3);
-            hc2 = hc3; d2 = d3; n2 = n3;
-        }
-
-        const int h0 = hc * TH;
-        const int rows = min(TH, Hp - h0);
-        float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
-        // each wave takes rows hh = wave, wave + 4, ... two at a time (hh and
-        // hh + 4); a row's w-blocks go in pairs, each block's K range split
-        // over two accumulators: eight independent MFMA chains in flight, with
-        // all their LDS reads issued first
-        auto store_block = [&](float *orow, int wv, const v4f &p, const v4f &q) {
+    for (int s = 0; s <= ntask; ++s) {
+        if (s < ntask) {
+            const int buf = s & 1;
+            const float *cur = slabs + buf * sfl;
+            float *stg = stage + buf * 16 * STR;
+            const int h0 = hc * TH;
+            const int rows = min(TH, Hp - h0);
+            float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
+            // staging row of channel co starts at its line base: the task's
+            // first output sits at its float index within its 128-byte line
+            float *srow[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (co_ok[r]) orow[co_off[r] + wv] = __builtin_fmaf(p[r] + q[r], alpha, beta[r]);
-        };
-        for (int hh = wave; hh < rows; hh += 2 * kWaves) {
-            const int hh2 = hh + kWaves;
-            const bool two = hh2 < rows;           // wave-uniform
-            const float *srowA = cur + hh * W, *srowB = cur + (two ? hh2 : hh) * W;
-            float *orowA = ob + hh * Wp, *orowB = ob + hh2 * Wp;
-            for (int wb = 0; wb < wblocks; wb += 2) {
-                const int wv0 = wb * 16 + col, wv1 = wv0 + 16;
-                const int wc0 = min(wv0, Wp - 1), wc1 = min(wv1, Wp - 1);
-                float a0[KS], a1[KS], b0[KS], b1[KS];
+                srow[r] = stg + (4 * kq + r) * STR + (int)(((uintptr_t)(ob + co_off[r]) >> 2) & (kLine - 1));
+            // each wave takes rows hh = wave, wave + 4, ... two at a time (hh
+            // and hh + 4); a row's w-blocks go in pairs, each block's K range
+            // split over two accumulators: eight independent MFMA chains in
+            // flight, with all their LDS reads issued first
+            auto stage_block = [&](int hh, int wv, const v4f &p, const v4f &q) {
 #pragma unroll
-                for (int j = 0; j < KS; ++j) {
-                    a0[j] = srowA[wc0 + soff[j]];
-                    a1[j] = srowA[wc1 + soff[j]];
-                    b0[j] = srowB[wc0 + soff[j]];
-                    b1[j] = srowB[wc1 + soff[j]];
-                }
-                v4f pA0 = {0.0f, 0.0f, 0.0f, 0.0f}, qA0 = pA0, pA1 = pA0, qA1 = pA0;
-                v4f pB0 = pA0, qB0 = pA0, pB1 = pA0, qB1 = pA0;
+                for (int r = 0; r < 4; ++r)
+                    if (co_ok[r]) srow[r][hh * Wp + wv] = __builtin_fmaf(p[r] + q[r], alpha, beta[r]);
+            };
+            for (int hh = wave; hh < rows; hh += 2 * kWaves) {
+                const int hh2 = hh + kWaves;
+                const bool two = hh2 < rows;           // wave-uniform
+                const float *srowA = cur + hh * W, *srowB = cur + (two ? hh2 : hh) * W;
+                for (int wb = 0; wb < wblocks; wb += 2) {
+                    const int wv0 = wb * 16 + col, wv1 = wv0 + 16;
+                    const int wc0 = min(wv0, Wp - 1), wc1 = min(wv1, Wp - 1);
+                    float a0[KS], a1[KS], b0[KS], b1[KS];
 #pragma unroll
-                for (int j = 0; j < KS; j += 2) {
-                    pA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a0[j], pA0, 0, 0, 0);
-                    pA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a1[j], pA1, 0, 0, 0);
-                    pB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b0[j], pB0, 0, 0, 0);
-                    pB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b1[j], pB1, 0, 0, 0);
-                    qA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a0[j + 1], qA0, 0, 0, 0);
-                    qA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a1[j + 1], qA1, 0, 0, 0);
-                    qB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b0[j + 1], qB0, 0, 0, 0);
-                    qB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b1[j + 1], qB1, 0, 0, 0);
-                }
-                const bool w1 = wb + 1 < wblocks && wv1 < Wp;
-                if (wv0 < Wp) store_block(orowA, wv0, pA0, qA0);
-                if (w1) store_block(orowA, wv1, pA1, qA1);
-                if (two) {
-                    if (wv0 < Wp) store_block(orowB, wv0, pB0, qB0);
-                    if (w1) store_block(orowB, wv1, pB1, qB1);
+                    for (int j = 0; j < KS; ++j) {
+                        a0[j] = srowA[wc0 + soff[j]];
+                        a1[j] = srowA[wc1 + soff[j]];
+                        b0[j] = srowB[wc0 + soff[j]];
+                        b1[j] = srowB[wc1 + soff[j]];
+                    }
+                    v4f pA0 = {0.0f, 0.0f, 0.0f, 0.0f}, qA0 = pA0, pA1 = pA0, qA1 = pA0;
+                    v4f pB0 = pA0, qB0 = pA0, pB1 = pA0, qB1 = pA0;
+#pragma unroll
+                    for (int j = 0; j < KS; j += 2) {
+                        pA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a0[j], pA0, 0, 0, 0);
+                        pA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a1[j], pA1, 0, 0, 0);
+                        pB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b0[j], pB0, 0, 0, 0);
+                        pB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b1[j], pB1, 0, 0, 0);
+                        qA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a0[j + 1], qA0, 0, 0, 0);
+                        qA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a1[j + 1], qA1, 0, 0, 0);
+                        qB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b0[j + 1], qB0, 0, 0, 0);
+                        qB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b1[j + 1], qB1, 0, 0, 0);
+                    }
+                    const bool w1 = wb + 1 < wblocks && wv1 < Wp;
+                    if (wv0 < Wp) stage_block(hh, wv0, pA0, qA0);
+                    if (w1) stage_block(hh, wv1, pA1, qA1);
+                    if (two) {
+                        if (wv0 < Wp) stage_block(hh2, wv0, pB0, qB0);
+                        if (w1) stage_block(hh2, wv1, pB1, qB1);
+                    }
                 }
             }
+            next(n, d, hc);
         }
-        __syncthreads();                       // next slab written; this one consumed
-        if (++hc == hchunks) { hc = 0; if (++d == Dp) { d = 0; ++n; } }
+        __syncthreads();
     }
 }
 
 }  // namespace
 
-constexpr size_t kSlabLdsMax = 48 * 1024;   // keep several workgroups resident per CU
+constexpr size_t kSlabLdsMax = 52 * 1024;   // three workgroups per CU
 
 template <int KS>
 static hipError_t launch_ks(const float *x, const float *w, const float *conv_bias,
@@ -461,9 +592,9 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
     const unsigned gy = (unsigned)((Cout + 15) / 16);
 
     if constexpr (KS > 0) {
-        // pooled rows per task: up to 16, as many as the LDS budget allows
-        int TH = Hp < 16 ? Hp : 16;
-        auto slab_bytes = [&](int th) { return (size_t)(KS * 64 + 2 * Cin * 2 * (th + 1) * W) * sizeof(float); };
+        // pooled rows per task: up to 8, as many as the LDS budget allows
+        int TH = Hp < 8 ? Hp : 8;
+        auto slab_bytes = [&](int th) { return (size_t)slab_lds_floats(KS, Cin, th, W, Wp) * sizeof(float); };
         while (TH > 1 && slab_bytes(TH) > kSlabLdsMax) --TH;
         if (slab_bytes(TH) <= kSlabLdsMax) {
             const size_t lds = slab_bytes(TH);
@@ -472,7 +603,7 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
             const bool vec4 = (W % 4 == 0) && (((uintptr_t)x & 15) == 0);
             const void *fn = vec4 ? (const void *)fused3d_f32_slab_kernel<KS, 4>
                                   : (const void *)fused3d_f32_slab_kernel<KS, 1>;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess ||
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSlabThreads, lds) != hipSuccess ||
                 per_cu < 1)
                 per_cu = 1;
             int64_t wgs = (int64_t)cus * per_cu / gy;
@@ -481,11 +612,11 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
             const int per = (int)((ntasks + wgs - 1) / wgs);
             const unsigned gx = (unsigned)((ntasks + per - 1) / per);
             if (vec4)
-                hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 4>), dim3(gx, gy), dim3(kThreads), lds,
+                hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 4>), dim3(gx, gy), dim3(kSlabThreads), lds,
                                    stream, x, w, conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H,
                                    (int)W, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
             else
-                hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 1>), dim3(gx, gy), dim3(kThreads), lds,
+                hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 1>), dim3(gx, gy), dim3(kSlabThreads), lds,
                                    stream, x, w, conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H,
                                    (int)W, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
             return hipGetLastError();
