@@ -22,10 +22,14 @@
 //    comes from lane l-1 through a DPP wave shift, not from memory;
 //  * per plane a wave loads the 9 input rows 2h0-1 .. 2h0+7 (contiguous in
 //    memory), two planes per step, so 18 independent 16-byte loads per lane
-//    are in flight;
-//  * 4 waves of a workgroup own 16 consecutive output rows, so the shared
-//    boundary row between waves is re-read from L2, not HBM; workgroups are
-//    remapped so consecutive tiles share one XCD's L2;
+//    are in flight.  The 7 rows only this wave reads are loaded
+//    non-temporally; the first and last rows, which the neighbouring waves
+//    read as well, are plain loads so the second read hits L2.  (Measured on
+//    this read/write mix: non-temporal loads and stores together stream
+//    faster than either alone.)
+//  * 8 waves of a workgroup own 32 consecutive output rows (65 contiguous
+//    input rows per plane) and walk 8 output planes; workgroups are remapped
+//    so consecutive tiles share one XCD's L2;
 //  * each lane stores its 2 outputs as one 8-byte non-temporal store (a wave
 //    writes a contiguous 512-byte output row segment).
 // Ragged W (not a multiple of 4, or a misaligned slice) takes the same path
@@ -35,15 +39,16 @@
 namespace ct {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTH = 4;            // output rows per wave
 constexpr int kRows = 2 * kTH + 1; // input rows per plane
-constexpr int kTD = 16;           // output planes per task
+constexpr int kTD = 8;            // output planes per task
 constexpr int kTW = 128;          // output columns per task (2 per lane)
 
 struct f4 { float x, y, z, w; };
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float shr1(float v)
 {
@@ -51,13 +56,14 @@ __device__ __forceinline__ float shr1(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, false));
 }
 
-template <bool kVec>
+template <bool kVec, bool kNT>
 __device__ __forceinline__ f4 load_row4(const float *__restrict__ row, int c, int W)
 {
     f4 v;
     if (kVec) {
         if (c + 3 < W) {
-            const float4 t = *reinterpret_cast<const float4 *>(row + c);
+            const v4f *p = reinterpret_cast<const v4f *>(row + c);
+            const v4f t = kNT ? __builtin_nontemporal_load(p) : *p;
             v.x = t.x; v.y = t.y; v.z = t.z; v.w = t.w;
         } else {
             v.x = v.y = v.z = v.w = 0.0f;   // W % 4 == 0: whole vector in or out
@@ -83,8 +89,11 @@ __device__ __forceinline__ void plane_sums(const float *__restrict__ xs, int pla
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
         const int row = 2 * h0 - 1 + r;
+        // rows 0 and kRows-1 are shared with the neighbouring waves
         if (pok && row >= 0 && row < H)
-            v[r] = load_row4<kVec>(xs + ((int64_t)plane * H + row) * W, c, W);
+            v[r] = (r != 0 && r != kRows - 1)
+                       ? load_row4<kVec, true>(xs + ((int64_t)plane * H + row) * W, c, W)
+                       : load_row4<kVec, false>(xs + ((int64_t)plane * H + row) * W, c, W);
         else
             v[r].x = v[r].y = v[r].z = v[r].w = 0.0f;
     }
