@@ -18,6 +18,9 @@ timed on a bounded sample of the same workloads.
   python bench.py --ops copy        # plain 1 GiB device copy (counter calibration)
   python bench.py --ops fused3d_f32,unfused3d_f32   # fusion vs materialising the
                                     # [128,16,31,63,63] pre-pool tensor, then a 2-pool
+  python bench.py --summarize-trace DIR              # rocprofv3 --kernel-trace CSVs -> table
+  python bench.py --summarize-counters FETCH WRITE   # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+                                    # CSVs -> table + profiles/traffic.json
 """
 from __future__ import annotations
 
@@ -52,8 +55,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash(op):
-    p = os.path.join(ROOT, "transposed_conv_pooling_amd", "csrc", OP_SOURCES[op])
+# Kernels as rocprofv3 names them -> (op or kernel key, source file,
+# algorithmic bytes of one launch at the bench workload).  The bytes are the
+# same figures make_ops() computes from the tensors.
+KERNELS = [
+    ("fused3d_f32_slab_kernel", "fused3d_f32", "fused3d_f32.hip", 143258752),
+    ("avgpool3d_k3s2p1_kernel", "avgpool3d", "avgpool3d.hip", 9663676416),
+    ("convT1d_f32", "convT1d", "convT1d_f32.hip", 1610752000),
+    ("fused3d_bf16_kernel", "fused3d_bf16", "fused3d_bf16.hip", 75931904),
+    ("convT1d_bf16_kernel", "convT1d_bf16", "convT1d_bf16.hip", 1342296064),
+    ("convT3d_s2_kernel", "convT3d_s2", "convT3d_s2.hip", 1033106496),
+    ("avgpool3d_generic_kernel", "avgpool3d_generic", "generic.hip", 1126023168),
+]
+
+
+def kernel_key(name):
+    for sub, key, src, nbytes in KERNELS:
+        if sub in name:
+            return key, src, nbytes
+    return None
+
+
+def source_hash(op, src=None):
+    p = os.path.join(ROOT, "transposed_conv_pooling_amd", "csrc", src or OP_SOURCES[op])
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
@@ -239,7 +263,88 @@ def make_ops(names, dev):
     return ops
 
 
+# ------------------------------------------------- rocprofv3 summaries --
+def _csv_rows(path):
+    import csv
+    files = [path] if os.path.isfile(path) else [
+        os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs]
+    rows = []
+    for f in sorted(files):
+        if f.endswith(".csv"):
+            rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def summarize_trace(path):
+    """Markdown table of a `rocprofv3 --kernel-trace` run: per kernel, calls
+    and duration statistics in microseconds, and algorithmic GB/s at the
+    average duration."""
+    durs = {}
+    for r in _csv_rows(path):
+        if "Kernel_Name" in r and "Start_Timestamp" in r and "End_Timestamp" in r:
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            durs.setdefault(r["Kernel_Name"], []).append(d)
+    total = sum(sum(v) for v in durs.values()) or 1.0
+    print("| kernel | calls | avg us | min us | max us | share | algorithmic GB/s at avg |")
+    print("|---|---|---|---|---|---|---|")
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        k = kernel_key(name)
+        avg = sum(v) / len(v)
+        gbs = f"{k[2] / avg / 1e3:.0f}" if k else "-"
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        label = f"{k[0]} (`{short}`)" if k else f"`{short}`"
+        print(f"| {label} | {len(v)} | {avg:.1f} | {min(v):.1f} | {max(v):.1f} | "
+              f"{100 * sum(v) / total:.2f}% | {gbs} |")
+
+
+def summarize_counters(fetch_path, write_path):
+    """HBM bytes per launch from two `rocprofv3 --pmc` runs (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+    for the bench's 1 GiB device copy; writes profiles/traffic.json (with a
+    hash of each kernel's source) and prints a markdown table."""
+    def per_kernel(path, counter):
+        vals, copy = {}, []
+        for r in _csv_rows(path):
+            if r.get("Counter_Name") != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in r["Kernel_Name"]:
+                if int(r.get("Grid_Size", 0)) >= 1 << 17:     # the 1 GiB copy, not the uploads
+                    copy.append(v)
+                continue
+            k = kernel_key(r["Kernel_Name"])
+            if k:
+                vals.setdefault(k, []).append(v)
+        return {k: sum(v) / len(v) for k, v in vals.items()}, (sum(copy) / len(copy) if copy else None)
+    fetch, fcopy = per_kernel(fetch_path, "FETCH_SIZE")
+    write, wcopy = per_kernel(write_path, "WRITE_SIZE")
+    if not fcopy or not wcopy:
+        raise SystemExit("no 1 GiB copy dispatch found: run the counters with --ops ...,copy")
+    gib_kib = float(1 << 20)
+    fs, ws = gib_kib / fcopy, gib_kib / wcopy
+    out = {}
+    print(f"Calibration (1 GiB copy): FETCH_SIZE {fcopy:.0f} KiB, WRITE_SIZE {wcopy:.0f} KiB per "
+          f"dispatch -> scale {fs:.4f} / {ws:.4f}.\n")
+    print("| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read bytes | scaled write bytes | "
+          "total bytes | algorithmic bytes | total / algorithmic |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (key, src, alg) in sorted(set(fetch) & set(write), key=lambda k: -k[2]):
+        rb, wb = fetch[(key, src, alg)] * 1024 * fs, write[(key, src, alg)] * 1024 * ws
+        out[key] = {"bytes_per_launch": int(rb + wb), "read_bytes": int(rb), "write_bytes": int(wb),
+                    "source_sha256_16": source_hash(None, src), "source": src,
+                    "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}
+        print(f"| {key} | {fetch[(key, src, alg)]:.0f} | {write[(key, src, alg)]:.0f} | {rb:.4g} | "
+              f"{wb:.4g} | {rb + wb:.4g} | {alg:.4g} | {(rb + wb) / alg:.3f} |")
+    dst = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(out, open(dst, "w"), indent=1)
+    print(f"\nwrote {os.path.relpath(dst, ROOT)}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        return summarize_trace(sys.argv[2])
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        return summarize_counters(sys.argv[2], sys.argv[3])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
