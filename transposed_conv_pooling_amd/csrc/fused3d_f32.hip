@@ -264,14 +264,17 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // partial lines in a workgroup are written with plain stores (for L2 to
 // merge with the neighbour's part).  Staging is double-buffered as well:
 // one barrier per task separates a task's compute from its store phase.
-constexpr int kSlabPrefetch = 8;   // slab pieces each loader lane keeps in flight
+constexpr int kSlabPrefetch = 5;   // slab pieces each loader lane keeps in flight
 constexpr int kLine = 32;          // floats per 128-byte line
 // 4 compute waves, 2 loader waves, 2 store waves.  vmcnt counts a wave's
 // loads and stores together and retires them in order, so a wave that both
 // stores and prefetches would wait for its earlier stores before each slab;
 // here only the loader waves load and only the store waves store.
-constexpr int kLoadWaves = 2;
-constexpr int kStoreWaves = 2;
+constexpr int kLoadWaves = 3;
+constexpr int kStoreWaves = 4;
+constexpr int kRowsPerStoreWave = 16 / kStoreWaves;       // staging rows per store wave
+constexpr int kLanesPerRow = 64 / kRowsPerStoreWave;      // lanes on one row (16 B each)
+constexpr int kLinesPerStore = kLanesPerRow / 8;          // lines of a row per store instruction
 constexpr int kLoadThreads = 64 * kLoadWaves;
 constexpr int kSlabThreads = 64 * (kWaves + kLoadWaves + kStoreWaves);
 
@@ -414,16 +417,20 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
     }
 
     if (wave >= kWaves + kLoadWaves) {
-        // ---- store waves: store wave k owns staging rows k*8 .. k*8+7; lane
-        // l serves row k*8 + l/8 with column j = l%8, so one store
-        // instruction writes a whole 128-byte line of each of the 8 rows and
-        // every per-row bound is a per-lane value.  `cont` says the lane's row
-        // starts with a carried line head.  Task s-1 is stored in stage s.
-        const int j = lane & 7;
-        const int sc = (wave - kWaves - kLoadWaves) * 8 + (lane >> 3);
+        // ---- store waves: store wave k owns kRowsPerStoreWave staging rows;
+        // lane l serves row k*kRowsPerStoreWave + l/kLanesPerRow with column
+        // j = l%kLanesPerRow, so one store instruction writes kLinesPerStore
+        // whole 128-byte lines of each of its rows and every per-row bound
+        // is a per-lane value.  (Stores are spread over several waves: each
+        // wave keeps at most 63 memory operations in flight, and
+        // non-temporal stores are acknowledged late.)  `cont` says the lane's
+        // row starts with a carried line head.  Task s-1 is stored in stage s.
+        const int j = lane % kLanesPerRow;
+        const int sc = (wave - kWaves - kLoadWaves) * kRowsPerStoreWave + lane / kLanesPerRow;
         const bool row_ok = cob * 16 + sc < Cout;
         const int64_t row_off = (int64_t)(cob * 16 + sc) * pplane;
-        const int kmax = (kLine - 1 + TH * Wp) / kLine;   // most whole lines in a row
+        // most store instructions a row needs: its whole lines, kLinesPerStore at a time
+        const int kmax = ((kLine - 1 + TH * Wp) / kLine + kLinesPerStore - 1) / kLinesPerStore;
         bool cont = false;
         __syncthreads();
         __syncthreads();                       // stage 0: nothing to store yet
@@ -449,23 +456,34 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             const int start = cont ? 0 : c0;
             const int lo = min((start + kLine - 1) & ~(kLine - 1), end);
             const int hi = max(lo, end & ~(kLine - 1));
-            const int nl = row_ok ? (hi - lo) / kLine : 0;
+            const int nf = row_ok ? (hi - lo) / 4 : 0;             // 16-byte pieces of whole lines
+            constexpr int kTail = (kLine + kLanesPerRow - 1) / kLanesPerRow;
+            constexpr int kStep = 4 * kLanesPerRow;                    // floats of a row per instruction
+            // all reads of a batch (and of the tail) go out before any store,
+            // so the wave waits for LDS once per batch
+            float tl[kTail];
+#pragma unroll
+            for (int u = 0; u < kTail; ++u) tl[u] = sr[min(hi + j + kLanesPerRow * u, STR - 1)];
             for (int k0 = 0; k0 < kmax; k0 += 4) {
                 v4f v[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)   // lo is a line boundary whenever nl > 0
-                    v[u] = *reinterpret_cast<const v4f *>(sr + min((lo & ~3) + (k0 + u) * kLine + 4 * j, STR - 4));
+                for (int u = 0; u < 4; ++u)   // lo is a line boundary whenever nf > 0
+                    v[u] = *reinterpret_cast<const v4f *>(sr + min((lo & ~3) + (k0 + u) * kStep + 4 * j, STR - 4));
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (k0 + u < nl)
-                        __builtin_nontemporal_store(v[u], reinterpret_cast<v4f *>(gl + lo + (k0 + u) * kLine + 4 * j));
+                    if ((k0 + u) * kLanesPerRow + j < nf)
+                        __builtin_nontemporal_store(v[u], reinterpret_cast<v4f *>(gl + lo + (k0 + u) * kStep + 4 * j));
             }
             if (row_ok)
-                for (int p = start + j; p < lo; p += 8) gl[p] = sr[p];       // head: partial line
-            if (next_same_n) {                                               // tail: carried
-                for (int p = hi + j; p < end; p += 8) sn[p - hi] = sr[p];
-            } else if (row_ok) {                                             // tail: partial line
-                for (int p = hi + j; p < end; p += 8) gl[p] = sr[p];
+                for (int p = start + j; p < lo; p += kLanesPerRow) gl[p] = sr[p];   // head: partial line
+            // tail [hi, end): fewer than 32 floats
+#pragma unroll
+            for (int u = 0; u < kTail; ++u) {
+                const int p = hi + j + kLanesPerRow * u;
+                if (p < end) {
+                    if (next_same_n) sn[p - hi] = tl[u];                     // carried
+                    else if (row_ok) gl[p] = tl[u];                          // partial line
+                }
             }
             // the next task's row starts with a carried line unless this
             // task's last line was written as a head
@@ -488,20 +506,16 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         const int ci = kap >> 3, tap = kap & 7;
         soff[j] = ((ci * 2 + (tap >> 2)) * R + ((tap >> 1) & 1)) * W + (tap & 1);
     }
+    // The MFMA runs with the operands swapped, D = S^T (16 voxels x 16
+    // channels): lane (kq, col) then holds voxels 4kq .. 4kq+3 of its block
+    // for channel cob*16 + col, four consecutive outputs of one channel.
     // folded epilogue ((S/8 + cb)*s1 + b)*s2 = S*alpha + beta[co]
     const float alpha = 0.125f * s1 * s2;
-    float beta[4];
-    int co_off[4];            // per-item output offsets fit in int32 (checked by the shim)
-    bool co_ok[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int co = cob * 16 + 4 * kq + r;
-        co_ok[r] = co < Cout;
-        const float cbv = (conv_bias && co_ok[r]) ? conv_bias[co] : 0.0f;
-        const float bv = (bias && co_ok[r]) ? bias[co] : 0.0f;
-        beta[r] = (cbv * s1 + bv) * s2;
-        co_off[r] = co * (int)pplane;
-    }
+    const int co_l = cob * 16 + col;
+    const bool co_ok = co_l < Cout;
+    const float beta = ((conv_bias && co_ok ? conv_bias[co_l] : 0.0f) * s1 +
+                        (bias && co_ok ? bias[co_l] : 0.0f)) * s2;
+    const int co_off = co_l * (int)pplane;    // per-item output offsets fit in int32 (checked by the shim)
     __syncthreads();                           // filter and first slab visible
     float a[KS];
 #pragma unroll
@@ -517,18 +531,17 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
             // staging row of channel co starts at its line base: the task's
             // first output sits at its float index within its 128-byte line
-            float *srow[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                srow[r] = stg + (4 * kq + r) * STR + (int)(((uintptr_t)(ob + co_off[r]) >> 2) & (kLine - 1));
+            float *srow = stg + col * STR + (int)(((uintptr_t)(ob + co_off) >> 2) & (kLine - 1)) + 4 * kq;
             // each wave takes rows hh = wave, wave + 4, ... two at a time (hh
             // and hh + 4); a row's w-blocks go in pairs, each block's K range
             // split over two accumulators: eight independent MFMA chains in
             // flight, with all their LDS reads issued first
-            auto stage_block = [&](int hh, int wv, const v4f &p, const v4f &q) {
+            // (block voxels 4kq+r at w = wv0 + r of the block start wv0)
+            auto stage_block = [&](int hh, int wv0, const v4f &p, const v4f &q) {
+                float *dst = srow + hh * Wp + wv0;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (co_ok[r]) srow[r][hh * Wp + wv] = __builtin_fmaf(p[r] + q[r], alpha, beta[r]);
+                    if (co_ok && wv0 + 4 * kq + r < Wp) dst[r] = __builtin_fmaf(p[r] + q[r], alpha, beta);
             };
             for (int hh = wave; hh < rows; hh += 2 * kWaves) {
                 const int hh2 = hh + kWaves;
@@ -549,21 +562,21 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
                     v4f pB0 = pA0, qB0 = pA0, pB1 = pA0, qB1 = pA0;
 #pragma unroll
                     for (int j = 0; j < KS; j += 2) {
-                        pA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a0[j], pA0, 0, 0, 0);
-                        pA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], a1[j], pA1, 0, 0, 0);
-                        pB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b0[j], pB0, 0, 0, 0);
-                        pB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b1[j], pB1, 0, 0, 0);
-                        qA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a0[j + 1], qA0, 0, 0, 0);
-                        qA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], a1[j + 1], qA1, 0, 0, 0);
-                        qB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b0[j + 1], qB0, 0, 0, 0);
-                        qB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j + 1], b1[j + 1], qB1, 0, 0, 0);
+                        pA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], a[j], pA0, 0, 0, 0);
+                        pA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j], a[j], pA1, 0, 0, 0);
+                        pB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(b0[j], a[j], pB0, 0, 0, 0);
+                        pB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b1[j], a[j], pB1, 0, 0, 0);
+                        qA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j + 1], a[j + 1], qA0, 0, 0, 0);
+                        qA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j + 1], a[j + 1], qA1, 0, 0, 0);
+                        qB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(b0[j + 1], a[j + 1], qB0, 0, 0, 0);
+                        qB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b1[j + 1], a[j + 1], qB1, 0, 0, 0);
                     }
-                    const bool w1 = wb + 1 < wblocks && wv1 < Wp;
-                    if (wv0 < Wp) stage_block(hh, wv0, pA0, qA0);
-                    if (w1) stage_block(hh, wv1, pA1, qA1);
+                    const bool w1 = wb + 1 < wblocks;     // second block exists
+                    stage_block(hh, wb * 16, pA0, qA0);
+                    if (w1) stage_block(hh, wb * 16 + 16, pA1, qA1);
                     if (two) {
-                        if (wv0 < Wp) stage_block(hh2, wv0, pB0, qB0);
-                        if (w1) stage_block(hh2, wv1, pB1, qB1);
+                        stage_block(hh2, wb * 16, pB0, qB0);
+                        if (w1) stage_block(hh2, wb * 16 + 16, pB1, qB1);
                     }
                 }
             }
