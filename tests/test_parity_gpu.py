@@ -284,6 +284,7 @@ CONV1D_SMALL = [
     (2, 32, 16, 8, 5, 3, False),         # one tile per item, most waves idle
     (1, 32, 64, 4, 5, 3, True),          # shortest fast-path input
     (5, 32, 64, 1028, 5, 3, False),      # tiles straddling batch items
+    (8, 32, 64, 20004, 5, 3, True),      # more tiles than waves: halos carried between tiles
 ]
 
 

@@ -37,6 +37,7 @@ namespace ct {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -142,7 +143,7 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // at compile time, so every LDS address is a per-lane base plus an immediate
 // offset and the k-loop carries no index arithmetic.  Requires L % 4 == 0 and
 // dil*(K-1) % 4 == 0 (whole float4 pieces are either inside or outside
-// [0, L)) and 16-byte aligned x.
+// [0, L) and [0, Lo)) and 16-byte aligned x and y.
 // Wave-independent path for the same specialised geometry: a workgroup of
 // WW waves shares one copy of the weight fragments (40 KiB of LDS, staged
 // once behind the kernel's only barrier); each wave then walks its own
@@ -211,10 +212,15 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
 
     // strip piece q = ci * (kTs/4) + t4; unconditional loads from clamped
     // addresses (L % 4 == 0: a piece is wholly inside or outside [0, L)),
-    // masked when written
+    // masked when written.  When a tile continues the previous tile of the
+    // same batch item, its halo pieces (t4 < kHalo/4) are the previous
+    // strip's last kHalo positions: they are copied inside LDS, not loaded
+    // (their load slot reads x[0..], so every tile issues the same number of
+    // loads), and the tile fetches only its own kTW positions per channel.
     v4f_ pre[G::kQPerLane];
-    unsigned pok = 0;                                        // bit i: piece i inside [0, L)
-    auto fetch = [&](int tile) {
+    unsigned pok = 0;                                        // bit i: piece i is loaded data
+    unsigned pput = 0;                                       // bit i: piece i is written
+    auto fetch = [&](int tile, bool carry) {
         const int n = tile / tiles_per_n;
         const int o0 = (tile - n * tiles_per_n) * G::kTW;
         const float *xb = x + (int64_t)n * Cin * L + (o0 - G::kHalo);
@@ -223,12 +229,14 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
             const int q = lane + 64 * i;
             const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
             const int pos = o0 - G::kHalo + 4 * t4;
-            const bool ok = q < G::kQ && ci < Cin && pos >= 0 && pos < L;
+            const bool mine = q < G::kQ && !(carry && t4 < G::kHalo / 4);
+            const bool ok = mine && ci < Cin && pos >= 0 && pos < L;
             pre[i] = *reinterpret_cast<const v4f_ *>(ok ? xb + ci * L + 4 * t4 : x);
             pok = ok ? pok | (1u << i) : pok & ~(1u << i);
+            pput = mine ? pput | (1u << i) : pput & ~(1u << i);
         }
     };
-    if (t_begin < t_end) fetch(t_begin);
+    if (t_begin < t_end) fetch(t_begin, false);
     __syncthreads();                                         // weights and bias staged
 
     const float *xl = xs + kq * G::kStr + G::kHalo + col;   // lane's B base
@@ -239,23 +247,51 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
         // this wave alone reads and writes its strip, and a wave's LDS
         // operations complete in order: compiler-only fences suffice
         __builtin_amdgcn_wave_barrier();
+        if (tile > t_begin && o0 > 0) {
+            // halo = the previous strip's positions kTW .. kTW+kHalo-1, moved
+            // to the front before the new pieces overwrite them
+            constexpr int kHq = CIN4 * (G::kHalo / 4);      // halo pieces
+            v4f_ hv[(kHq + 63) / 64];
+#pragma unroll
+            for (int i = 0; i < (kHq + 63) / 64; ++i) {
+                const int q = lane + 64 * i;
+                const int ci = q / (G::kHalo / 4), u = q % (G::kHalo / 4);
+                hv[i] = *reinterpret_cast<const v4f_ *>(xs + min(ci, CIN4 - 1) * G::kStr + G::kTW + 4 * u);
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < (kHq + 63) / 64; ++i) {
+                const int q = lane + 64 * i;
+                const int ci = q / (G::kHalo / 4), u = q % (G::kHalo / 4);
+                if (q < kHq) *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * u) = hv[i];
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
 #pragma unroll
         for (int i = 0; i < G::kQPerLane; ++i) {
             const int q = lane + 64 * i;
-            if (q < G::kQ) {
+            if ((pput >> i) & 1) {
                 const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
                 *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * t4) =
                     ((pok >> i) & 1) ? pre[i] : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
         __builtin_amdgcn_wave_barrier();
-        if (tile + 1 < t_end) fetch(tile + 1);
+        if (tile + 1 < t_end) {
+            // the next tile continues this one when it is in the same batch item
+            const int n1 = (tile + 1) / tiles_per_n;
+            fetch(tile + 1, n1 == n);
+        }
 
-        // accumulators start at the bias of their channels (D rows 4kq .. +3)
+        // The MFMAs run with the operands swapped, D = Y^T (16 outputs x 16
+        // channels): lane (kq, col) holds outputs 16b + 4kq .. +3 of channel
+        // 16m + col, four consecutive floats of one output row.  Each
+        // accumulator starts at its channel's bias.
         v4f acc[4][NB];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const v4f b4 = *reinterpret_cast<const v4f *>(bsh + 16 * m + 4 * kq);
+            const float bc = bsh[16 * m + col];
+            const v4f b4 = {bc, bc, bc, bc};
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[m][b] = b4;
         }
@@ -273,29 +309,30 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
-                        acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bvv[b], acc[m][b], 0, 0, 0);
+                        acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(bvv[b], av[m], acc[m][b], 0, 0, 0);
             }
         }
 
-        // buffer stores over this batch item's output (word 3 0x00020000:
-        // 32-bit data format); masked lanes store past the range, which the
-        // hardware drops, so no store sits behind a branch
+        // 16-byte buffer stores over this batch item's output (word 3
+        // 0x00020000: 32-bit data format): rows start 16-byte aligned and a
+        // lane's four outputs are wholly inside or outside [0, Lo) (Lo % 4 ==
+        // 0); masked lanes store past the range, which the hardware drops, so
+        // no store sits behind a branch and every tile issues the same number
+        // of stores (4*NB, well under the 63 memory operations a wave can have
+        // in flight, so waiting for the next strip's loads never waits for
+        // this tile's stores)
         const __amdgpu_buffer_rsrc_t yr =
             __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * Cout * Lo, 0, Cout * Lo * 4, 0x00020000);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) {
+            const int co = cog * kCO + 16 * m + col;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int co = cog * kCO + 16 * m + 4 * kq + r;
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const int o = o0 + 16 * b + col;
-                    const int off = (co < Cout && o < Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;   // past the range
-                    // (__float_as_uint: a bit_cast of the vector element
-                    // lvalue acc[m][b][r] read element 0 for every r)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][b][r]), yr, off, 0, 0);
-                }
+            for (int b = 0; b < NB; ++b) {
+                const int o = o0 + 16 * b + 4 * kq;
+                const int off = (co < Cout && o < Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;   // past the range
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[m][b]), yr, off, 0, 0);
             }
+        }
     }
 }
 
@@ -331,7 +368,7 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
     int64_t str = ((ts + 63) / 64) * 64 + 16;
     if (str - 64 >= ts) str -= 64;
     if (cin4 == 32 && Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 &&
-        (((uintptr_t)x) & 15) == 0) {
+        (((uintptr_t)x) & 15) == 0 && (((uintptr_t)out) & 15) == 0) {
         typedef WaveGeom<32, 5, 3, kWaveNB, kWaveWW> G;
         const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW>;
         const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
