@@ -58,20 +58,17 @@ __device__ __forceinline__ float bf16_to_f32(unsigned short b)
     return __uint_as_float(((unsigned)b) << 16);
 }
 
-// round to nearest even; NaN stays a quiet NaN
+// round to nearest even (one v_cvt_pk_bf16_f32 on gfx950); NaN stays a NaN
 __device__ __forceinline__ unsigned short f32_to_bf16(float f)
 {
-    unsigned u = __float_as_uint(f);
-    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (unsigned short)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (unsigned short)(u >> 16);
+    return __builtin_bit_cast(unsigned short, (__bf16)f);
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Byte sizes of the LDS regions (shared with the launcher).
 __host__ __device__ inline int raw_bytes() { return kCiChunk * kCoGroup * 27 * 2; }
-__host__ __device__ inline int afrag_bytes(int ksteps) { return 2 * 8 * kCoGroup * (4 * ksteps + 2) * 2; }
+__host__ __device__ inline int afrag_bytes(int ksteps) { return 2 * 8 * kCoGroup * (4 * ksteps + 8) * 2; }
 // one slab: 2 planes x (th + 1) rows x W positions x cs channels (u16)
 __host__ __device__ inline int slab_bytes(int th, int W, int cs) { return 2 * (th + 1) * W * cs * 2; }
 // The epilogue constants sit after the larger of the prologue regions and the
@@ -166,8 +163,8 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
 
     // ---- prologue: Weff hi/lo -------------------------------------------
     // raw weights of a 16-channel chunk: raw[cil][col][27]; weffT[h][tap][col][ci]
-    // (row stride Cin8 + 2 u16 = an odd number of dwords: conflict-free writes)
-    constexpr int WS = Cin8 + 2;
+    // (row stride Cin8 + 8 u16: rows 16-byte aligned for the fragment reads)
+    constexpr int WS = Cin8 + 8;
     unsigned short *weffT = lds + raw_bytes() / 2;
     constexpr int kChunks = (Cin8 + kCiChunk - 1) / kCiChunk;
     constexpr int kVecPerThread = (kCiChunk * kCoGroup * 27 / 8 + kThreads - 1) / kThreads;
@@ -252,16 +249,10 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                 const int cl = 16 * (2 * cp + i) + col;
                 const int kap = 32 * j + 8 * g;
                 const int tap = kap / Cin8, ci0 = kap % Cin8;
-                const unsigned *src = reinterpret_cast<const unsigned *>(
-                    weffT + ((h * 8 + tap) * kCoGroup + cl) * WS + ci0);
-                u16x8 v;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const unsigned u = src[q];
-                    v[2 * q] = (unsigned short)(u & 0xFFFFu);
-                    v[2 * q + 1] = (unsigned short)(u >> 16);
-                }
-                A[i][j][h] = __builtin_bit_cast(bf16x8, v);
+                // one 16-byte read: rows are 16-byte aligned (WS = Cin8 + 8),
+                // and the 80-byte row stride spreads lanes over all banks
+                A[i][j][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(
+                    weffT + ((h * 8 + tap) * kCoGroup + cl) * WS + ci0));
             }
     // folded epilogue ((S/8 + cb)*s1 + b)*s2 = S*alpha + beta[co]
     const float alpha = 0.125f * s1 * s2;
