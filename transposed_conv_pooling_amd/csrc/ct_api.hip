@@ -211,7 +211,9 @@ ct_status ct_convT3d_scale_pool_bias(
             fast = fast && Cin <= 128;
         } else {
             const size_t lb = ct::fused3d_bf16_lds_bytes(Cin, W);
-            fast = fast && Cin <= 32 && W % 8 == 0 && aligned(x, 16) && lb != 0 && lb <= kLdsMax;
+            // (its buffer stores take 32-bit byte offsets within one batch item)
+            fast = fast && Cin <= 32 && W % 8 == 0 && aligned(x, 16) && lb != 0 && lb <= kLdsMax &&
+                   oitem <= kI32Max / 4;
         }
     }
     hipError_t e;

@@ -79,7 +79,10 @@ __host__ __device__ inline int epi_offset(int th, int W, int cs)
     return ((a > b ? a : b) + 15) & ~15;
 }
 
-template <int KSTEPS, int kTH>
+// kWB > 0: the output rows' 16-voxel block count (Wp + 15) / 16 known at
+// compile time (2 for the page's W = 32), so a wave's voxel-block loop has a
+// fixed trip count and every tile issues a fixed number of stores; 0: runtime.
+template <int KSTEPS, int kTH, int kWB>
 __global__ __launch_bounds__(kThreads)
 void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                          const unsigned short *__restrict__ w,
@@ -272,8 +275,11 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     }
 
     // ---- main loop over tiles (n, d, pooled row pair) --------------------
-    const int wblocks = (Wp + 15) / 16;
+    const int wblocks = kWB > 0 ? kWB : (Wp + 15) / 16;
     const int nvb = kTH * wblocks;                // voxel blocks per tile
+    // voxel blocks of this slot per tile (slot, slot+4, ...); a compile-time
+    // count when kWB > 0 and the tile's blocks split evenly over the 4 slots
+    const int nvb_slot = (kWB > 0 && (kTH * kWB) % 4 == 0) ? kTH * kWB / 4 : (nvb - slot + 3) / 4;
     int vb_hh0 = 0, vb_wb0 = slot;               // first voxel block of this slot
     while (vb_wb0 >= wblocks) { vb_wb0 -= wblocks; ++vb_hh0; }
 
@@ -314,19 +320,27 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     }
     __syncthreads();
 
+    // Per tile t: MFMA and stores of tile t, then slab t+1 into the spare
+    // buffer and the loads of slab t+2, then the barrier.  Waiting for slab
+    // t+1's loads (issued before tile t's stores; loads and stores retire in
+    // order) then never waits for tile t's stores, and the wait sees the same
+    // loads-then-stores sequence on the first tile as on every later one.
     for (int t = t_begin; t < t_end; ++t) {
         const int h0 = kTH * hp;
         unsigned short *cur = slab + ((t - t_begin) & 1) * slab_u16;
-        if (t + 1 < t_end) {
-            // the spare buffer's last readers finished before the previous barrier
-            put_all(slab + (((t - t_begin) & 1) ^ 1) * slab_u16, n2, d2, hp2);
-            next_pos(n2, d2, hp2);
-            if (t + 2 < t_end) fetch(n2, d2, hp2);
-        }
 
-        float *ob = out + (int64_t)n * Cout * pplane + ((int64_t)d * Hp + h0) * Wp;
+        // Stores go through a buffer resource over this batch item's output
+        // (word 3 0x00020000: 32-bit data format; the host keeps an item's
+        // output below 2^31 bytes); masked lanes store past the range, which
+        // the hardware drops.  No store sits behind a branch, so every tile
+        // issues the same number of stores, and the next tile's wait for the
+        // slab loads issued before them (loads and stores retire in order)
+        // does not wait for these stores.
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            out + (int64_t)n * Cout * pplane, 0, (int)(Cout * pplane * 4), 0x00020000);
+        const int obase = (d * Hp + h0) * Wp;       // per-item offsets fit in int32 (shim)
         int hh = vb_hh0, wb = vb_wb0;
-        for (int vb = slot; vb < nvb; vb += 4) {
+        for (int it = 0; it < nvb_slot; ++it) {
             const int h = h0 + hh;
             const int wv = wb * 16 + col;
             const bool valid = (wv < Wp) && (h < Hp);
@@ -341,21 +355,26 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                 a0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][1], B, a0l, 0, 0, 0);
                 a1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][1], B, a1l, 0, 0, 0);
             }
-            if (valid) {
-                float *on = ob + hh * Wp + wv;        // per-item offsets fit in int32 (shim)
+            const int opos = obase + hh * Wp + wv;
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int cl = 16 * (2 * cp + i) + 4 * g + r;
-                        if (co0 + cl < Cout) {
-                            const float sum = i ? (a1h[r] + a1l[r]) : (a0h[r] + a0l[r]);
-                            on[(co0 + cl) * (int)pplane] = __builtin_fmaf(sum, alpha, epi[cl]);
-                        }
-                    }
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int cl = 16 * (2 * cp + i) + 4 * g + r;
+                    const float sum = i ? (a1h[r] + a1l[r]) : (a0h[r] + a0l[r]);
+                    const int off = (valid && co0 + cl < Cout) ? ((co0 + cl) * (int)pplane + opos) * 4
+                                                               : 0x7ffffff0;   // past the range
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(__builtin_fmaf(sum, alpha, epi[cl])), orsrc, off, 0, 0);
+                }
             wb += 4;
             while (wb >= wblocks) { wb -= wblocks; ++hh; }
+        }
+        if (t + 1 < t_end) {
+            // the spare buffer's last readers finished before the previous barrier
+            put_all(slab + (((t - t_begin) & 1) ^ 1) * slab_u16, n2, d2, hp2);
+            next_pos(n2, d2, hp2);
+            if (t + 2 < t_end) fetch(n2, d2, hp2);
         }
         __syncthreads();                           // next slab written; this one consumed
         next_pos(n, d, hp);
@@ -410,28 +429,32 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w, const float
     const int tpw = (int)((ntiles + gx - 1) / gx);
     gx = (ntiles + tpw - 1) / tpw;
 
-#define CT_LAUNCH_BF16(KS, TH)                                                                \
+#define CT_LAUNCH_BF16(KS, TH, WB)                                                            \
     do {                                                                                      \
-        hipError_t e = hipFuncSetAttribute((const void *)fused3d_bf16_kernel<KS, TH>,         \
+        hipError_t e = hipFuncSetAttribute((const void *)fused3d_bf16_kernel<KS, TH, WB>,         \
                                            hipFuncAttributeMaxDynamicSharedMemorySize,        \
                                            (int)lds);                                         \
         if (e != hipSuccess) return e;                                                        \
-        hipLaunchKernelGGL((fused3d_bf16_kernel<KS, TH>), dim3((unsigned)gx, gy),             \
+        hipLaunchKernelGGL((fused3d_bf16_kernel<KS, TH, WB>), dim3((unsigned)gx, gy),             \
                            dim3(kThreads), lds, stream, (const unsigned short *)x,            \
                            (const unsigned short *)w, conv_bias, bias, s1, s2, (int)Cin,      \
                            (int)D, (int)H, (int)W, (int)Cout, Dp, Hp, Wp, hchunks,            \
                            (int)ntiles, tpw, out);                                            \
     } while (0)
 
+    if (ksteps == 8 && th == 8 && (Wp + 15) / 16 == 2) {
+        CT_LAUNCH_BF16(8, 8, 2);          // the page's wide workload (Cin 25..32, W 18..32)
+        return hipGetLastError();
+    }
     switch (ksteps * 16 + th) {
-    case 2 * 16 + 8: CT_LAUNCH_BF16(2, 8); break;
-    case 4 * 16 + 8: CT_LAUNCH_BF16(4, 8); break;
-    case 6 * 16 + 8: CT_LAUNCH_BF16(6, 8); break;
-    case 8 * 16 + 8: CT_LAUNCH_BF16(8, 8); break;
-    case 2 * 16 + 2: CT_LAUNCH_BF16(2, 2); break;
-    case 4 * 16 + 2: CT_LAUNCH_BF16(4, 2); break;
-    case 6 * 16 + 2: CT_LAUNCH_BF16(6, 2); break;
-    case 8 * 16 + 2: CT_LAUNCH_BF16(8, 2); break;
+    case 2 * 16 + 8: CT_LAUNCH_BF16(2, 8, 0); break;
+    case 4 * 16 + 8: CT_LAUNCH_BF16(4, 8, 0); break;
+    case 6 * 16 + 8: CT_LAUNCH_BF16(6, 8, 0); break;
+    case 8 * 16 + 8: CT_LAUNCH_BF16(8, 8, 0); break;
+    case 2 * 16 + 2: CT_LAUNCH_BF16(2, 2, 0); break;
+    case 4 * 16 + 2: CT_LAUNCH_BF16(4, 2, 0); break;
+    case 6 * 16 + 2: CT_LAUNCH_BF16(6, 2, 0); break;
+    case 8 * 16 + 2: CT_LAUNCH_BF16(8, 2, 0); break;
     default: return hipErrorInvalidValue;
     }
 #undef CT_LAUNCH_BF16
