@@ -214,6 +214,11 @@ POOL_SMALL = [
     (1, 1, 4, 5, 514),        # two column chunks, element path
     (1, 2, 33, 35, 64),       # several plane chunks and row groups
     (2, 1, 7, 3, 1),
+    (1, 1, 3, 131, 8),        # two row groups: the row above a group comes from memory
+    (1, 1, 2, 140, 264),      # two row groups and two column chunks
+    (1, 1, 5, 258, 520),      # three row groups, three column chunks, ragged last of each
+    (4, 25, 40, 6, 8),        # 100 slices: several plane chunks of more than one plane
+    (3, 1, 1, 4, 4),          # a single input plane
 ]
 
 
