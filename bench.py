@@ -60,7 +60,7 @@ def log(msg):
 # same figures make_ops() computes from the tensors.
 KERNELS = [
     ("fused3d_f32_slab_kernel", "fused3d_f32", "fused3d_f32.hip", 143258752),
-    ("avgpool3d_k3s2p1_kernel", "avgpool3d", "avgpool3d.hip", 9663676416),
+    ("avgpool3d_k3s2p1_", "avgpool3d", "avgpool3d.hip", 9663676416),
     ("convT1d_f32", "convT1d", "convT1d_f32.hip", 1610752000),
     ("fused3d_bf16_kernel", "fused3d_bf16", "fused3d_bf16.hip", 75931904),
     ("convT1d_bf16_kernel", "convT1d_bf16", "convT1d_bf16.hip", 1342296064),
