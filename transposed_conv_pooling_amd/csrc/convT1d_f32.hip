@@ -295,22 +295,30 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[m][b] = b4;
         }
-#pragma unroll 1
-        for (int k = 0; k < K; ++k) {
-            const float *xk = xl - DIL * k;
-            const float *ak = al + k * (CIN4 / 4) * 256;
+        // 40 k-steps fully unrolled, fragments double-buffered in registers:
+        // step s+1's LDS reads are issued before step s's MFMAs (the
+        // scheduling barriers keep that order), so the MFMAs never wait on
+        // a read issued just before them
+        constexpr int kSteps = K * (CIN4 / 4);
+        v4f_ fa[2];
+        float fb[2][NB];
+        auto ldf = [&](int s, int buf) {
+            const int k = s / (CIN4 / 4), c = s % (CIN4 / 4);
+            fa[buf] = *reinterpret_cast<const v4f_ *>(al + s * 256);
 #pragma unroll
-            for (int c = 0; c < CIN4 / 4; ++c) {
-                const v4f_ av = *reinterpret_cast<const v4f_ *>(ak + c * 256);
-                float bvv[NB];
+            for (int b = 0; b < NB; ++b) fb[buf][b] = xl[-DIL * k + 4 * c * G::kStr + 16 * b];
+        };
+        ldf(0, 0);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) bvv[b] = xk[4 * c * G::kStr + 16 * b];
+        for (int s = 0; s < kSteps; ++s) {
+            if (s + 1 < kSteps) ldf(s + 1, (s + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int b = 0; b < NB; ++b)
-                        acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(bvv[b], av[m], acc[m][b], 0, 0, 0);
-            }
+                for (int b = 0; b < NB; ++b)
+                    acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fb[s & 1][b], fa[s & 1][m], acc[m][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // 16-byte buffer stores over this batch item's output (word 3
