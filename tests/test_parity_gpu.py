@@ -160,6 +160,12 @@ FUSED_BF16 = [
     (10, 8, 64, 9, 23, 24),
     (20, 8, 96, 4, 10, 40),
     (12, 32, 64, 6, 18, 16),
+    # one 64-channel group, weights read straight into registers: input
+    # channels padded to 32, 8 (one couple per thread) and 24 (some threads
+    # with a second couple)
+    (3, 25, 64, 3, 4, 32),
+    (2, 3, 64, 2, 3, 8),
+    (2, 20, 64, 3, 6, 16),
 ]
 
 

@@ -162,40 +162,89 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
         for (int k = 0; k < 8; ++k)
             dst[k * (CS / 2)] = (unsigned)v0[k] | ((unsigned)v1[k] << 16);
     };
-    if (t_begin < t_end) fetch(n, d, hp);
-
     // ---- prologue: Weff hi/lo -------------------------------------------
-    // raw weights of a 16-channel chunk: raw[cil][col][27]; weffT[h][tap][col][ci]
-    // (row stride Cin8 + 8 u16: rows 16-byte aligned for the fragment reads)
+    // weffT[h][tap][col][ci] (row stride Cin8 + 8 u16: rows 16-byte aligned
+    // for the fragment reads)
     constexpr int WS = Cin8 + 8;
     unsigned short *weffT = lds + raw_bytes() / 2;
-    constexpr int kChunks = (Cin8 + kCiChunk - 1) / kCiChunk;
-    constexpr int kVecPerThread = (kCiChunk * kCoGroup * 27 / 8 + kThreads - 1) / kThreads;
-    const bool vec_w = (Cout == kCoGroup) && (Cin % kCiChunk == 0) && ((((uintptr_t)w) & 15) == 0);
-    u16x8 wreg[kChunks][kVecPerThread];
-    if (vec_w) {              // both chunks' loads in flight at once
+    // The 27 weights of pair (ci, col) -> Weff for the 8 input taps, split
+    // into bf16 hi and lo.  Per axis, input offset 0 takes kernel taps {1,2}
+    // and offset 1 takes tap {0}; the 3-D sum is done axis by axis.
+    auto emit = [&](const float (&wv)[27], int cl, int ci) {
+        float s1w[9][2];
 #pragma unroll
-        for (int ch = 0; ch < kChunks; ++ch)
+        for (int r = 0; r < 9; ++r) {
+            s1w[r][0] = wv[r * 3 + 1] + wv[r * 3 + 2];
+            s1w[r][1] = wv[r * 3 + 0];
+        }
+        float s2w[3][2][2];
 #pragma unroll
-            for (int i = 0; i < kVecPerThread; ++i) {
-                const int e = tid + i * kThreads;
-                if (e < kCiChunk * kCoGroup * 27 / 8 && (ch + 1) * kCiChunk <= Cin)
-                    wreg[ch][i] = reinterpret_cast<const u16x8 *>(w + (int64_t)ch * kCiChunk * kCoGroup * 27)[e];
+        for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                s2w[kd][0][c] = s1w[kd * 3 + 1][c] + s1w[kd * 3 + 2][c];
+                s2w[kd][1][c] = s1w[kd * 3 + 0][c];
             }
+#pragma unroll
+        for (int tap = 0; tap < 8; ++tap) {
+            const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
+            const float we = a ? s2w[0][b][c] : (s2w[1][b][c] + s2w[2][b][c]);
+            const unsigned short hi = f32_to_bf16(we);
+            weffT[((0 * 8 + tap) * kCoGroup + cl) * WS + ci] = hi;
+            weffT[((1 * 8 + tap) * kCoGroup + cl) * WS + ci] = f32_to_bf16(we - bf16_to_f32(hi));
+        }
+    };
+    // Direct path (one 64-channel group, 4-byte aligned w): couple q holds the
+    // pairs (ci, 2m) and (ci, 2m+1), q = 32*ci + m, whose 54 weights are the
+    // 27 consecutive dwords q*27 .. q*27+26 of w.  Every thread loads its (at
+    // most two) couples before the first slab's loads are issued, so the
+    // weights return first; the filter is formed straight from registers.
+    constexpr int kCouples = Cin8 * kCoGroup / 2;
+    constexpr int kCouplesPerThread = (kCouples + kThreads - 1) / kThreads;
+    const bool direct_w = (Cout == kCoGroup) && ((((uintptr_t)w) & 3) == 0);
+    unsigned wd[kCouplesPerThread][27];
+    if (direct_w) {
+        const unsigned *w32 = reinterpret_cast<const unsigned *>(w);
+#pragma unroll
+        for (int j = 0; j < kCouplesPerThread; ++j) {
+            const int q = tid + j * kThreads;
+            // unconditional loads (couples past Cin read couple 0, zeroed below)
+            const unsigned *src = w32 + ((q < kCouples && (q >> 5) < Cin) ? q * 27 : 0);
+#pragma unroll
+            for (int k = 0; k < 27; ++k) wd[j][k] = src[k];
+        }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (t_begin < t_end) fetch(n, d, hp);
+
+    if (direct_w) {
 #pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-        const int c0 = ch * kCiChunk;
-        const int nci = min(kCiChunk, Cin - c0);
-        __syncthreads();                               // previous chunk's raw consumed
-        if (vec_w) {
+        for (int j = 0; j < kCouplesPerThread; ++j) {
+            const int q = tid + j * kThreads;
+            if (q < kCouples) {
+                const int ci = q >> 5, cl = 2 * (q & 31);
+                const bool ok = ci < Cin;
 #pragma unroll
-            for (int i = 0; i < kVecPerThread; ++i) {
-                const int e = tid + i * kThreads;
-                if (e < kCiChunk * kCoGroup * 27 / 8)
-                    reinterpret_cast<u16x8 *>(raw)[e] = wreg[ch][i];
+                for (int half = 0; half < 2; ++half) {
+                    float wv[27];
+#pragma unroll
+                    for (int k = 0; k < 27; ++k) {
+                        const int e = 27 * half + k;   // u16 element of the couple
+                        const unsigned u = (wd[j][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                        wv[k] = ok ? bf16_to_f32((unsigned short)u) : 0.0f;
+                    }
+                    emit(wv, cl + half, ci);
+                }
             }
-        } else {
+        }
+    } else {
+        // general path: raw weights of a 16-channel chunk staged in LDS as
+        // raw[cil][col][27], zero beyond Cin and Cout
+        constexpr int kChunks = (Cin8 + kCiChunk - 1) / kCiChunk;
+        for (int ch = 0; ch < kChunks; ++ch) {
+            const int c0 = ch * kCiChunk;
+            const int nci = min(kCiChunk, Cin - c0);
+            __syncthreads();                               // previous chunk's raw consumed
             const int run = ncog * 27;
             for (int cil = 0; cil < kCiChunk; ++cil) {
                 unsigned short *rd = raw + cil * kCoGroup * 27;
@@ -204,38 +253,16 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                 for (int e = tid; e < kCoGroup * 27; e += kThreads)
                     rd[e] = e < n_in ? w[base + e] : (unsigned short)0;
             }
-        }
-        __syncthreads();
-        // pairs (cil, col), output channel fastest: raw reads 27 u16 apart
-        for (int pr = tid; pr < kCiChunk * kCoGroup; pr += kThreads) {
-            const int cil = pr / kCoGroup, cl = pr % kCoGroup;
-            const int ci = c0 + cil;
-            if (ci >= Cin8) continue;
-            float wv[27];
+            __syncthreads();
+            // pairs (cil, col), output channel fastest: raw reads 27 u16 apart
+            for (int pr = tid; pr < kCiChunk * kCoGroup; pr += kThreads) {
+                const int cil = pr / kCoGroup, cl = pr % kCoGroup;
+                const int ci = c0 + cil;
+                if (ci >= Cin8) continue;
+                float wv[27];
 #pragma unroll
-            for (int k = 0; k < 27; ++k) wv[k] = bf16_to_f32(raw[pr * 27 + k]);
-            // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
-            float s1w[9][2];
-#pragma unroll
-            for (int r = 0; r < 9; ++r) {
-                s1w[r][0] = wv[r * 3 + 1] + wv[r * 3 + 2];
-                s1w[r][1] = wv[r * 3 + 0];
-            }
-            float s2w[3][2][2];
-#pragma unroll
-            for (int kd = 0; kd < 3; ++kd)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    s2w[kd][0][c] = s1w[kd * 3 + 1][c] + s1w[kd * 3 + 2][c];
-                    s2w[kd][1][c] = s1w[kd * 3 + 0][c];
-                }
-#pragma unroll
-            for (int tap = 0; tap < 8; ++tap) {
-                const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
-                const float we = a ? s2w[0][b][c] : (s2w[1][b][c] + s2w[2][b][c]);
-                const unsigned short hi = f32_to_bf16(we);
-                weffT[((0 * 8 + tap) * kCoGroup + cl) * WS + ci] = hi;
-                weffT[((1 * 8 + tap) * kCoGroup + cl) * WS + ci] = f32_to_bf16(we - bf16_to_f32(hi));
+                for (int k = 0; k < 27; ++k) wv[k] = bf16_to_f32(raw[pr * 27 + k]);
+                emit(wv, cl, ci);
             }
         }
     }
