@@ -166,6 +166,9 @@ FUSED_BF16 = [
     (3, 25, 64, 3, 4, 32),
     (2, 3, 64, 2, 3, 8),
     (2, 20, 64, 3, 6, 16),
+    # direct weights, but the slab is larger than the raw-weight region, so
+    # the first slab is staged after the fragments are loaded
+    (1, 32, 64, 2, 3, 128),
 ]
 
 

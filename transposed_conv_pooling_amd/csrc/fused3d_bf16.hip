@@ -162,6 +162,34 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
         for (int k = 0; k < 8; ++k)
             dst[k * (CS / 2)] = (unsigned)v0[k] | ((unsigned)v1[k] << 16);
     };
+    // slab staging: all pieces of a tile into one slab buffer
+    const int slab_u16 = slab_bytes(kTH, W, CS) / 2;
+    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto put_all = [&](unsigned short *buf, int n_, int d_, int hp_) {
+        const int h0 = kTH * hp_;
+#pragma unroll
+        for (int i = 0; i < kPrefetch; ++i)
+            if (prow[i] < (1 << 30))
+                put(buf, dst_off[i], (pok[i] & 2) ? pre0[i] : z8, (pok[i] & 4) ? pre1[i] : z8);
+        for (int q = tid + kPrefetch * kThreads; q < npieces; q += kThreads) {
+            const int cpair = q % (Cin8 / 2);
+            int tt = q / (Cin8 / 2);
+            const int w8 = tt % W8;
+            tt /= W8;
+            const int row = tt % kRows, a = tt / kRows;
+            const int ci = 2 * cpair;
+            const unsigned short *src = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW +
+                                        (int64_t)h0 * W + ci * DHW + a * HW + row * W + 8 * w8;
+            const bool rok = h0 + row < H;
+            const u16x8 v0 = (rok && ci < Cin) ? *reinterpret_cast<const u16x8 *>(src) : z8;
+            const u16x8 v1 = (rok && ci + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(src + DHW) : z8;
+            put(buf, ((a * kRows + row) * W + 8 * w8) * CS + ci, v0, v1);
+        }
+    };
+    auto next_pos = [&](int &n_, int &d_, int &hp_) {
+        if (++hp_ == hpairs) { hp_ = 0; if (++d_ == Dp) { d_ = 0; ++n_; } }
+    };
+
     // ---- prologue: Weff hi/lo -------------------------------------------
     // weffT[h][tap][col][ci] (row stride Cin8 + 8 u16: rows 16-byte aligned
     // for the fragment reads)
@@ -216,6 +244,8 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     }
     __builtin_amdgcn_sched_barrier(0);
     if (t_begin < t_end) fetch(n, d, hp);
+    int n2 = n, d2 = d, hp2 = hp;   // the next tile to stage
+    const bool early_slab = direct_w && slab_bytes(kTH, W, CS) <= raw_bytes();
 
     if (direct_w) {
 #pragma unroll
@@ -236,6 +266,13 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                     emit(wv, cl + half, ci);
                 }
             }
+        }
+        if (early_slab && t_begin < t_end) {
+            // slab buffer 0 lies below the filter table here: stage the first
+            // tile now and issue the second tile's loads before the fragments
+            put_all(slab, n, d, hp);
+            next_pos(n2, d2, hp2);
+            if (t_begin + 1 < t_end) fetch(n2, d2, hp2);
         }
     } else {
         // general path: raw weights of a 16-channel chunk staged in LDS as
@@ -310,42 +347,17 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     int vb_hh0 = 0, vb_wb0 = slot;               // first voxel block of this slot
     while (vb_wb0 >= wblocks) { vb_wb0 -= wblocks; ++vb_hh0; }
 
-    // first tile's slab into buffer 0 (its loads were issued before the
-    // prologue), the second tile's loads into registers
-    const int slab_u16 = slab_bytes(kTH, W, CS) / 2;
-    const u16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto put_all = [&](unsigned short *buf, int n_, int d_, int hp_) {
-        const int h0 = kTH * hp_;
-#pragma unroll
-        for (int i = 0; i < kPrefetch; ++i)
-            if (prow[i] < (1 << 30))
-                put(buf, dst_off[i], (pok[i] & 2) ? pre0[i] : z8, (pok[i] & 4) ? pre1[i] : z8);
-        for (int q = tid + kPrefetch * kThreads; q < npieces; q += kThreads) {
-            const int cpair = q % (Cin8 / 2);
-            int tt = q / (Cin8 / 2);
-            const int w8 = tt % W8;
-            tt /= W8;
-            const int row = tt % kRows, a = tt / kRows;
-            const int ci = 2 * cpair;
-            const unsigned short *src = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW +
-                                        (int64_t)h0 * W + ci * DHW + a * HW + row * W + 8 * w8;
-            const bool rok = h0 + row < H;
-            const u16x8 v0 = (rok && ci < Cin) ? *reinterpret_cast<const u16x8 *>(src) : z8;
-            const u16x8 v1 = (rok && ci + 1 < Cin) ? *reinterpret_cast<const u16x8 *>(src + DHW) : z8;
-            put(buf, ((a * kRows + row) * W + 8 * w8) * CS + ci, v0, v1);
-        }
-    };
-    auto next_pos = [&](int &n_, int &d_, int &hp_) {
-        if (++hp_ == hpairs) { hp_ = 0; if (++d_ == Dp) { d_ = 0; ++n_; } }
-    };
-    int n2 = n, d2 = d, hp2 = hp;
     __syncthreads();              // every wave holds its fragments: the slabs may reuse that LDS
-    if (t_begin < t_end) {
-        put_all(slab, n, d, hp);
-        next_pos(n2, d2, hp2);
-        if (t_begin + 1 < t_end) fetch(n2, d2, hp2);
+    if (!early_slab) {
+        // first tile's slab into buffer 0 (its loads were issued before the
+        // prologue), the second tile's loads into registers
+        if (t_begin < t_end) {
+            put_all(slab, n, d, hp);
+            next_pos(n2, d2, hp2);
+            if (t_begin + 1 < t_end) fetch(n2, d2, hp2);
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // Per tile t: MFMA and stores of tile t, then slab t+1 into the spare
     // buffer and the loads of slab t+2, then the barrier.  Waiting for slab
