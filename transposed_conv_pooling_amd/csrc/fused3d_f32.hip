@@ -264,9 +264,10 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // partial lines in a workgroup are written with plain stores (for L2 to
 // merge with the neighbour's part).  Staging is double-buffered as well:
 // one barrier per task separates a task's compute from its store phase.
-constexpr int kSlabPrefetch = 5;   // slab pieces each loader lane keeps in flight
+constexpr int kSlabPrefetch = 3;   // slab pieces each loader lane keeps in flight (more
+                                   // would cost the registers of a third workgroup per CU)
 constexpr int kLine = 32;          // floats per 128-byte line
-// 4 compute waves, 2 loader waves, 2 store waves.  vmcnt counts a wave's
+// 4 compute waves, 3 loader waves, 4 store waves.  vmcnt counts a wave's
 // loads and stores together and retires them in order, so a wave that both
 // stores and prefetches would wait for its earlier stores before each slab;
 // here only the loader waves load and only the store waves store.
@@ -532,10 +533,11 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             // staging row of channel co starts at its line base: the task's
             // first output sits at its float index within its 128-byte line
             float *srow = stg + col * STR + (int)(((uintptr_t)(ob + co_off) >> 2) & (kLine - 1)) + 4 * kq;
-            // each wave takes rows hh = wave, wave + 4, ... two at a time (hh
-            // and hh + 4); a row's w-blocks go in pairs, each block's K range
-            // split over two accumulators: eight independent MFMA chains in
-            // flight, with all their LDS reads issued first
+            // each wave takes rows hh = wave, wave + 4, ... one at a time; a
+            // row's w-blocks go in pairs, each block's K range split over two
+            // accumulators: four independent MFMA chains in flight, with all
+            // their LDS reads issued first.  (One row, not two, per pass keeps
+            // every role under 56 VGPRs, so three workgroups fit on a CU.)
             // (block voxels 4kq+r at w = wv0 + r of the block start wv0)
             auto stage_block = [&](int hh, int wv0, const v4f &p, const v4f &q) {
                 float *dst = srow + hh * Wp + wv0;
@@ -543,41 +545,27 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
                 for (int r = 0; r < 4; ++r)
                     if (co_ok && wv0 + 4 * kq + r < Wp) dst[r] = __builtin_fmaf(p[r] + q[r], alpha, beta);
             };
-            for (int hh = wave; hh < rows; hh += 2 * kWaves) {
-                const int hh2 = hh + kWaves;
-                const bool two = hh2 < rows;           // wave-uniform
-                const float *srowA = cur + hh * W, *srowB = cur + (two ? hh2 : hh) * W;
+            for (int hh = wave; hh < rows; hh += kWaves) {
+                const float *srowA = cur + hh * W;
                 for (int wb = 0; wb < wblocks; wb += 2) {
                     const int wv0 = wb * 16 + col, wv1 = wv0 + 16;
                     const int wc0 = min(wv0, Wp - 1), wc1 = min(wv1, Wp - 1);
-                    float a0[KS], a1[KS], b0[KS], b1[KS];
+                    float a0[KS], a1[KS];
 #pragma unroll
                     for (int j = 0; j < KS; ++j) {
                         a0[j] = srowA[wc0 + soff[j]];
                         a1[j] = srowA[wc1 + soff[j]];
-                        b0[j] = srowB[wc0 + soff[j]];
-                        b1[j] = srowB[wc1 + soff[j]];
                     }
                     v4f pA0 = {0.0f, 0.0f, 0.0f, 0.0f}, qA0 = pA0, pA1 = pA0, qA1 = pA0;
-                    v4f pB0 = pA0, qB0 = pA0, pB1 = pA0, qB1 = pA0;
 #pragma unroll
                     for (int j = 0; j < KS; j += 2) {
                         pA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j], a[j], pA0, 0, 0, 0);
                         pA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j], a[j], pA1, 0, 0, 0);
-                        pB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(b0[j], a[j], pB0, 0, 0, 0);
-                        pB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b1[j], a[j], pB1, 0, 0, 0);
                         qA0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[j + 1], a[j + 1], qA0, 0, 0, 0);
                         qA1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[j + 1], a[j + 1], qA1, 0, 0, 0);
-                        qB0 = __builtin_amdgcn_mfma_f32_16x16x4f32(b0[j + 1], a[j + 1], qB0, 0, 0, 0);
-                        qB1 = __builtin_amdgcn_mfma_f32_16x16x4f32(b1[j + 1], a[j + 1], qB1, 0, 0, 0);
                     }
-                    const bool w1 = wb + 1 < wblocks;     // second block exists
                     stage_block(hh, wb * 16, pA0, qA0);
-                    if (w1) stage_block(hh, wb * 16 + 16, pA1, qA1);
-                    if (two) {
-                        stage_block(hh2, wb * 16, pB0, qB0);
-                        if (w1) stage_block(hh2, wb * 16 + 16, pB1, qB1);
-                    }
+                    if (wb + 1 < wblocks) stage_block(hh, wb * 16 + 16, pA1, qA1);
                 }
             }
             next(n, d, hc);
