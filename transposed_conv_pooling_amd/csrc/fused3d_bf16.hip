@@ -119,9 +119,11 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     int hp, d, n;
     {
         int t = t_begin;
-        hp = uniform(t % hpairs); t /= hpairs;
-        d = uniform(t % Dp);
-        n = uniform(t / Dp);
+        // tile order (n, row chunk, d), d fastest: a workgroup's consecutive
+        // tiles share an input plane, whose second read then hits its L2
+        d = uniform(t % Dp); t /= Dp;
+        hp = uniform(t % hpairs);
+        n = uniform(t / hpairs);
     }
     // tile-invariant staging plan: piece q = ((a*kRows + row)*W8 + w8)*(Cin8/2) + cpair
     // covers channels 2*cpair, 2*cpair+1 at x[.., d+a, h0+row, 8*w8 .. 8*w8+7]
@@ -187,7 +189,7 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
         }
     };
     auto next_pos = [&](int &n_, int &d_, int &hp_) {
-        if (++hp_ == hpairs) { hp_ = 0; if (++d_ == Dp) { d_ = 0; ++n_; } }
+        if (++d_ == Dp) { d_ = 0; if (++hp_ == hpairs) { hp_ = 0; ++n_; } }
     };
 
     // ---- prologue: Weff hi/lo -------------------------------------------
