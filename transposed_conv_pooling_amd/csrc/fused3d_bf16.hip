@@ -24,20 +24,22 @@
 // 8 kappas are 8 consecutive channels at one tap: with the input slab held
 // channels-last in LDS that is one 16-byte ds_read_b128.
 //  * Workgroup = 8 waves, persistent, one 64-channel output group
-//    (blockIdx.y).  Prologue: the raw weights come in with coalesced 16-byte
-//    loads (all chunks in flight at once) and are staged in LDS; every
-//    thread forms Weff and its hi/lo split for two (ci, co) pairs into a
-//    [half][tap][co][ci] table, from which each wave loads its fragments
-//    (2 output-channel blocks x all k-steps x hi/lo) into registers for the
-//    whole kernel.
+//    (blockIdx.y).  Prologue: every thread forms Weff and its hi/lo split
+//    for its (ci, co) pairs into a [half][tap][co][ci] table, from which each
+//    wave loads its fragments (2 output-channel blocks x all k-steps x
+//    hi/lo) into registers for the whole kernel.  With one 64-channel group
+//    a thread reads its pairs' 54 weights straight into registers, before
+//    the first slab's loads; otherwise the raw weights are staged in LDS in
+//    16-channel chunks.
 //  * Tile = (n, d, 8 pooled rows): the input slab x[n, :, d..d+1, h0..h0+8, :]
 //    is transposed to [plane][row][w][ci] in a double-buffered LDS slab.  A
 //    tile's loads are issued two tiles ahead into registers and written to
 //    the spare buffer one tile ahead; one barrier per tile.
 //  * Wave = (voxel-block slot s = w%4, channel pair p = w/4): each B read
 //    feeds 4 MFMAs (2 channel blocks x hi/lo).
-//  * Each workgroup walks a contiguous range of tiles, so neighbouring tiles
-//    (which share input rows) run on the same XCD and hit its L2.
+//  * Each workgroup walks a contiguous range of tiles in (n, row chunk, d)
+//    order, so consecutive tiles share an input plane and its second read
+//    hits the same XCD's L2.
 #include "ct_internal.h"
 
 namespace ct {
