@@ -192,6 +192,10 @@ void avgpool3d_k3s2p1_vec_kernel(const float *__restrict__ x, float *__restrict_
     put_rows<kWide>(A, T[0], wave, lane);
     __builtin_amdgcn_sched_barrier(0);
     issue_plane<kWide>(A, xs, 2 * d0 + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+    // (an empty asm with a memory clobber after each issue keeps the loads
+    // ahead of the barrier in get_vsums; without it the compiler sinks them
+    // past the barrier and the LDS reads, delaying the next plane)
+    asm volatile("" ::: "memory");
     get_vsums<kWide>(T[0], xs, 2 * d0 - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
     // stores past the range, so that the memory-counter state entering the
     // loop matches the one at its back-edge
@@ -207,12 +211,14 @@ void avgpool3d_k3s2p1_vec_kernel(const float *__restrict__ x, float *__restrict_
         put_rows<kWide>(B, T[1], wave, lane);
         __builtin_amdgcn_sched_barrier(0);
         issue_plane<kWide>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        asm volatile("" ::: "memory");
         get_vsums<kWide>(T[1], xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
 #pragma unroll
         for (int i = 0; i < kTH; ++i) acc[i] = carry[i] + v[i];
         put_rows<kWide>(A, T[0], wave, lane);
         __builtin_amdgcn_sched_barrier(0);
         issue_plane<kWide>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        asm volatile("" ::: "memory");
         get_vsums<kWide>(T[0], xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
         const __amdgpu_buffer_rsrc_t ro = plane_rsrc(os + (int64_t)d * Ho * Wo, true, obytes);
 #pragma unroll
