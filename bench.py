@@ -58,6 +58,8 @@ def log(msg):
 # Kernels as rocprofv3 names them -> (op or kernel key, source file,
 # algorithmic bytes of one launch at the bench workload).  The bytes are the
 # same figures make_ops() computes from the tensors.
+ORACLE_MIN_S = 2.5          # seconds of oracle time per op in the CPU baseline
+
 KERNELS = [
     ("fused3d_f32_slab_kernel", "fused3d_f32", "fused3d_f32.hip", 143258752),
     ("avgpool3d_k3s2p1_", "avgpool3d", "avgpool3d.hip", 9663676416),
@@ -428,11 +430,17 @@ def main():
     if not args.no_cpu_baseline and all(o.oracle_sample for o in ops):
         import oracle
         log("cpu baseline: oracle on a bounded sample of each workload")
+        # each op's sample is repeated until it has run for ORACLE_MIN_S, so
+        # the baseline rests on ~10 s of CPU work in all
         est_s, samples = 0.0, []
         for op in ops:
-            secs, frac, what = op.oracle_sample()
-            est_s += secs / frac
-            samples.append(f"{op.name}: {what} in {secs:.2f} s")
+            total, reps = 0.0, 0
+            while total < ORACLE_MIN_S:
+                secs, frac, what = op.oracle_sample()
+                total += secs
+                reps += 1
+            est_s += total / reps / frac
+            samples.append(f"{op.name}: {what}, {reps} passes in {total:.1f} s")
         cpu = {"value": round(total_bytes / est_s / 1e9, 4), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": "; ".join(samples) + f"; full step extrapolated to {est_s:.1f} s"}
