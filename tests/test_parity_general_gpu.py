@@ -227,6 +227,7 @@ CONV1D_GENERAL = [
     (1, 32, 70, 520, 5, 1, 0, 3, 0, True, "bf16"),    # two output-channel groups, ragged
     (1, 32, 16, 8, 5, 1, 0, 3, 0, True, "bf16"),      # shortest input
     (3, 32, 64, 1024, 5, 1, 0, 3, 0, True, "bf16"),   # several tiles per item
+    (8, 32, 64, 40000, 5, 1, 0, 3, 0, True, "bf16"),  # more tiles than workgroups, ranges across items
 ]
 
 
