@@ -299,7 +299,7 @@ def summarize_trace(path):
               f"{100 * sum(v) / total:.2f}% | {gbs} |")
 
 
-def summarize_counters(fetch_path, write_path):
+def summarize_counters(fetch_path, write_path, dst=None):
     """HBM bytes per launch from two `rocprofv3 --pmc` runs (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
     for the bench's 1 GiB device copy; writes profiles/traffic.json (with a
@@ -337,7 +337,7 @@ def summarize_counters(fetch_path, write_path):
                     "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}
         print(f"| {key} | {fetch[(key, src, alg)]:.0f} | {write[(key, src, alg)]:.0f} | {rb:.4g} | "
               f"{wb:.4g} | {rb + wb:.4g} | {alg:.4g} | {(rb + wb) / alg:.3f} |")
-    dst = os.path.join(ROOT, "profiles", "traffic.json")
+    dst = dst or os.path.join(ROOT, "profiles", "traffic.json")
     json.dump(out, open(dst, "w"), indent=1)
     print(f"\nwrote {os.path.relpath(dst, ROOT)}")
 
