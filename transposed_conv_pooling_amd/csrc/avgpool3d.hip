@@ -40,8 +40,9 @@
 //  * a workgroup walks as many output planes as keeps two workgroups per CU,
 //    so that for the large case every slice is read by one workgroup from
 //    its first plane to its last and no plane is read twice.
-// Other inputs (ragged W, misaligned x) take the element kernel: one wave per
-// 4 output rows, element-wise masked loads, same arithmetic.
+// Other inputs (ragged W, misaligned x or out, planes of 2^30 bytes or more)
+// take the element kernel: one wave per 4 output rows, element-wise masked
+// loads, same arithmetic.
 #include "ct_internal.h"
 
 namespace ct {
