@@ -266,6 +266,29 @@ def test_pool_constant_input_border_values(dev):
     assert abs(o[-1, -1, -1] - 1.0) < 1e-6
 
 
+def test_pool_plane_of_2_30_bytes_takes_element_path(dev):
+    """A [16384, 16384] plane (2^30 bytes) is past the vector kernel's plane
+    limit and runs on the element kernel; checked on bands at the top and
+    bottom edges, where the oracle run on the band alone is exact (bands start
+    on an even input row; the bottom band's first output row, whose window
+    reaches above the band, is skipped)."""
+    H = W = 16384
+    log(f"pool (1, 1, 1, {H}, {W}) element path")
+    x = synth.normal(2077, 0, (1, 1, 1, H, W))
+    xg = torch.from_numpy(x).to(dev)
+    out = nan_like((1, 1, 1, H // 2, W // 2), dev)
+    ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
+    torch.cuda.synchronize()
+    del xg
+    top = oracle.avgpool3d(x[..., :34, :], 3, 2, 1, True)
+    assert_close(out[..., :16, :].cpu().numpy(), top[..., :16, :], F32_TOL, "pool 2^30-byte plane, top band")
+    s = H - 34
+    bottom = oracle.avgpool3d(x[..., s:, :], 3, 2, 1, True)
+    assert_close(out[..., s // 2 + 1:, :].cpu().numpy(), bottom[..., 1:, :], F32_TOL,
+                 "pool 2^30-byte plane, bottom band")
+    assert bool(torch.isfinite(out).all())
+
+
 def test_pool_c3_full_sampled(dev):
     """Full-size [16,32,128,128,256] (2^31 elements); 6 whole (n, c) slices
     recomputed by the oracle, plus global finiteness."""
