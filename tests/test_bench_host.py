@@ -93,3 +93,11 @@ def test_traffic_reported_only_for_the_measured_source(tmp_path, monkeypatch):
     assert bench.measured_traffic("avgpool3d") == 123
     (src_dir / "avgpool3d.hip").write_text("kernel v2\n")      # source changed since
     assert bench.measured_traffic("avgpool3d") is None
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "exactly one GPU" in r.stdout + r.stderr
