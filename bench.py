@@ -48,6 +48,7 @@ OP_SOURCES = {
     "fused3d_bf16": "fused3d_bf16.hip",
     "unfused3d_f32": "generic.hip",
     "convT1d_bf16": "convT1d_bf16.hip",
+    "avgpool3d_bf16": "avgpool3d.hip",
 }
 
 
@@ -62,6 +63,9 @@ ORACLE_MIN_S = 2.5          # seconds of oracle time per op in the CPU baseline
 
 KERNELS = [
     ("fused3d_f32_slab_kernel", "fused3d_f32", "fused3d_f32.hip", 143258752),
+    # bf16 pool kernels first: the fp32 ones share the name prefix
+    ("avgpool3d_k3s2p1_vec_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
+    ("avgpool3d_k3s2p1_elem_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
     ("avgpool3d_k3s2p1_", "avgpool3d", "avgpool3d.hip", 9663676416),
     ("convT1d_f32", "convT1d", "convT1d_f32.hip", 1610752000),
     ("fused3d_bf16_kernel", "fused3d_bf16", "fused3d_bf16.hip", 75931904),
@@ -105,6 +109,15 @@ class Op:
         self.bound, self.peak = bound, peak
         self.inputs = inputs
         self.oracle_sample = oracle_sample    # () -> (seconds, fraction of the op)
+        # arithmetic type of the products: the bf16 contractions multiply bf16
+        # operands on the matrix cores (fp32 accumulation); every other op,
+        # bf16 pooling included, computes in fp32
+        self.arith = "bf16" if name in ("fused3d_bf16", "convT1d_bf16") else "f32"
+
+
+def bf16_label(wl):
+    """Workload label for the bf16-data variant of an fp32 workload."""
+    return wl.description.rsplit(" ", 1)[0] + " bf16"
 
 
 def make_ops(names, dev):
@@ -224,7 +237,29 @@ def make_ops(names, dev):
 
         flops = 2 * 32 * 32 * 131072 * 5 * 64
         ops.append(Op("convT1d_bf16", run, nbytes(x, w, out), flops, "hbm", HBM_PEAK_GBS,
-                      [wl.description + " in bf16"], sample))
+                      [bf16_label(wl)], sample))
+
+    if "avgpool3d_bf16" in names:
+        # the large pooling shape with bf16 data (bf16 means of fp32 sums)
+        wl = synth.WORKLOADS["c3"]
+        log(f"inputs: {wl.description} in bf16 (8.6 GB host generation)")
+        xb = synth.to_bf16_bits(synth.normal(wl.seed, synth.STREAM_X, wl.x_shape))
+        x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        out = torch.empty((16, 32, 64, 64, 128), dtype=torch.bfloat16, device=dev)
+
+        def run(x=x, out=out):
+            ct.ct_avgpool3d(x, 3, 2, 1, True, out=out)
+
+        def sample(xb=xb):
+            import oracle
+            k = 128
+            xf = synth.bf16_bits_to_f32(xb.reshape(512, 128, 128, 256)[:k])
+            t0 = time.perf_counter()
+            oracle.avgpool3d(xf, 3, 2, 1, True)
+            return time.perf_counter() - t0, k / 512.0, f"{k} of 512 (n,c) slices"
+
+        ops.append(Op("avgpool3d_bf16", run, nbytes(x, out), 27 * out.numel(), "hbm",
+                      HBM_PEAK_GBS, [bf16_label(wl)], sample))
 
     if "unfused3d_f32" in names:
         # The chain without fusion: ConvTranspose3d writes the full pre-pool
@@ -458,7 +493,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "+".join(dict.fromkeys(o.arith for o in ops)),
         "data": "synthetic (seeded Philox N(0,1) activations and biases, U(+-1/sqrt(fan)) weights)",
         "config": {"workload": "one full-size pass of " + ", ".join(o.name for o in ops),
                    "ops": {o.name: o.inputs[0] for o in ops}},

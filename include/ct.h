@@ -174,6 +174,25 @@ CT_API ct_status ct_avgpool3d(const float *x,
                        float *out, void *stream);
 
 /*
+ * The same AvgPool3d on bf16 data ([p46]'s operation with the tensor in
+ * bf16, as PyTorch's AvgPool3d runs on a bf16 tensor): every tap is widened
+ * exactly to fp32, the window sum and the division are fp32, and each mean is
+ * rounded to the nearest bf16 (ties to even; NaN stays NaN).
+ *
+ *   x    [N, C, D, H, W] bf16 bit patterns (uint16_t), 2-byte aligned
+ *   out  [N, C, Do, Ho, Wo] bf16 bit patterns, sizes as for ct_avgpool3d
+ *
+ * Geometry, limits, ownership and errors as for ct_avgpool3d (sizes in
+ * bf16 elements).  k = 3, stride 2, pad 1 with count_include_pad = 1 runs on
+ * the same separable streaming kernels (the vector one when W % 4 == 0, x is
+ * 8-byte and out 4-byte aligned); anything else on the general gather kernel.
+ */
+CT_API ct_status ct_avgpool3d_bf16(const uint16_t *x,
+                       int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                       int k, int stride, int pad, int count_include_pad,
+                       uint16_t *out, void *stream);
+
+/*
  * Transposed 1D convolution ([p74], gather form derived on the page):
  *   y[n,co,o] = sum_ci sum_{k<K} x[n,ci,(o + pad - dilation*k)/stride]
  *               * w[ci,co,k]  (+ bias[co])

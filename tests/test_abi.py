@@ -111,15 +111,15 @@ def test_fused_rejects(kw, status):
     assert ct.ct_last_error() != ""
 
 
-def pool(**kw):
+def pool(fn="ct_avgpool3d", **kw):
     a = dict(x=FAKE, N=16, C=32, D=128, H=128, W=256, k=3, stride=2, pad=1, cip=1,
              out=FAKE2 * 8, stream=None)
     a.update(kw)
-    return ct.lib.ct_avgpool3d(a["x"], a["N"], a["C"], a["D"], a["H"], a["W"], a["k"],
+    return getattr(ct.lib, fn)(a["x"], a["N"], a["C"], a["D"], a["H"], a["W"], a["k"],
                                a["stride"], a["pad"], a["cip"], a["out"], a["stream"])
 
 
-@pytest.mark.parametrize("kw,status", [
+POOL_REJECTS = [
     (dict(x=None), ct.CT_EINVAL),
     (dict(out=None), ct.CT_EINVAL),
     (dict(C=0), ct.CT_EINVAL),
@@ -131,11 +131,20 @@ def pool(**kw):
     (dict(k=2, pad=0, N=1, C=1, D=2, H=2, W=(1 << 30) + 2, out=1 << 44),
      ct.CT_EUNSUPPORTED),                           # general kernel's index range
     (dict(k=1025, pad=0, N=1, C=1, D=2000, H=2000, W=2000, out=1 << 44), ct.CT_EUNSUPPORTED),
-    (dict(x=FAKE + 1), ct.CT_EINVAL),
+    (dict(x=FAKE + 1), ct.CT_EINVAL),               # misaligned for 4- and 2-byte elements
     (dict(out=FAKE + 4096), ct.CT_EINVAL),          # overlaps x
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", POOL_REJECTS)
 def test_pool_rejects(kw, status):
     assert pool(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", POOL_REJECTS)
+def test_pool_bf16_rejects(kw, status):
+    assert pool("ct_avgpool3d_bf16", **kw) == status
+    assert ct.ct_last_error().startswith("avgpool3d_bf16")
 
 
 def conv1d(**kw):

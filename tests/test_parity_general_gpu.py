@@ -204,6 +204,23 @@ def test_pool_general(dev, case):
     assert_close(out.cpu().numpy(), ref, F32_TOL, str(case))
 
 
+@pytest.mark.parametrize("case", POOL_GENERAL, ids=lambda c: "x".join(map(str, c[0])) +
+                         f"_k{c[1]}s{c[2]}p{c[3]}c{int(c[4])}")
+def test_pool_general_bf16(dev, case):
+    """bf16 data on the general kernel: fp32 sums, each mean rounded to the
+    nearest bf16 (within one bf16 step of the fp64 oracle on the same values)."""
+    shape, k, s, p, cip = case
+    log(f"pool general bf16 {case}")
+    x = bf16_round(synth.normal(7500 + sum(shape) + k, 0, shape))
+    ref = oracle.avgpool3d(x, k, s if s else k, p, cip)
+    out = torch.full(ref.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ct.ct_avgpool3d(to_dev(x, dev, "bf16"), k, s, p, cip, out=out)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    got = synth.bf16_bits_to_f32(o).reshape(o.shape)
+    assert_close(got, ref, (1e-5, 2.0 ** -8), str(case))
+
+
 def test_pool_valid_tap_divisor_border_values(dev):
     """count_include_pad off: an all-ones input averages to exactly 1 everywhere."""
     x = torch.ones((1, 1, 6, 7, 9), dtype=torch.float32, device=dev)

@@ -266,6 +266,67 @@ def test_pool_constant_input_border_values(dev):
     assert abs(o[-1, -1, -1] - 1.0) < 1e-6
 
 
+# bf16 pooling: fp32 sums of exactly widened taps, each mean rounded to the
+# nearest bf16.  The rounding is at most half a bf16 step (2^-9 relative) and
+# the fp32 sum/divide adds ~1e-6 absolute at these magnitudes, so one step
+# (2^-8 relative) plus 1e-5 absolute bounds the difference from the fp64
+# oracle on the same bf16 values (well inside the rel 2e-2 bf16 bound).
+POOL_BF16_TOL = (1e-5, 2.0 ** -8)
+
+
+def pool_bf16(dev, x, shift=0):
+    """Pool the bf16 values x (fp32 array) on the GPU; returns fp32.  shift > 0
+    places x that many elements into its buffer (misaligned starts)."""
+    bits = torch.from_numpy(synth.to_bf16_bits(x).reshape(-1).view(np.int16))
+    buf = torch.zeros(bits.numel() + shift, dtype=torch.int16, device=dev)
+    buf[shift:] = bits.to(dev)
+    xg = buf[shift:].view(torch.bfloat16).view(x.shape)
+    dims = [(n - 1) // 2 + 1 for n in x.shape[2:]]
+    out = torch.full(x.shape[:2] + tuple(dims), float("nan"), dtype=torch.bfloat16, device=dev)
+    ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return synth.bf16_bits_to_f32(o).reshape(o.shape)
+
+
+@pytest.mark.parametrize("shape", POOL_SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_pool_bf16_small(dev, shape):
+    log(f"pool bf16 {shape}")
+    x = bf16_round(synth.normal(2500 + sum(shape), 0, shape))
+    assert_close(pool_bf16(dev, x), oracle.avgpool3d(x, 3, 2, 1, True), POOL_BF16_TOL,
+                 f"pool bf16 {shape}")
+
+
+@pytest.mark.parametrize("shift", [1, 2], ids=["2-byte", "4-byte"])
+def test_pool_bf16_misaligned_input_takes_element_path(dev, shift):
+    shape = (2, 2, 6, 7, 64)
+    x = bf16_round(synth.normal(33, 0, shape))
+    assert_close(pool_bf16(dev, x, shift), oracle.avgpool3d(x, 3, 2, 1, True), POOL_BF16_TOL,
+                 f"pool bf16 shifted by {shift}")
+
+
+def test_pool_bf16_c3_shape_sampled(dev):
+    """The large pooling shape [16,32,128,128,256] with bf16 data (4.3 GB);
+    6 whole (n, c) slices recomputed by the oracle, plus global finiteness."""
+    wl = synth.WORKLOADS["c3"]
+    log(wl.description + " in bf16")
+    x = synth.normal(wl.seed, synth.STREAM_X, wl.x_shape)
+    bits = synth.to_bf16_bits(x).reshape(x.shape)
+    del x
+    xg = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = torch.full((16, 32, 64, 64, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
+    torch.cuda.synchronize()
+    del xg
+    assert bool(torch.isfinite(out).all())
+    for (n, c) in [(0, 0), (0, 31), (7, 13), (11, 2), (15, 0), (15, 31)]:
+        xs = synth.bf16_bits_to_f32(bits[n, c]).reshape(bits[n, c].shape)
+        o = out[n, c].view(torch.int16).cpu().numpy().view(np.uint16)
+        got = synth.bf16_bits_to_f32(o).reshape(o.shape)
+        assert_close(got, oracle.avgpool3d(xs, 3, 2, 1, True), POOL_BF16_TOL,
+                     f"c3 bf16 slice {(n, c)}")
+
+
 def test_pool_plane_of_2_30_bytes_takes_element_path(dev):
     """A [16384, 16384] plane (2^30 bytes) is past the vector kernel's plane
     limit and runs on the element kernel; checked on bands at the top and

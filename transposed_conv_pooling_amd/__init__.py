@@ -56,6 +56,8 @@ def _load():
     lib.ct_convT3d.argtypes = [_ptr, _int, _ptr, _int, _ptr] + [_i64] * 6 + [_int] * 4 + [_ptr, _ptr]
     lib.ct_avgpool3d.restype = _int
     lib.ct_avgpool3d.argtypes = [_ptr] + [_i64] * 5 + [_int] * 4 + [_ptr, _ptr]
+    lib.ct_avgpool3d_bf16.restype = _int
+    lib.ct_avgpool3d_bf16.argtypes = [_ptr] + [_i64] * 5 + [_int] * 4 + [_ptr, _ptr]
     lib.ct_convT1d.restype = _int
     lib.ct_convT1d.argtypes = [_ptr, _int, _ptr, _int, _ptr] + [_i64] * 4 + [_int] * 5 + [_ptr, _ptr]
     lib.ct_status_str.restype = ctypes.c_char_p
@@ -199,20 +201,21 @@ def ct_convT3d(x, w, bias=None, stride: int = 2, pad: int = 1, out_pad: int = 0,
 
 def ct_avgpool3d(x, k: int = 3, stride: int = 2, pad: int = 1, count_include_pad: bool = True,
                  out=None, stream=None):
-    """AvgPool3d over zero padding; x [N,C,D,H,W] float32 -> float32."""
+    """AvgPool3d over zero padding; x [N,C,D,H,W] float32 -> float32, or
+    bfloat16 -> bfloat16 (fp32 sums, each mean rounded to the nearest bf16)."""
     torch = _torch()
     N, C, D, H, W = x.shape
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    dt = x.dtype
     dims = [ct_pool_out_len(n, k, stride, pad) for n in (D, H, W)]
     if out is None:
-        out = torch.empty((N, C, *[max(d, 0) for d in dims]), dtype=torch.float32,
-                          device=x.device)
-    elif tuple(out.shape) != (N, C, *dims) or out.dtype != torch.float32:
-        raise ValueError(f"out must be float32 {(N, C, *dims)}")
-    if x.dtype != torch.float32:
-        raise TypeError("x must be float32")
-    st = lib.ct_avgpool3d(_dev_ptr(x, "x"), N, C, D, H, W, k, stride, pad,
-                          1 if count_include_pad else 0, _dev_ptr(out, "out"),
-                          _stream_handle(x, stream))
+        out = torch.empty((N, C, *[max(d, 0) for d in dims]), dtype=dt, device=x.device)
+    elif tuple(out.shape) != (N, C, *dims) or out.dtype != dt:
+        raise ValueError(f"out must be {dt} {(N, C, *dims)}")
+    fn = lib.ct_avgpool3d if dt == torch.float32 else lib.ct_avgpool3d_bf16
+    st = fn(_dev_ptr(x, "x"), N, C, D, H, W, k, stride, pad,
+            1 if count_include_pad else 0, _dev_ptr(out, "out"), _stream_handle(x, stream))
     _check(st)
     return out
 

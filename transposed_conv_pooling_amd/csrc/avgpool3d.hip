@@ -1,5 +1,6 @@
 // avgpool3d.hip - AvgPool3d(k3, s2, p1) with zero padding counted in the
-// divisor (27), fp32, streaming each input byte from HBM about once.
+// divisor (27), streaming each input byte from HBM about once.  fp32 data,
+// or bf16 data with fp32 sums and each mean rounded to the nearest bf16.
 //
 // Method ([p46] "Kimi-K2.6 l1_p46"): out[d,h,w] is the sum of
 // x[2d-1+kd, 2h-1+kh, 2w-1+kw] over kd,kh,kw < 3, out-of-range taps reading 0,
@@ -61,6 +62,55 @@ __device__ __forceinline__ float shr1(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x138, 0xf, 0xf, false));
 }
 
+// Element type of the pooled tensor: fp32, or bf16 carried as its 16-bit
+// pattern (widened exactly to fp32 for the sums; the mean is rounded to the
+// nearest bf16, ties to even, by the hardware conversion).
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <typename E> struct Elem;
+template <> struct Elem<float> {
+    typedef v4f raw4;                        // 4 consecutive elements as loaded
+    template <int kAux>
+    static __device__ __forceinline__ raw4 load4(__amdgpu_buffer_rsrc_t r, unsigned off)
+    {
+        return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kAux));
+    }
+    static __device__ __forceinline__ v4f widen(raw4 v) { return v; }
+    static __device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, unsigned off)
+    {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+    static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, unsigned off, float a, float b)
+    {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v2f{a, b}), r, (int)off, 0, 2);
+    }
+    static __device__ __forceinline__ float to_f32(float v) { return v; }
+    static __device__ __forceinline__ float from_f32(float v) { return v; }
+};
+template <> struct Elem<uint16_t> {
+    typedef u32x2 raw4;                      // 4 bf16 in two dwords
+    template <int kAux>
+    static __device__ __forceinline__ raw4 load4(__amdgpu_buffer_rsrc_t r, unsigned off)
+    {
+        return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kAux);
+    }
+    static __device__ __forceinline__ v4f widen(raw4 v)
+    {
+        return v4f{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                   __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+    }
+    static __device__ __forceinline__ float load1(__amdgpu_buffer_rsrc_t r, unsigned off)
+    {
+        return __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0) << 16);
+    }
+    static __device__ __forceinline__ uint16_t from_f32(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+    static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, unsigned off, float a, float b)
+    {
+        const unsigned u = (unsigned)from_f32(a) | ((unsigned)from_f32(b) << 16);
+        __builtin_amdgcn_raw_buffer_store_b32(u, r, (int)off, 0, 2);
+    }
+    static __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((unsigned)v << 16); }
+};
+
 // ------------------------------------------------------------ vector kernel --
 constexpr int kVWaves = 16;                  // waves per workgroup
 constexpr int kVThreads = 64 * kVWaves;
@@ -69,7 +119,7 @@ constexpr int kGroupRows = kVWaves * kTH;    // output rows per workgroup
 constexpr int kGroupIn = 2 * kGroupRows;     // input rows per workgroup
 constexpr unsigned kOOB = 0x40000000u;       // past every buffer (planes < 2^30 bytes)
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const float *base, bool valid, int bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void *base, bool valid, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, valid ? bytes : 0, 0x00020000);
 }
@@ -77,29 +127,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const float *base, 
 // Raw rows of one plane in flight: row rowbase + wave + kVWaves*k in v[k];
 // (kWide) lane k also holds the element left of the wave's first column in
 // that row.
+template <typename E>
 struct Rows {
-    v4f v[kOwn];
+    typename Elem<E>::raw4 v[kOwn];
     float lf;
 };
 
-template <bool kWide>
-__device__ __forceinline__ void issue_plane(Rows &R, const float *xs, int p, bool want, int D, int H,
+template <typename E, bool kWide>
+__device__ __forceinline__ void issue_plane(Rows<E> &R, const E *xs, int p, bool want, int D, int H,
                                             int W, int rowbase, int wave, int lane,
                                             unsigned laneoff, int c0w)
 {
     const bool ok = want && p >= 0 && p < D;
-    const __amdgpu_buffer_rsrc_t rs = plane_rsrc(xs + (int64_t)(ok ? p : 0) * H * W, ok, H * W * 4);
+    constexpr int ES = (int)sizeof(E);
+    const __amdgpu_buffer_rsrc_t rs = plane_rsrc(xs + (int64_t)(ok ? p : 0) * H * W, ok, H * W * ES);
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) {
         const int row = rowbase + wave + kVWaves * k;
-        const unsigned roff = row < H ? (unsigned)(row * W * 4) : kOOB;
-        R.v[k] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(roff + laneoff), 0, 2));
+        const unsigned roff = row < H ? (unsigned)(row * W * ES) : kOOB;
+        R.v[k] = Elem<E>::template load4<2>(rs, roff + laneoff);
     }
     if (kWide) {
         const int row = rowbase + wave + kVWaves * lane;
         const unsigned loff = (lane < kOwn && row < H && c0w > 0)
-                                  ? (unsigned)((row * W + c0w - 1) * 4) : kOOB;
-        R.lf = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)loff, 0, 0));
+                                  ? (unsigned)((row * W + c0w - 1) * ES) : kOOB;
+        R.lf = Elem<E>::load1(rs, loff);
     }
 }
 
@@ -114,21 +166,21 @@ __device__ __forceinline__ v2f hsum(v4f v, float lf, int lane)
 }
 
 // The wave's rows of one plane, as horizontal sums, into the row table.
-template <bool kWide>
-__device__ __forceinline__ void put_rows(const Rows &R, v2f (*T)[64], int wave, int lane)
+template <typename E, bool kWide>
+__device__ __forceinline__ void put_rows(const Rows<E> &R, v2f (*T)[64], int wave, int lane)
 {
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) {
         const int lf = kWide ? __builtin_amdgcn_readlane(__float_as_int(R.lf), k) : 0;
-        T[wave + kVWaves * k][lane] = hsum<kWide>(R.v[k], __int_as_float(lf), lane);
+        T[wave + kVWaves * k][lane] = hsum<kWide>(Elem<E>::widen(R.v[k]), __int_as_float(lf), lane);
     }
 }
 
 // After the barrier: vertical sums of the wave's kTH output rows from table
 // rows 8w-1 .. 8w+7.  Row -1 of the table is padding for the first row
 // group and the last row of the previous group otherwise (read from memory).
-template <bool kWide>
-__device__ __forceinline__ void get_vsums(v2f (*T)[64], const float *xs, int p, int D, int H, int W,
+template <typename E, bool kWide>
+__device__ __forceinline__ void get_vsums(v2f (*T)[64], const E *xs, int p, int D, int H, int W,
                                           int rowbase, int wave, int lane, unsigned laneoff,
                                           int c0w, v2f vs[kTH])
 {
@@ -139,13 +191,14 @@ __device__ __forceinline__ void get_vsums(v2f (*T)[64], const float *xs, int p, 
     if (wave > 0) {
         r[0] = T[kOwn * wave - 1][lane];
     } else if (rowbase > 0 && p >= 0 && p < D) {
-        const __amdgpu_buffer_rsrc_t rs = plane_rsrc(xs + (int64_t)p * H * W, true, H * W * 4);
-        const unsigned roff = (unsigned)((rowbase - 1) * W * 4);
-        const v4f a = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(roff + laneoff), 0, 0));
+        constexpr int ES = (int)sizeof(E);
+        const __amdgpu_buffer_rsrc_t rs = plane_rsrc(xs + (int64_t)p * H * W, true, H * W * ES);
+        const unsigned roff = (unsigned)((rowbase - 1) * W * ES);
+        const v4f a = Elem<E>::widen(Elem<E>::template load4<0>(rs, roff + laneoff));
         float lf = 0.0f;
         if (kWide) {
-            const unsigned loff = (lane == 0 && c0w > 0) ? roff + (unsigned)((c0w - 1) * 4) : kOOB;
-            lf = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)loff, 0, 0));
+            const unsigned loff = (lane == 0 && c0w > 0) ? roff + (unsigned)((c0w - 1) * ES) : kOOB;
+            lf = Elem<E>::load1(rs, loff);
         }
         r[0] = hsum<kWide>(a, lf, lane);
     } else {
@@ -157,9 +210,9 @@ __device__ __forceinline__ void get_vsums(v2f (*T)[64], const float *xs, int p, 
 
 // Grid: one workgroup per (slice, plane chunk of td output planes, column
 // chunk, row group of kGroupRows output rows), row groups fastest.
-template <bool kWide>
+template <typename E, bool kWide>
 __global__ __launch_bounds__(kVThreads)
-void avgpool3d_k3s2p1_vec_kernel(const float *__restrict__ x, float *__restrict__ out,
+void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
                                  int D, int H, int W, int Do, int Ho, int Wo,
                                  int hgroups, int dchunks, int wchunks, int td)
 {
@@ -179,56 +232,56 @@ void avgpool3d_k3s2p1_vec_kernel(const float *__restrict__ x, float *__restrict_
     const int c0w = wc * (2 * kTW);
     const int c = c0w + 4 * lane;
     const int wo = wc * kTW + 2 * lane;
-    const unsigned laneoff = c < W ? (unsigned)(c * 4) : kOOB;
-    const float *xs = x + sl * (int64_t)D * H * W;
-    float *os = out + sl * (int64_t)Do * Ho * Wo;
-    const int obytes = Ho * Wo * 4;
+    constexpr int ES = (int)sizeof(E);
+    const unsigned laneoff = c < W ? (unsigned)(c * ES) : kOOB;
+    const E *xs = x + sl * (int64_t)D * H * W;
+    E *os = out + sl * (int64_t)Do * Ho * Wo;
+    const int obytes = Ho * Wo * ES;
     const float inv27 = 1.0f / 27.0f;
 
     // planes go through T[0], T[1], T[0], ... starting with plane 2*d0-1
-    Rows A, B;
+    Rows<E> A, B;
     v2f carry[kTH];
-    issue_plane<kWide>(A, xs, 2 * d0 - 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-    issue_plane<kWide>(B, xs, 2 * d0, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-    put_rows<kWide>(A, T[0], wave, lane);
+    issue_plane<E, kWide>(A, xs, 2 * d0 - 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+    issue_plane<E, kWide>(B, xs, 2 * d0, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+    put_rows<E, kWide>(A, T[0], wave, lane);
     __builtin_amdgcn_sched_barrier(0);
-    issue_plane<kWide>(A, xs, 2 * d0 + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+    issue_plane<E, kWide>(A, xs, 2 * d0 + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
     // (an empty asm with a memory clobber after each issue keeps the loads
     // ahead of the barrier in get_vsums; without it the compiler sinks them
     // past the barrier and the LDS reads, delaying the next plane)
     asm volatile("" ::: "memory");
-    get_vsums<kWide>(T[0], xs, 2 * d0 - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
+    get_vsums<E, kWide>(T[0], xs, 2 * d0 - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
     // stores past the range, so that the memory-counter state entering the
     // loop matches the one at its back-edge
     const __amdgpu_buffer_rsrc_t none = plane_rsrc(os, false, 0);
 #pragma unroll
-    for (int i = 0; i < kTH; ++i)
-        __builtin_amdgcn_raw_buffer_store_b64(v2i{0, 0}, none, (int)kOOB, 0, 2);
+    for (int i = 0; i < kTH; ++i) Elem<E>::store2(none, kOOB, 0.0f, 0.0f);
 
     // invariant: B holds plane 2d and A plane 2d+1, both in flight
     for (int d = d0; d < d1; ++d) {
         const bool more = d + 1 < d1;
         v2f acc[kTH], v[kTH];
-        put_rows<kWide>(B, T[1], wave, lane);
+        put_rows<E, kWide>(B, T[1], wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        issue_plane<kWide>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        issue_plane<E, kWide>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
         asm volatile("" ::: "memory");
-        get_vsums<kWide>(T[1], xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
+        get_vsums<E, kWide>(T[1], xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
 #pragma unroll
         for (int i = 0; i < kTH; ++i) acc[i] = carry[i] + v[i];
-        put_rows<kWide>(A, T[0], wave, lane);
+        put_rows<E, kWide>(A, T[0], wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        issue_plane<kWide>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        issue_plane<E, kWide>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
         asm volatile("" ::: "memory");
-        get_vsums<kWide>(T[0], xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
+        get_vsums<E, kWide>(T[0], xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
         const __amdgpu_buffer_rsrc_t ro = plane_rsrc(os + (int64_t)d * Ho * Wo, true, obytes);
 #pragma unroll
         for (int i = 0; i < kTH; ++i) {
             const int h = h0 + i;
             const v2f o = (acc[i] + v[i]) * inv27;
             // Wo is even here (W % 4 == 0), so wo < Wo covers the pair
-            const unsigned off = (h < Ho && wo < Wo) ? (unsigned)((h * Wo + wo) * 4) : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, o), ro, (int)off, 0, 2);
+            const unsigned off = (h < Ho && wo < Wo) ? (unsigned)((h * Wo + wo) * ES) : kOOB;
+            Elem<E>::store2(ro, off, o.x, o.y);
             carry[i] = v[i];
         }
     }
@@ -242,7 +295,8 @@ constexpr int kETD = 8;               // output planes per workgroup
 
 // Vertical 3-row sums of one input plane for the wave's kTH output rows,
 // element-wise masked loads.  vs[i][0/1] = V[plane][h0+i][2 outputs of this lane].
-__device__ __forceinline__ void plane_sums_elem(const float *__restrict__ xs, int plane, int D,
+template <typename E>
+__device__ __forceinline__ void plane_sums_elem(const E *__restrict__ xs, int plane, int D,
                                                 int H, int W, int h0, int c, int lane,
                                                 float vs[kTH][2])
 {
@@ -254,11 +308,11 @@ __device__ __forceinline__ void plane_sums_elem(const float *__restrict__ xs, in
         float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         float left = 0.0f;
         if (pok && row >= 0 && row < H) {
-            const float *rp = xs + ((int64_t)plane * H + row) * W;
+            const E *rp = xs + ((int64_t)plane * H + row) * W;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (c + j < W) v[j] = rp[c + j];
-            if (lane == 0 && c > 0) left = rp[c - 1];
+                if (c + j < W) v[j] = Elem<E>::to_f32(rp[c + j]);
+            if (lane == 0 && c > 0) left = Elem<E>::to_f32(rp[c - 1]);
         }
         left += shr1(v[3]);
         rs[r][0] = left + v[0] + v[1];
@@ -271,8 +325,9 @@ __device__ __forceinline__ void plane_sums_elem(const float *__restrict__ xs, in
     }
 }
 
+template <typename E>
 __global__ __launch_bounds__(kEThreads)
-void avgpool3d_k3s2p1_elem_kernel(const float *__restrict__ x, float *__restrict__ out,
+void avgpool3d_k3s2p1_elem_kernel(const E *__restrict__ x, E *__restrict__ out,
                                   int D, int H, int W, int Do, int Ho, int Wo,
                                   int hgroups, int dchunks, int wchunks)
 {
@@ -291,8 +346,8 @@ void avgpool3d_k3s2p1_elem_kernel(const float *__restrict__ x, float *__restrict
     const int c = wc * (2 * kTW) + 4 * lane;    // first input column of this lane
     const int wo = wc * kTW + 2 * lane;         // first output column of this lane
 
-    const float *xs = x + sl * (int64_t)D * H * W;
-    float *os = out + sl * (int64_t)Do * Ho * Wo;
+    const E *xs = x + sl * (int64_t)D * H * W;
+    E *os = out + sl * (int64_t)Do * Ho * Wo;
 
     float carry[kTH][2];
     plane_sums_elem(xs, 2 * d0 - 1, D, H, W, h0, c, lane, carry);
@@ -307,9 +362,9 @@ void avgpool3d_k3s2p1_elem_kernel(const float *__restrict__ x, float *__restrict
             const float o0 = (carry[i][0] + va[i][0] + vb[i][0]) * inv27;
             const float o1 = (carry[i][1] + va[i][1] + vb[i][1]) * inv27;
             if (h < Ho) {
-                float *orow = os + ((int64_t)d * Ho + h) * Wo;
-                if (wo < Wo) __builtin_nontemporal_store(o0, orow + wo);
-                if (wo + 1 < Wo) __builtin_nontemporal_store(o1, orow + wo + 1);
+                E *orow = os + ((int64_t)d * Ho + h) * Wo;
+                if (wo < Wo) __builtin_nontemporal_store(Elem<E>::from_f32(o0), orow + wo);
+                if (wo + 1 < Wo) __builtin_nontemporal_store(Elem<E>::from_f32(o1), orow + wo + 1);
             }
             carry[i][0] = vb[i][0];
             carry[i][1] = vb[i][1];
@@ -319,16 +374,20 @@ void avgpool3d_k3s2p1_elem_kernel(const float *__restrict__ x, float *__restrict
 
 }  // namespace
 
-hipError_t launch_avgpool3d_k3s2p1(const float *x, int64_t NC, int64_t D,
-                                   int64_t H, int64_t W, float *out,
-                                   hipStream_t stream)
+namespace {
+template <typename E>
+hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W, E *out,
+                         hipStream_t stream)
 {
     const int Do = (int)((D - 1) / 2 + 1);
     const int Ho = (int)((H - 1) / 2 + 1);
     const int Wo = (int)((W - 1) / 2 + 1);
     const int wchunks = (Wo + kTW - 1) / kTW;
-    const bool vec = (W % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(out) & 7) == 0) && H * W * 4 < (int64_t)kOOB;
+    constexpr int ES = (int)sizeof(E);
+    // vector path: 4 elements per lane load, 2 per lane store, planes < 2^30 bytes
+    const bool vec = (W % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) % (4 * ES)) == 0) &&
+                     ((reinterpret_cast<uintptr_t>(out) % (2 * ES)) == 0) &&
+                     H * W * ES < (int64_t)kOOB;
     if (vec) {
         const int hgroups = (Ho + kGroupRows - 1) / kGroupRows;
         // as few plane chunks as still give every CU two workgroups
@@ -343,22 +402,33 @@ hipError_t launch_avgpool3d_k3s2p1(const float *x, int64_t NC, int64_t D,
         dchunks = (Do + td - 1) / td;
         const int64_t nwg = base * dchunks;
         if (wchunks > 1)
-            hipLaunchKernelGGL(avgpool3d_k3s2p1_vec_kernel<true>, dim3((unsigned)nwg),
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true>), dim3((unsigned)nwg),
                                dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do,
                                Ho, Wo, hgroups, (int)dchunks, wchunks, td);
         else
-            hipLaunchKernelGGL(avgpool3d_k3s2p1_vec_kernel<false>, dim3((unsigned)nwg),
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, false>), dim3((unsigned)nwg),
                                dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do,
                                Ho, Wo, hgroups, (int)dchunks, wchunks, td);
     } else {
         const int hgroups = (Ho + kEWaves * kTH - 1) / (kEWaves * kTH);
         const int dchunks = (Do + kETD - 1) / kETD;
         const int64_t nwg = NC * (int64_t)hgroups * dchunks * wchunks;
-        hipLaunchKernelGGL(avgpool3d_k3s2p1_elem_kernel, dim3((unsigned)nwg), dim3(kEThreads), 0,
-                           stream, x, out, (int)D, (int)H, (int)W, Do, Ho, Wo, hgroups, dchunks,
-                           wchunks);
+        hipLaunchKernelGGL((avgpool3d_k3s2p1_elem_kernel<E>), dim3((unsigned)nwg),
+                           dim3(kEThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do, Ho,
+                           Wo, hgroups, dchunks, wchunks);
     }
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, int64_t NC, int64_t D, int64_t H,
+                                   int64_t W, void *out, hipStream_t stream)
+{
+    if (bf16)
+        return launch_k3s2p1(static_cast<const uint16_t *>(x), NC, D, H, W,
+                             static_cast<uint16_t *>(out), stream);
+    return launch_k3s2p1(static_cast<const float *>(x), NC, D, H, W, static_cast<float *>(out),
+                         stream);
 }
 
 }  // namespace ct

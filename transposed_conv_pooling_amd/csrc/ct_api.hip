@@ -268,31 +268,35 @@ ct_status ct_convT3d(const void *x, int x_dtype, const void *w, int w_dtype, con
     return hip_status(e, "convT3d launch");
 }
 
-ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
-                       int k, int stride, int pad, int count_include_pad, float *out,
-                       void *stream)
+namespace {
+// ct_avgpool3d and ct_avgpool3d_bf16: x and out are fp32 (bf16 = false) or
+// bf16 bit patterns (bf16 = true); es is the element size in bytes.
+ct_status avgpool3d_impl(const char *fn, const void *x, bool bf16, int64_t N, int64_t C,
+                         int64_t D, int64_t H, int64_t W, int k, int stride, int pad,
+                         int count_include_pad, void *out, void *stream)
 {
-    if (!x || !out) return fail(CT_EINVAL, "avgpool3d: x and out must be non-null");
+    const int es = bf16 ? 2 : 4;
+    if (!x || !out) return fail(CT_EINVAL, "%s: x and out must be non-null", fn);
     if (N < 1 || C < 1 || D < 1 || H < 1 || W < 1)
-        return fail(CT_EINVAL, "avgpool3d: sizes must be >= 1");
+        return fail(CT_EINVAL, "%s: sizes must be >= 1", fn);
     if (k < 1 || stride < 0 || pad < 0 || 2 * (int64_t)pad > k ||
         (count_include_pad != 0 && count_include_pad != 1))
-        return fail(CT_EINVAL, "avgpool3d: invalid geometry k=%d stride=%d pad=%d count_include_pad=%d "
-                    "(pad must be <= k/2)", k, stride, pad, count_include_pad);
+        return fail(CT_EINVAL, "%s: invalid geometry k=%d stride=%d pad=%d count_include_pad=%d "
+                    "(pad must be <= k/2)", fn, k, stride, pad, count_include_pad);
     const int s = stride == 0 ? k : stride;
     int64_t o[3];
     const int64_t in[3] = {D, H, W};
     for (int i = 0; i < 3; ++i) {
         o[i] = ct_pool_out_len(in[i], k, s, pad);
         if (o[i] <= 0)
-            return fail(CT_EINVAL, "avgpool3d: empty output along axis %d", i);
+            return fail(CT_EINVAL, "%s: empty output along axis %d", fn, i);
     }
-    if (!aligned(x, 4) || !aligned(out, 4)) return fail(CT_EINVAL, "avgpool3d: misaligned pointer");
+    if (!aligned(x, es) || !aligned(out, es)) return fail(CT_EINVAL, "%s: misaligned pointer", fn);
     int64_t nx, no, slice;
-    if (!prod({N, C, D, H, W, 4}, &nx) || !prod({N, C, o[0], o[1], o[2], 4}, &no) ||
+    if (!prod({N, C, D, H, W, es}, &nx) || !prod({N, C, o[0], o[1], o[2], es}, &no) ||
         !prod({D, H, W}, &slice))
-        return fail(CT_EINVAL, "avgpool3d: tensor size overflows");
-    if (overlap(out, no, x, nx)) return fail(CT_EINVAL, "avgpool3d: out overlaps x");
+        return fail(CT_EINVAL, "%s: tensor size overflows", fn);
+    if (overlap(out, no, x, nx)) return fail(CT_EINVAL, "%s: out overlaps x", fn);
 
     bool fast = k == 3 && s == 2 && pad == 1 && count_include_pad == 1;
     if (fast) {
@@ -303,17 +307,34 @@ ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t 
     }
     hipError_t e;
     if (fast) {
-        e = ct::launch_avgpool3d_k3s2p1(x, N * C, D, H, W, out, (hipStream_t)stream);
+        e = ct::launch_avgpool3d_k3s2p1(x, bf16, N * C, D, H, W, out, (hipStream_t)stream);
     } else {
         if (D > kGenericMaxLen || H > kGenericMaxLen || W > kGenericMaxLen || k > kGenericMaxTap ||
             s > kGenericMaxLen)
-            return fail(CT_EUNSUPPORTED, "avgpool3d: sizes beyond the general kernel's index range "
-                        "(lengths and stride <= %lld, k <= %d)", (long long)kGenericMaxLen,
+            return fail(CT_EUNSUPPORTED, "%s: sizes beyond the general kernel's index range "
+                        "(lengths and stride <= %lld, k <= %d)", fn, (long long)kGenericMaxLen,
                         kGenericMaxTap);
-        e = ct::launch_avgpool3d_generic(x, N * C, D, H, W, k, s, pad, count_include_pad, out,
-                                         (hipStream_t)stream);
+        e = ct::launch_avgpool3d_generic(x, bf16, N * C, D, H, W, k, s, pad, count_include_pad,
+                                         out, (hipStream_t)stream);
     }
-    return hip_status(e, "avgpool3d launch");
+    return hip_status(e, fn);
+}
+}  // namespace
+
+ct_status ct_avgpool3d(const float *x, int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,
+                       int k, int stride, int pad, int count_include_pad, float *out,
+                       void *stream)
+{
+    return avgpool3d_impl("avgpool3d", x, false, N, C, D, H, W, k, stride, pad,
+                          count_include_pad, out, stream);
+}
+
+ct_status ct_avgpool3d_bf16(const uint16_t *x, int64_t N, int64_t C, int64_t D, int64_t H,
+                            int64_t W, int k, int stride, int pad, int count_include_pad,
+                            uint16_t *out, void *stream)
+{
+    return avgpool3d_impl("avgpool3d_bf16", x, true, N, C, D, H, W, k, stride, pad,
+                          count_include_pad, out, stream);
 }
 
 ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, const float *bias,

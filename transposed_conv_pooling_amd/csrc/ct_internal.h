@@ -25,9 +25,10 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w,
                                int64_t D, int64_t H, int64_t W, int64_t Cout,
                                float *out, hipStream_t stream);
 
-// AvgPool3d(k3, s2, p1), divisor 27, over NC independent [D][H][W] slices.
-hipError_t launch_avgpool3d_k3s2p1(const float *x, int64_t NC, int64_t D,
-                                   int64_t H, int64_t W, float *out,
+// AvgPool3d(k3, s2, p1), divisor 27, over NC independent [D][H][W] slices;
+// x and out fp32, or (bf16 = true) bf16 bit patterns with fp32 sums.
+hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, int64_t NC, int64_t D,
+                                   int64_t H, int64_t W, void *out,
                                    hipStream_t stream);
 
 // ConvTranspose1d, stride 1, pad 0, any K and dilation, fp32.
@@ -63,8 +64,8 @@ hipError_t launch_convT3d_generic(const void *x, const void *w, bool bf16, const
                                   int64_t N, int64_t Cin, int64_t D, int64_t H, int64_t W,
                                   int64_t Cout, int k, int s, int p, int op, float *y,
                                   hipStream_t stream);
-hipError_t launch_avgpool3d_generic(const float *x, int64_t NC, int64_t D, int64_t H, int64_t W,
-                                    int k, int s, int p, int include_pad, float *out,
+hipError_t launch_avgpool3d_generic(const void *x, bool bf16, int64_t NC, int64_t D, int64_t H,
+                                    int64_t W, int k, int s, int p, int include_pad, void *out,
                                     hipStream_t stream);
 hipError_t launch_convT1d_generic(const void *x, const void *w, bool bf16, const float *bias,
                                   int64_t N, int64_t Cin, int64_t L, int64_t Cout, int K, int s,

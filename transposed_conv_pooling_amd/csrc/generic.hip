@@ -55,6 +55,13 @@ template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t *p, int
 {
     return __uint_as_float(((unsigned)p[i]) << 16);   // bf16 -> fp32, exact
 }
+// fp32 result -> element: as is, or rounded to the nearest bf16 (ties to even)
+template <typename T, typename I> __device__ __forceinline__ void st(T *p, I i, float v);
+template <typename I> __device__ __forceinline__ void st(float *p, I i, float v) { p[i] = v; }
+template <typename I> __device__ __forceinline__ void st(uint16_t *p, I i, float v)
+{
+    p[i] = __builtin_bit_cast(uint16_t, (__bf16)v);
+}
 
 // Geometry of a 3D transposed convolution (dilation 1) and the pool after it.
 struct Geo3 {
@@ -161,16 +168,16 @@ void convT3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
 // KC > 0: window size known at compile time; every tap is loaded from a
 // clamped (always valid) address and masked, so that all KC^3 loads are in
 // flight together.  KC == 0: run-time k, taps outside the input skipped.
-template <int KC, typename I>
+template <int KC, typename T, typename I>
 __global__ __launch_bounds__(kThreads)
-void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, int k, int s,
+void avgpool3d_generic_kernel(const T *__restrict__ x, int D, int H, int W, int k, int s,
                               int p, int include_pad, float kvol, Div dWo, Div dHo, Div dDo,
-                              I total, float *__restrict__ out)
+                              I total, T *__restrict__ out)
 {
     for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
         I t = e;
         const int ow = peel(t, dWo), oh = peel(t, dHo), od = peel(t, dDo);
-        const float *xs = x + (int64_t)t * D * H * W;
+        const T *xs = x + (int64_t)t * D * H * W;
         float sum = 0.0f;
         int cnt = 0;
         if constexpr (KC > 0) {
@@ -192,7 +199,7 @@ void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, 
                 for (int b = 0; b < KC; ++b)
 #pragma unroll
                     for (int c = 0; c < KC; ++c) {
-                        const float v = xs[((int64_t)id[a] * H + ih[b]) * W + iw[c]];
+                        const float v = ld(xs, ((int64_t)id[a] * H + ih[b]) * W + iw[c]);
                         const bool in = vd[a] && vh[b] && vw[c];
                         sum += in ? v : 0.0f;
                         cnt += in;
@@ -207,13 +214,13 @@ void avgpool3d_generic_kernel(const float *__restrict__ x, int D, int H, int W, 
                     for (int kw = 0; kw < k; ++kw) {
                         const int iw = ow * s - p + kw;
                         if (iw < 0 || iw >= W) continue;
-                        sum += xs[((int64_t)id * H + ih) * W + iw];
+                        sum += ld(xs, ((int64_t)id * H + ih) * W + iw);
                         ++cnt;
                     }
                 }
             }
         }
-        out[e] = sum / (include_pad ? kvol : (float)cnt);
+        st(out, e, sum / (include_pad ? kvol : (float)cnt));
     }
 }
 
@@ -307,8 +314,8 @@ hipError_t launch_convT3d_generic(const void *x, const void *w, bool bf16, const
     return hipGetLastError();
 }
 
-hipError_t launch_avgpool3d_generic(const float *x, int64_t NC, int64_t D, int64_t H, int64_t W,
-                                    int k, int s, int p, int include_pad, float *out,
+hipError_t launch_avgpool3d_generic(const void *x, bool bf16, int64_t NC, int64_t D, int64_t H,
+                                    int64_t W, int k, int s, int p, int include_pad, void *out,
                                     hipStream_t stream)
 {
     const int64_t Do = (D + 2 * p - k) / s + 1, Ho = (H + 2 * p - k) / s + 1,
@@ -317,14 +324,21 @@ hipError_t launch_avgpool3d_generic(const float *x, int64_t NC, int64_t D, int64
     const Div dW = make_div((uint32_t)Wo), dH = make_div((uint32_t)Ho), dD = make_div((uint32_t)Do);
     const float kvol = (float)k * k * k;
     const dim3 grid(grid_for(total)), block(kThreads);
-#define CT_POOL(KC, I)                                                                          \
-    hipLaunchKernelGGL((avgpool3d_generic_kernel<KC, I>), grid, block, 0, stream, x, (int)D,    \
-                       (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, dD, (I)total, out)
+#define CT_POOL(KC, T, I)                                                                       \
+    hipLaunchKernelGGL((avgpool3d_generic_kernel<KC, T, I>), grid, block, 0, stream,             \
+                       (const T *)x, (int)D, (int)H, (int)W, k, s, p, include_pad, kvol, dW, dH, \
+                       dD, (I)total, (T *)out)
+#define CT_POOL_T(T)                                                                            \
+    do {                                                                                        \
+        if (k == 2 && small) CT_POOL(2, T, uint32_t);                                           \
+        else if (k == 3 && small) CT_POOL(3, T, uint32_t);                                      \
+        else if (small) CT_POOL(0, T, uint32_t);                                                \
+        else CT_POOL(0, T, uint64_t);                                                           \
+    } while (0)
     const bool small = small_index(total);
-    if (k == 2 && small) CT_POOL(2, uint32_t);
-    else if (k == 3 && small) CT_POOL(3, uint32_t);
-    else if (small) CT_POOL(0, uint32_t);
-    else CT_POOL(0, uint64_t);
+    if (bf16) CT_POOL_T(uint16_t);
+    else CT_POOL_T(float);
+#undef CT_POOL_T
 #undef CT_POOL
     return hipGetLastError();
 }
