@@ -228,6 +228,7 @@ POOL_SMALL = [
     (1, 1, 5, 258, 520),      # three row groups, three column chunks, ragged last of each
     (4, 25, 40, 6, 8),        # 100 slices: several plane chunks of more than one plane
     (3, 1, 1, 4, 4),          # a single input plane
+    (8, 40, 40, 10, 16),      # 320 slices in ranges of 10 planes: every start offset of a bf16 range
 ]
 
 

@@ -40,7 +40,10 @@
 //    segment); the column 4l-1 comes from lane l-1 through a DPP wave shift;
 //  * a workgroup walks as many output planes as keeps two workgroups per CU,
 //    so that for the large case every slice is read by one workgroup from
-//    its first plane to its last and no plane is read twice.
+//    its first plane to its last and no plane is read twice (fp32); bf16
+//    workgroups start at staggered plane offsets and wrap around, so that
+//    the workgroups running together stream different offsets of their
+//    slices, at the cost of one plane read twice.
 // Other inputs (ragged W, misaligned x or out, planes of 2^30 bytes or more)
 // take the element kernel: one wave per 4 output rows, element-wise masked
 // loads, same arithmetic.
@@ -220,6 +223,7 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t t = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t blk = t;
     const int hg = (int)(t % hgroups); t /= hgroups;
     const int wc = (int)(t % wchunks); t /= wchunks;
     const int dc = (int)(t % dchunks); t /= dchunks;
@@ -239,50 +243,71 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
     const int obytes = Ho * Wo * ES;
     const float inv27 = 1.0f / 27.0f;
 
-    // planes go through T[0], T[1], T[0], ... starting with plane 2*d0-1
-    Rows<E> A, B;
-    v2f carry[kTH];
-    issue_plane<E, kWide>(A, xs, 2 * d0 - 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-    issue_plane<E, kWide>(B, xs, 2 * d0, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-    put_rows<E, kWide>(A, T[0], wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    issue_plane<E, kWide>(A, xs, 2 * d0 + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-    // (an empty asm with a memory clobber after each issue keeps the loads
-    // ahead of the barrier in get_vsums; without it the compiler sinks them
-    // past the barrier and the LDS reads, delaying the next plane)
-    asm volatile("" ::: "memory");
-    get_vsums<E, kWide>(T[0], xs, 2 * d0 - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
-    // stores past the range, so that the memory-counter state entering the
-    // loop matches the one at its back-edge
-    const __amdgpu_buffer_rsrc_t none = plane_rsrc(os, false, 0);
-#pragma unroll
-    for (int i = 0; i < kTH; ++i) Elem<E>::store2(none, kOOB, 0.0f, 0.0f);
-
-    // invariant: B holds plane 2d and A plane 2d+1, both in flight
-    for (int d = d0; d < d1; ++d) {
-        const bool more = d + 1 < d1;
-        v2f acc[kTH], v[kTH];
-        put_rows<E, kWide>(B, T[1], wave, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        issue_plane<E, kWide>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
-        asm volatile("" ::: "memory");
-        get_vsums<E, kWide>(T[1], xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
-#pragma unroll
-        for (int i = 0; i < kTH; ++i) acc[i] = carry[i] + v[i];
+    // Output planes [pa, pb): input planes go through T[0], T[1], T[0], ...
+    // starting with plane 2*pa-1
+    auto run = [&](const int pa, const int pb) {
+        Rows<E> A, B;
+        v2f carry[kTH];
+        issue_plane<E, kWide>(A, xs, 2 * pa - 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        issue_plane<E, kWide>(B, xs, 2 * pa, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
         put_rows<E, kWide>(A, T[0], wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        issue_plane<E, kWide>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        issue_plane<E, kWide>(A, xs, 2 * pa + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        // (an empty asm with a memory clobber after each issue keeps the loads
+        // ahead of the barrier in get_vsums; without it the compiler sinks them
+        // past the barrier and the LDS reads, delaying the next plane)
         asm volatile("" ::: "memory");
-        get_vsums<E, kWide>(T[0], xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
-        const __amdgpu_buffer_rsrc_t ro = plane_rsrc(os + (int64_t)d * Ho * Wo, true, obytes);
+        get_vsums<E, kWide>(T[0], xs, 2 * pa - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
+        // stores past the range, so that the memory-counter state entering the
+        // loop matches the one at its back-edge
+        const __amdgpu_buffer_rsrc_t none = plane_rsrc(os, false, 0);
 #pragma unroll
-        for (int i = 0; i < kTH; ++i) {
-            const int h = h0 + i;
-            const v2f o = (acc[i] + v[i]) * inv27;
-            // Wo is even here (W % 4 == 0), so wo < Wo covers the pair
-            const unsigned off = (h < Ho && wo < Wo) ? (unsigned)((h * Wo + wo) * ES) : kOOB;
-            Elem<E>::store2(ro, off, o.x, o.y);
-            carry[i] = v[i];
+        for (int i = 0; i < kTH; ++i) Elem<E>::store2(none, kOOB, 0.0f, 0.0f);
+
+        // invariant: B holds plane 2d and A plane 2d+1, both in flight
+        for (int d = pa; d < pb; ++d) {
+            const bool more = d + 1 < pb;
+            v2f acc[kTH], v[kTH];
+            put_rows<E, kWide>(B, T[1], wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_plane<E, kWide>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+            asm volatile("" ::: "memory");
+            get_vsums<E, kWide>(T[1], xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
+#pragma unroll
+            for (int i = 0; i < kTH; ++i) acc[i] = carry[i] + v[i];
+            put_rows<E, kWide>(A, T[0], wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_plane<E, kWide>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+            asm volatile("" ::: "memory");
+            get_vsums<E, kWide>(T[0], xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
+            const __amdgpu_buffer_rsrc_t ro = plane_rsrc(os + (int64_t)d * Ho * Wo, true, obytes);
+#pragma unroll
+            for (int i = 0; i < kTH; ++i) {
+                const int h = h0 + i;
+                const v2f o = (acc[i] + v[i]) * inv27;
+                // Wo is even here (W % 4 == 0), so wo < Wo covers the pair
+                const unsigned off = (h < Ho && wo < Wo) ? (unsigned)((h * Wo + wo) * ES) : kOOB;
+                Elem<E>::store2(ro, off, o.x, o.y);
+                carry[i] = v[i];
+            }
+        }
+    };
+    if constexpr (sizeof(E) == 4) {
+        run(d0, d1);
+    } else {
+        // bf16: each workgroup starts at its own plane offset and wraps
+        // around, so the workgroups running together stream different offsets
+        // of their slices (one plane is read twice).  At [16,32,128,128,256]
+        // this took 917 to 840 us; the same rotation made the fp32 kernel
+        // 3-4% slower, so fp32 keeps one pass from the first plane.
+        const int n = d1 - d0;
+        const int r = n > 1 ? (int)((blk * 13 + 5) % n) : 0;
+        if (r == 0) {
+            run(d0, d1);
+        } else {
+            run(d0 + r, d1);
+            __syncthreads();   // the second range's prologue rewrites T[0]
+            run(d0, d0 + r);
         }
     }
 }
