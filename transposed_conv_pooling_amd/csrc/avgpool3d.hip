@@ -82,9 +82,9 @@ template <> struct Elem<float> {
     {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
     }
-    static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, unsigned off, float a, float b)
+    static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, unsigned off, int soff, float a, float b)
     {
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v2f{a, b}), r, (int)off, 0, 2);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v2f{a, b}), r, (int)off, soff, 2);
     }
     static __device__ __forceinline__ float to_f32(float v) { return v; }
     static __device__ __forceinline__ float from_f32(float v) { return v; }
@@ -106,10 +106,10 @@ template <> struct Elem<uint16_t> {
         return __uint_as_float((unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0) << 16);
     }
     static __device__ __forceinline__ uint16_t from_f32(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
-    static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, unsigned off, float a, float b)
+    static __device__ __forceinline__ void store2(__amdgpu_buffer_rsrc_t r, unsigned off, int soff, float a, float b)
     {
         const unsigned u = (unsigned)from_f32(a) | ((unsigned)from_f32(b) << 16);
-        __builtin_amdgcn_raw_buffer_store_b32(u, r, (int)off, 0, 2);
+        __builtin_amdgcn_raw_buffer_store_b32(u, r, (int)off, soff, 2);
     }
     static __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((unsigned)v << 16); }
 };
@@ -238,6 +238,8 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
     const int wo = wc * kTW + 2 * lane;
     constexpr int ES = (int)sizeof(E);
     const unsigned laneoff = c < W ? (unsigned)(c * ES) : kOOB;
+    // Wo is even here (W % 4 == 0), so wo < Wo covers the lane's pair
+    const unsigned wooff = wo < Wo ? (unsigned)(wo * ES) : kOOB;
     const E *xs = x + sl * (int64_t)D * H * W;
     E *os = out + sl * (int64_t)Do * Ho * Wo;
     const int obytes = Ho * Wo * ES;
@@ -262,7 +264,7 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
         // loop matches the one at its back-edge
         const __amdgpu_buffer_rsrc_t none = plane_rsrc(os, false, 0);
 #pragma unroll
-        for (int i = 0; i < kTH; ++i) Elem<E>::store2(none, kOOB, 0.0f, 0.0f);
+        for (int i = 0; i < kTH; ++i) Elem<E>::store2(none, kOOB, 0, 0.0f, 0.0f);
 
         // invariant: B holds plane 2d and A plane 2d+1, both in flight
         for (int d = pa; d < pb; ++d) {
@@ -285,9 +287,10 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
             for (int i = 0; i < kTH; ++i) {
                 const int h = h0 + i;
                 const v2f o = (acc[i] + v[i]) * inv27;
-                // Wo is even here (W % 4 == 0), so wo < Wo covers the pair
-                const unsigned off = (h < Ho && wo < Wo) ? (unsigned)((h * Wo + wo) * ES) : kOOB;
-                Elem<E>::store2(ro, off, o.x, o.y);
+                // the row (wave-uniform) in the scalar offset, the lane's
+                // column in the vector offset; a row past the plane takes the
+                // zero-size resource
+                Elem<E>::store2(h < Ho ? ro : none, wooff, h < Ho ? h * Wo * ES : 0, o.x, o.y);
                 carry[i] = v[i];
             }
         }
