@@ -49,6 +49,9 @@ OP_SOURCES = {
     "unfused3d_f32": "generic.hip",
     "convT1d_bf16": "convT1d_bf16.hip",
     "avgpool3d_bf16": "avgpool3d.hip",
+    "fused3d_general": "generic.hip",
+    "avgpool3d_nopad": "generic.hip",
+    "convT1d_general": "generic.hip",
 }
 
 
@@ -71,7 +74,11 @@ KERNELS = [
     ("fused3d_bf16_kernel", "fused3d_bf16", "fused3d_bf16.hip", 75931904),
     ("convT1d_bf16_kernel", "convT1d_bf16", "convT1d_bf16.hip", 1342296064),
     ("convT3d_s2_kernel", "convT3d_s2", "convT3d_s2.hip", 1033106496),
+    # the k=3 general pool is the count_include_pad=False op; k=2 the unfused chain's pool
+    ("avgpool3d_generic_kernel<3", "avgpool3d_nopad", "generic.hip", 9663676416),
     ("avgpool3d_generic_kernel", "avgpool3d_generic", "generic.hip", 1126023168),
+    ("fused3d_generic_kernel", "fused3d_general", "generic.hip", 159388864),
+    ("convT1d_generic_kernel", "convT1d_general", "generic.hip", 2684477696),
 ]
 
 
@@ -286,6 +293,75 @@ def make_ops(names, dev):
 
         ops.append(Op("unfused3d_f32", run, nbytes(x, w, y, y, out), 2 * y.numel() * 3 * 27 // 8,
                       "hbm", HBM_PEAK_GBS, [wl.description + ", unfused"], sample))
+
+    if "fused3d_general" in names:
+        # the general gather kernel on the full-size fused workload with a
+        # conv bias and output_padding=1 (pre-pool 32x64x64, pooled 16x32x32)
+        wl = synth.WORKLOADS["c2"]
+        log(f"inputs: {wl.description}, conv bias, output_padding=1")
+        t = synth.make_inputs(wl, conv_bias=True)
+        x, w, cb, b = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "conv_bias", "bias"))
+        out = torch.empty((128, 16, 16, 32, 32), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, cb=cb, b=b, out=out):
+            ct.ct_convT3d_scale_pool_bias(x, w, cb, b, 0.5, 1.0, 2, 1, 1, out=out)
+
+        def sample(t=t):
+            import oracle
+            n = 8
+            t0 = time.perf_counter()
+            oracle.convT3d_scale_pool_bias(t["x"][:n], t["w"], t["conv_bias"], t["bias"], 0.5, 1.0, 2, 1, 1)
+            return time.perf_counter() - t0, n / 128.0, f"{n} of 128 batch items"
+
+        # every weight once per pooled output and input channel: 27 products per ci
+        ops.append(Op("fused3d_general", run, nbytes(x, w, cb, b, out), 2 * out.numel() * 3 * 27,
+                      "hbm", HBM_PEAK_GBS, [wl.description + ", conv bias, output_padding=1"], sample))
+
+    if "avgpool3d_nopad" in names:
+        # the large pooling shape with count_include_pad=False (divisor = taps
+        # inside the input), on the general pool kernel
+        wl = synth.WORKLOADS["c3"]
+        log(f"inputs: {wl.description}, count_include_pad=False (8.6 GB host generation)")
+        xh = synth.normal(wl.seed, synth.STREAM_X, wl.x_shape)
+        x = torch.from_numpy(xh).to(dev)
+        out = torch.empty((16, 32, 64, 64, 128), dtype=torch.float32, device=dev)
+
+        def run(x=x, out=out):
+            ct.ct_avgpool3d(x, 3, 2, 1, False, out=out)
+
+        def sample(xh=xh):
+            import oracle
+            k = 64
+            t0 = time.perf_counter()
+            oracle.avgpool3d(xh.reshape(512, 128, 128, 256)[:k][:, None], 3, 2, 1, False)
+            return time.perf_counter() - t0, k / 512.0, f"{k} of 512 (n,c) slices"
+
+        ops.append(Op("avgpool3d_nopad", run, nbytes(x, out), 27 * out.numel(), "hbm",
+                      HBM_PEAK_GBS, [wl.description + ", count_include_pad=False"], sample))
+
+    if "convT1d_general" in names:
+        # the 1D conv shapes with stride 2, pad 1, output_padding 1 and a bias,
+        # on the general gather kernel (L_out = 2L + 10)
+        wl = synth.WORKLOADS["c4"]
+        log(f"inputs: {wl.description}, stride 2, pad 1, output_padding 1, bias")
+        t = synth.make_inputs(wl, conv_bias=True)
+        x, w, bg = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "bias"))
+        out = torch.empty((32, 64, 262154), dtype=torch.float32, device=dev)
+
+        def run(x=x, w=w, bg=bg, out=out):
+            ct.ct_convT1d(x, w, bg, 2, 1, 3, 1, out=out)
+
+        def sample(t=t):
+            import oracle
+            n = 4
+            t0 = time.perf_counter()
+            oracle.convT1d(t["x"][:n], t["w"], t["bias"], 2, 1, 3, 1)
+            return time.perf_counter() - t0, n / 32.0, f"{n} of 32 batch items"
+
+        # every input-weight product once, as at stride 1
+        flops = 2 * 32 * 32 * 131072 * 5 * 64
+        ops.append(Op("convT1d_general", run, nbytes(x, w, bg, out), flops, "hbm", HBM_PEAK_GBS,
+                      [wl.description + ", stride 2, pad 1, output_padding 1, bias"], sample))
 
     if "copy" in names:
         n = 1 << 28                      # 1 GiB of fp32
