@@ -239,6 +239,12 @@ CONV1D_GENERAL = [
     (1, 2, 2, 1, 1, 1, 0, 1, 0, True, "f32"),
     (1, 8, 9, 50, 6, 4, 3, 2, 3, True, "bf16"),
     (1, 300, 8, 20, 3, 1, 0, 1, 0, False, "f32"),    # weights beyond the LDS tile
+    # the residue-ordered gather (stride <= 8, L_out >= 64*stride)
+    (2, 6, 7, 200, 5, 2, 1, 3, 1, True, "f32"),      # the stride-2 shape of the general bench op
+    (1, 5, 3, 300, 4, 3, 2, 2, 2, False, "f32"),
+    (2, 3, 4, 150, 3, 8, 0, 1, 7, True, "bf16"),     # largest stride it takes
+    (1, 33, 65, 520, 5, 2, 1, 3, 1, True, "f32"),    # a partial group of four channels
+    (1, 4, 3, 100, 2, 1, 5, 1, 0, False, "f32"),     # pad 5: early taps fall before the input
     # the bf16 matrix-core kernel (Cin 32, K 5, dilation 3, L % 8 == 0)
     (2, 32, 64, 296, 5, 1, 0, 3, 0, False, "bf16"),
     (1, 32, 70, 520, 5, 1, 0, 3, 0, True, "bf16"),    # two output-channel groups, ragged

@@ -97,21 +97,21 @@ __device__ __forceinline__ Taps axis_taps(int o, int k, const Div &ds, int pad, 
 // infinity behaviour are those of the plain loop.  Used by the 1D kernel (32 channels at
 // its large shape: 60 -> 35 ms); the 3D gather keeps the plain loop, which
 // was faster with 3 channels (1.4 against 2.2 ms).
-template <typename T>
+template <int G = 4, typename T>
 __device__ __forceinline__ float dot_ci(const T *__restrict__ xn, int64_t xs, int64_t xo,
                                         const T *__restrict__ w, int64_t ws, int64_t wo, int Cin,
                                         float acc)
 {
-    for (int ci = 0; ci < Cin; ci += 4) {
-        float xv[4], wv[4];
+    for (int ci = 0; ci < Cin; ci += G) {
+        float xv[G], wv[G];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < G; ++u) {
             const int c = min(ci + u, Cin - 1);
             xv[u] = ld(xn, c * xs + xo);
             wv[u] = ld(w, c * ws + wo);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < G; ++u) {
             const float f = __builtin_fmaf(xv[u], wv[u], acc);
             acc = ci + u < Cin ? f : acc;
         }
@@ -278,6 +278,52 @@ void convT1d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
     }
 }
 
+// The same sum with a wave per (n, co, residue r of o modulo the stride, 64
+// consecutive j): lane l computes o = r + s*(64*chunk + l).  Every lane of a
+// wave then has the same valid taps (o + p - dil*k is a multiple of s for all
+// of them or for none), and a tap's inputs are consecutive across the lanes.
+// Consecutive waves take the next output channel, then the next residue, so
+// the input segment of a chunk is reused from cache by all of them (ordered
+// by output position instead, the large 1D shape re-read its input 67 times
+// from HBM).  Sums run in the same order as in convT1d_generic_kernel.
+template <typename T, typename I>
+__global__ __launch_bounds__(kThreads)
+void convT1d_residue_kernel(const T *__restrict__ x, const T *__restrict__ w,
+                            const float *__restrict__ bias, int Cin, int L, int Cout, int K,
+                            int p, int dil, int s, int Lo, Div dCout, Div dS, Div dChunks,
+                            I total, float *__restrict__ y)
+{
+    // the grid stride is a multiple of 64, so e >> 6 is the same on every
+    // lane of a wave and (co, r, chunk) are wave-uniform
+    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+        const int lane = (int)(e & 63);
+        I t = e >> 6;
+        const int co = __builtin_amdgcn_readfirstlane(peel(t, dCout));
+        const int r = __builtin_amdgcn_readfirstlane(peel(t, dS));
+        const int ch = __builtin_amdgcn_readfirstlane(peel(t, dChunks));
+        const int j = ch * 64 + lane;
+        const int64_t o = (int64_t)r + (int64_t)s * j;
+        const T *xn = x + (int64_t)t * Cin * L;
+        float acc = 0.0f;
+        for (int kk = 0; kk < K; ++kk) {
+            // input (o + p - dil*kk) / s = c0/s + j when c0 = r + p - dil*kk
+            // is a multiple of s (the same for every lane; |c0| < 2^31 is
+            // checked by the launcher)
+            const int c0 = r + p - dil * kk;
+            if (c0 % s != 0) continue;
+            const int64_t i = (int64_t)(c0 / s) + j;
+            if (i >= 0 && i < L) {
+                // 16 channels' loads in flight per wait when there are enough
+                if (Cin >= 16)
+                    acc = dot_ci<16>(xn, (int64_t)L, i, w, (int64_t)Cout * K, (int64_t)co * K + kk, Cin, acc);
+                else
+                    acc = dot_ci<4>(xn, (int64_t)L, i, w, (int64_t)Cout * K, (int64_t)co * K + kk, Cin, acc);
+            }
+        }
+        if (o < Lo) y[((int64_t)t * Cout + co) * Lo + o] = acc + (bias ? bias[co] : 0.0f);
+    }
+}
+
 // One thread per output up to 2^16 workgroups (256 per CU); larger problems
 // loop over the grid.
 unsigned grid_for(int64_t total)
@@ -376,9 +422,29 @@ hipError_t launch_convT1d_generic(const void *x, const void *w, bool bf16, const
                                   int p, int dil, int op, float *y, hipStream_t stream)
 {
     const int64_t Lo = (L - 1) * s - 2 * p + (int64_t)dil * (K - 1) + op + 1;
+    const dim3 block(kThreads);
+    if (s <= 8 && Lo >= 64 * (int64_t)s && p + (int64_t)dil * (K - 1) + s < (int64_t(1) << 31)) {
+        // waves over (n, chunk of 64 j, residue, co); at most 63 idle lanes
+        // per (n, residue, co) with these bounds
+        const int64_t chunks = ((Lo + s - 1) / s + 63) / 64;
+        const int64_t total = N * chunks * s * Cout * 64;
+        const Div dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s),
+                  dK = make_div((uint32_t)chunks);
+        const dim3 grid(grid_for(total));
+#define CT_C1R(T, I)                                                                            \
+        hipLaunchKernelGGL((convT1d_residue_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
+                           (const T *)w, bias, (int)Cin, (int)L, (int)Cout, K, p, dil, s, (int)Lo,  \
+                           dC, dS, dK, (I)total, y)
+        if (bf16 && small_index(total)) CT_C1R(uint16_t, uint32_t);
+        else if (bf16) CT_C1R(uint16_t, uint64_t);
+        else if (small_index(total)) CT_C1R(float, uint32_t);
+        else CT_C1R(float, uint64_t);
+#undef CT_C1R
+        return hipGetLastError();
+    }
     const int64_t total = N * Cout * Lo;
     const Div dL = make_div((uint32_t)Lo), dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s);
-    const dim3 grid(grid_for(total)), block(kThreads);
+    const dim3 grid(grid_for(total));
 #define CT_C1D(T, I)                                                                            \
     hipLaunchKernelGGL((convT1d_generic_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
                        (const T *)w, bias, (int)Cin, (int)L, (int)Cout, K, p, dil, dL, dC, dS,  \
