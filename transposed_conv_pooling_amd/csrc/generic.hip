@@ -294,8 +294,12 @@ void convT1d_residue_kernel(const T *__restrict__ x, const T *__restrict__ w,
                             I total, float *__restrict__ y)
 {
     // the grid stride is a multiple of 64, so e >> 6 is the same on every
-    // lane of a wave and (co, r, chunk) are wave-uniform
-    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+    // lane of a wave and (co, r, chunk) are wave-uniform.  Neighbouring
+    // logical workgroups (the next output channels over the same inputs, and
+    // the other residues of the same output lines) run on one XCD, so they
+    // share its L2.
+    const I b = (I)xcd_remap(blockIdx.x, gridDim.x);
+    for (I e = b * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
         const int lane = (int)(e & 63);
         I t = e >> 6;
         const int co = __builtin_amdgcn_readfirstlane(peel(t, dCout));
