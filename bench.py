@@ -50,7 +50,7 @@ OP_SOURCES = {
     "convT1d_bf16": "convT1d_bf16.hip",
     "avgpool3d_bf16": "avgpool3d.hip",
     "fused3d_general": "generic.hip",
-    "avgpool3d_nopad": "generic.hip",
+    "avgpool3d_nopad": "avgpool3d.hip",
     "convT1d_general": "generic.hip",
 }
 
@@ -69,13 +69,15 @@ KERNELS = [
     # bf16 pool kernels first: the fp32 ones share the name prefix
     ("avgpool3d_k3s2p1_vec_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
     ("avgpool3d_k3s2p1_elem_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
+    # count_include_pad=False instantiations (last template argument false)
+    ("avgpool3d_k3s2p1_vec_kernel<float, false, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
+    ("avgpool3d_k3s2p1_vec_kernel<float, true, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
+    ("avgpool3d_k3s2p1_elem_kernel<float, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
     ("avgpool3d_k3s2p1_", "avgpool3d", "avgpool3d.hip", 9663676416),
     ("convT1d_f32", "convT1d", "convT1d_f32.hip", 1610752000),
     ("fused3d_bf16_kernel", "fused3d_bf16", "fused3d_bf16.hip", 75931904),
     ("convT1d_bf16_kernel", "convT1d_bf16", "convT1d_bf16.hip", 1342296064),
     ("convT3d_s2_kernel", "convT3d_s2", "convT3d_s2.hip", 1033106496),
-    # the k=3 general pool is the count_include_pad=False op; k=2 the unfused chain's pool
-    ("avgpool3d_generic_kernel<3", "avgpool3d_nopad", "generic.hip", 9663676416),
     ("avgpool3d_generic_kernel", "avgpool3d_generic", "generic.hip", 1126023168),
     ("fused3d_generic_kernel", "fused3d_general", "generic.hip", 159388864),
     ("convT1d_generic_kernel", "convT1d_general", "generic.hip", 2684477696),
@@ -320,7 +322,7 @@ def make_ops(names, dev):
 
     if "avgpool3d_nopad" in names:
         # the large pooling shape with count_include_pad=False (divisor = taps
-        # inside the input), on the general pool kernel
+        # inside the input), on the streaming kernel
         wl = synth.WORKLOADS["c3"]
         log(f"inputs: {wl.description}, count_include_pad=False (8.6 GB host generation)")
         xh = synth.normal(wl.seed, synth.STREAM_X, wl.x_shape)

@@ -163,7 +163,7 @@ CT_API ct_status ct_convT3d(const void *x, int x_dtype,
  *   out  [N, C, Do, Ho, Wo] fp32, Do = ct_pool_out_len(D, k, stride, pad)
  *
  * Geometry: k >= 1, stride >= 0 (0 = k), 0 <= pad <= k/2 (PyTorch's rule),
- * floor mode.  k = 3, stride 2, pad 1 with count_include_pad = 1 runs on a
+ * floor mode.  k = 3, stride 2, pad 1 (either count_include_pad) runs on a
  * separable streaming kernel (per-slice size below 2^31 elements); anything
  * else on a general gather kernel (one thread per output; lengths and
  * stride up to 2^30, k up to 1024, else CT_EUNSUPPORTED).
@@ -183,7 +183,7 @@ CT_API ct_status ct_avgpool3d(const float *x,
  *   out  [N, C, Do, Ho, Wo] bf16 bit patterns, sizes as for ct_avgpool3d
  *
  * Geometry, limits, ownership and errors as for ct_avgpool3d (sizes in
- * bf16 elements).  k = 3, stride 2, pad 1 with count_include_pad = 1 runs on
+ * bf16 elements).  k = 3, stride 2, pad 1 (either count_include_pad) runs on
  * the same separable streaming kernels (the vector one when W % 4 == 0, x is
  * 8-byte and out 4-byte aligned); anything else on the general gather kernel.
  */

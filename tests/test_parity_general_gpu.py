@@ -188,6 +188,12 @@ POOL_GENERAL = [
     ((1, 1, 3, 4, 5), 1, 1, 0, True),       # identity
     ((1, 1, 1, 1, 1), 1, 2, 0, False),
     ((1, 2, 2, 3, 300), 2, 1, 1, False),
+    # the page's window with the valid-tap divisor on the streaming kernels
+    ((2, 5, 9, 10, 16), 3, 2, 1, False),     # vector kernel, one column chunk
+    ((1, 2, 5, 6, 260), 3, 2, 1, False),     # two column chunks
+    ((40, 8, 12, 10, 16), 3, 2, 1, False),   # 320 slices in plane ranges (bf16 staggered starts)
+    ((1, 1, 1, 1, 4), 3, 2, 1, False),       # length-1 axes: one valid tap
+    ((1, 1, 2, 131, 8), 3, 2, 1, False),     # two row groups
 ]
 
 

@@ -1,6 +1,7 @@
 // avgpool3d.hip - AvgPool3d(k3, s2, p1) with zero padding counted in the
-// divisor (27), streaming each input byte from HBM about once.  fp32 data,
-// or bf16 data with fp32 sums and each mean rounded to the nearest bf16.
+// divisor (27) or, with count_include_pad off, a divisor of the window taps
+// inside the input, streaming each input byte from HBM about once.  fp32
+// data, or bf16 data with fp32 sums and each mean rounded to the nearest bf16.
 //
 // Method ([p46] "Kimi-K2.6 l1_p46"): out[d,h,w] is the sum of
 // x[2d-1+kd, 2h-1+kh, 2w-1+kw] over kd,kh,kw < 3, out-of-range taps reading 0,
@@ -114,6 +115,10 @@ template <> struct Elem<uint16_t> {
     static __device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((unsigned)v << 16); }
 };
 
+// Taps of output q's window 2q-1 .. 2q+1 inside an axis of length n (1..3);
+// with count_include_pad=False the mean divides by the product over the axes.
+__device__ __forceinline__ int taps3(int q, int n) { return 3 - (q == 0) - (2 * q + 1 >= n); }
+
 // ------------------------------------------------------------ vector kernel --
 constexpr int kVWaves = 16;                  // waves per workgroup
 constexpr int kVThreads = 64 * kVWaves;
@@ -213,7 +218,7 @@ __device__ __forceinline__ void get_vsums(v2f (*T)[64], const E *xs, int p, int 
 
 // Grid: one workgroup per (slice, plane chunk of td output planes, column
 // chunk, row group of kGroupRows output rows), row groups fastest.
-template <typename E, bool kWide>
+template <typename E, bool kWide, bool kIncl>
 __global__ __launch_bounds__(kVThreads)
 void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
                                  int D, int H, int W, int Do, int Ho, int Wo,
@@ -244,6 +249,8 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
     E *os = out + sl * (int64_t)Do * Ho * Wo;
     const int obytes = Ho * Wo * ES;
     const float inv27 = 1.0f / 27.0f;
+    // (count_include_pad=False) valid taps along W of the lane's two outputs
+    const int cw0 = taps3(wo, W), cw1 = taps3(wo + 1, W);
 
     // Output planes [pa, pb): input planes go through T[0], T[1], T[0], ...
     // starting with plane 2*pa-1
@@ -286,7 +293,14 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
 #pragma unroll
             for (int i = 0; i < kTH; ++i) {
                 const int h = h0 + i;
-                const v2f o = (acc[i] + v[i]) * inv27;
+                v2f o;
+                if constexpr (kIncl) {
+                    o = (acc[i] + v[i]) * inv27;
+                } else {
+                    const int cdh = taps3(d, D) * taps3(h, H);
+                    const v2f sum = acc[i] + v[i];
+                    o = v2f{sum.x * (1.0f / (float)(cdh * cw0)), sum.y * (1.0f / (float)(cdh * cw1))};
+                }
                 // the row (wave-uniform) in the scalar offset, the lane's
                 // column in the vector offset; a row past the plane takes the
                 // zero-size resource
@@ -353,7 +367,7 @@ __device__ __forceinline__ void plane_sums_elem(const E *__restrict__ xs, int pl
     }
 }
 
-template <typename E>
+template <typename E, bool kIncl>
 __global__ __launch_bounds__(kEThreads)
 void avgpool3d_k3s2p1_elem_kernel(const E *__restrict__ x, E *__restrict__ out,
                                   int D, int H, int W, int Do, int Ho, int Wo,
@@ -387,8 +401,14 @@ void avgpool3d_k3s2p1_elem_kernel(const E *__restrict__ x, E *__restrict__ out,
 #pragma unroll
         for (int i = 0; i < kTH; ++i) {
             const int h = h0 + i;
-            const float o0 = (carry[i][0] + va[i][0] + vb[i][0]) * inv27;
-            const float o1 = (carry[i][1] + va[i][1] + vb[i][1]) * inv27;
+            const float s0 = carry[i][0] + va[i][0] + vb[i][0];
+            const float s1 = carry[i][1] + va[i][1] + vb[i][1];
+            float o0 = s0 * inv27, o1 = s1 * inv27;
+            if constexpr (!kIncl) {
+                const int cdh = taps3(d, D) * taps3(h, H);
+                o0 = s0 * (1.0f / (float)(cdh * taps3(wo, W)));
+                o1 = s1 * (1.0f / (float)(cdh * taps3(wo + 1, W)));
+            }
             if (h < Ho) {
                 E *orow = os + ((int64_t)d * Ho + h) * Wo;
                 if (wo < Wo) __builtin_nontemporal_store(Elem<E>::from_f32(o0), orow + wo);
@@ -403,7 +423,7 @@ void avgpool3d_k3s2p1_elem_kernel(const E *__restrict__ x, E *__restrict__ out,
 }  // namespace
 
 namespace {
-template <typename E>
+template <typename E, bool kIncl>
 hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W, E *out,
                          hipStream_t stream)
 {
@@ -430,18 +450,18 @@ hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W
         dchunks = (Do + td - 1) / td;
         const int64_t nwg = base * dchunks;
         if (wchunks > 1)
-            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true>), dim3((unsigned)nwg),
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true, kIncl>), dim3((unsigned)nwg),
                                dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do,
                                Ho, Wo, hgroups, (int)dchunks, wchunks, td);
         else
-            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, false>), dim3((unsigned)nwg),
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, false, kIncl>), dim3((unsigned)nwg),
                                dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do,
                                Ho, Wo, hgroups, (int)dchunks, wchunks, td);
     } else {
         const int hgroups = (Ho + kEWaves * kTH - 1) / (kEWaves * kTH);
         const int dchunks = (Do + kETD - 1) / kETD;
         const int64_t nwg = NC * (int64_t)hgroups * dchunks * wchunks;
-        hipLaunchKernelGGL((avgpool3d_k3s2p1_elem_kernel<E>), dim3((unsigned)nwg),
+        hipLaunchKernelGGL((avgpool3d_k3s2p1_elem_kernel<E, kIncl>), dim3((unsigned)nwg),
                            dim3(kEThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do, Ho,
                            Wo, hgroups, dchunks, wchunks);
     }
@@ -449,14 +469,18 @@ hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W
 }
 }  // namespace
 
-hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, int64_t NC, int64_t D, int64_t H,
-                                   int64_t W, void *out, hipStream_t stream)
+hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, bool include_pad, int64_t NC,
+                                   int64_t D, int64_t H, int64_t W, void *out, hipStream_t stream)
 {
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const float *xf = static_cast<const float *>(x);
+    uint16_t *ob = static_cast<uint16_t *>(out);
+    float *of = static_cast<float *>(out);
     if (bf16)
-        return launch_k3s2p1(static_cast<const uint16_t *>(x), NC, D, H, W,
-                             static_cast<uint16_t *>(out), stream);
-    return launch_k3s2p1(static_cast<const float *>(x), NC, D, H, W, static_cast<float *>(out),
-                         stream);
+        return include_pad ? launch_k3s2p1<uint16_t, true>(xb, NC, D, H, W, ob, stream)
+                           : launch_k3s2p1<uint16_t, false>(xb, NC, D, H, W, ob, stream);
+    return include_pad ? launch_k3s2p1<float, true>(xf, NC, D, H, W, of, stream)
+                       : launch_k3s2p1<float, false>(xf, NC, D, H, W, of, stream);
 }
 
 }  // namespace ct

@@ -298,7 +298,8 @@ ct_status avgpool3d_impl(const char *fn, const void *x, bool bf16, int64_t N, in
         return fail(CT_EINVAL, "%s: tensor size overflows", fn);
     if (overlap(out, no, x, nx)) return fail(CT_EINVAL, "%s: out overlaps x", fn);
 
-    bool fast = k == 3 && s == 2 && pad == 1 && count_include_pad == 1;
+    // k3 s2 p1 takes the streaming kernels with either divisor
+    bool fast = k == 3 && s == 2 && pad == 1;
     if (fast) {
         const int64_t hgroups = (o[1] + 15) / 16, dchunks = (o[0] + 15) / 16,
                       wchunks = (o[2] + 127) / 128;
@@ -307,7 +308,8 @@ ct_status avgpool3d_impl(const char *fn, const void *x, bool bf16, int64_t N, in
     }
     hipError_t e;
     if (fast) {
-        e = ct::launch_avgpool3d_k3s2p1(x, bf16, N * C, D, H, W, out, (hipStream_t)stream);
+        e = ct::launch_avgpool3d_k3s2p1(x, bf16, count_include_pad == 1, N * C, D, H, W, out,
+                                        (hipStream_t)stream);
     } else {
         if (D > kGenericMaxLen || H > kGenericMaxLen || W > kGenericMaxLen || k > kGenericMaxTap ||
             s > kGenericMaxLen)

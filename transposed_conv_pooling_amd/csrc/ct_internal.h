@@ -25,10 +25,11 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w,
                                int64_t D, int64_t H, int64_t W, int64_t Cout,
                                float *out, hipStream_t stream);
 
-// AvgPool3d(k3, s2, p1), divisor 27, over NC independent [D][H][W] slices;
-// x and out fp32, or (bf16 = true) bf16 bit patterns with fp32 sums.
-hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, int64_t NC, int64_t D,
-                                   int64_t H, int64_t W, void *out,
+// AvgPool3d(k3, s2, p1) over NC independent [D][H][W] slices, divisor 27
+// (include_pad) or the number of window taps inside the slice; x and out
+// fp32, or (bf16 = true) bf16 bit patterns with fp32 sums.
+hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, bool include_pad, int64_t NC,
+                                   int64_t D, int64_t H, int64_t W, void *out,
                                    hipStream_t stream);
 
 // ConvTranspose1d, stride 1, pad 0, any K and dilation, fp32.
