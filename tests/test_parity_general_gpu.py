@@ -74,6 +74,8 @@ FUSED_GENERAL = [
     (1, 130, 4, 3, 3, 5, 3, 2, 1, 0, 2, 2, "f32"),    # page geometry, Cin beyond the MFMA path
     (1, 40, 8, 3, 4, 8, 3, 2, 1, 0, 2, 2, "bf16"),    # page geometry, bf16 Cin > 32
     (2, 3, 16, 4, 5, 13, 3, 2, 1, 0, 2, 2, "bf16"),   # page geometry, bf16 W % 8 != 0
+    (2, 3, 16, 9, 17, 33, 3, 2, 1, 1, 2, 2, "f32"),   # output_padding 1 on the effective-filter gather
+    (1, 40, 40, 3, 3, 4, 3, 2, 1, 1, 2, 2, "f32"),    # Cin*Cout > 1024: the plain gather
 ]
 
 

@@ -180,6 +180,89 @@ void fused3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
     }
 }
 
+// The page's geometry (k3, s2, p1, 2-pool) with any output padding, from the
+// effective filter ([p50], passage grouping the 27 weight terms by input
+// tap): a pooled voxel is sum_ci sum_{a,b,c} x[ci, d+a, h+b, w+c] *
+// Weff[ci, co, abc] / 8, where input offset 0 along an axis pairs with taps
+// {1, 2} and offset 1 with tap {0}.  Inputs past the far edge read 0, which
+// is all that output_padding = 1 changes.  Weff is formed once per workgroup
+// in LDS.  A thread takes one pooled voxel and a block of up to 16 output
+// channels: it loads each input channel's 8 taps once (together, from clamped
+// addresses, masking the ones past the edge with a select) and applies them
+// to every channel of the block.
+template <typename T, typename I>
+__global__ __launch_bounds__(kThreads)
+void fused3d_weff_kernel(const T *__restrict__ x, const T *__restrict__ w,
+                         const float *__restrict__ conv_bias, const float *__restrict__ bias,
+                         float s1, float s2, Geo3 g, int Dp, int Hp, int Wp, Div dWp, Div dHp,
+                         Div dDp, Div dCb, I total, float *__restrict__ out)
+{
+    extern __shared__ float weff[];            // [Cin][Cout][8], tap = 4a + 2b + c
+    const int nw = g.Cin * g.Cout * 8;
+    for (int e = threadIdx.x; e < nw; e += kThreads) {
+        const int tap = e & 7;
+        const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
+        const T *wk = w + (int64_t)(e >> 3) * 27;   // w[ci][co][3][3][3]
+        float sum = 0.0f;
+        for (int kd = a ? 0 : 1; kd <= (a ? 0 : 2); ++kd)
+            for (int kh = b ? 0 : 1; kh <= (b ? 0 : 2); ++kh)
+                for (int kw = c ? 0 : 1; kw <= (c ? 0 : 2); ++kw)
+                    sum += ld(wk, (kd * 3 + kh) * 3 + kw);
+        weff[e] = sum;
+    }
+    __syncthreads();
+    constexpr int kCB = 16;                    // output channels per thread
+    const int64_t HW = (int64_t)g.H * g.W, DHW = (int64_t)g.D * HW, xitem = (int64_t)g.Cin * DHW;
+    const int64_t pplane = (int64_t)Dp * Hp * Wp;
+    for (I e = (I)blockIdx.x * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
+        I t = e;
+        const int wp = peel(t, dWp), hp = peel(t, dHp), dp = peel(t, dDp), cb = peel(t, dCb);
+        const int co0 = cb * kCB;
+        const T *xc = x + (int64_t)t * xitem + dp * HW + (int64_t)hp * g.W + wp;
+        const bool vd = dp + 1 < g.D, vh = hp + 1 < g.H, vw = wp + 1 < g.W;
+        const int64_t od = vd ? HW : 0, oh = vh ? g.W : 0, ow = vw ? 1 : 0;
+        float S[kCB];
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) S[j] = 0.0f;
+        // input channels four at a time: all 32 tap loads go out before the fmas
+        for (int ci0 = 0; ci0 < g.Cin; ci0 += 4) {
+            float xv[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const T *xi = xc + min(ci0 + u, g.Cin - 1) * DHW;   // clamped: always valid
+#pragma unroll
+                for (int tp = 0; tp < 8; ++tp) {
+                    const int a = tp >> 2, b = (tp >> 1) & 1, c = tp & 1;
+                    const float v = ld(xi, (a ? od : 0) + (b ? oh : 0) + (c ? ow : 0));
+                    xv[u][tp] = ((a && !vd) || (b && !vh) || (c && !vw)) ? 0.0f : v;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (ci0 + u >= g.Cin) break;              // same for every lane
+                // channels past Cout read the block's first channel (never stored)
+                const float *wrow = weff + (int64_t)(ci0 + u) * g.Cout * 8;
+#pragma unroll
+                for (int j = 0; j < kCB; ++j) {
+                    const float *wf = wrow + (co0 + j < g.Cout ? co0 + j : co0) * 8;
+#pragma unroll
+                    for (int tp = 0; tp < 8; ++tp) S[j] = __builtin_fmaf(xv[u][tp], wf[tp], S[j]);
+                }
+            }
+        }
+        float *ob = out + ((int64_t)t * g.Cout + co0) * pplane + ((int64_t)dp * Hp + hp) * Wp + wp;
+#pragma unroll
+        for (int j = 0; j < kCB; ++j) {
+            if (co0 + j < g.Cout) {
+                float v = S[j] * 0.125f;
+                v = (v + (conv_bias ? conv_bias[co0 + j] : 0.0f)) * s1;
+                v = (v + (bias ? bias[co0 + j] : 0.0f)) * s2;
+                ob[(int64_t)j * pplane] = v;
+            }
+        }
+    }
+}
+
 template <typename T, typename I>
 __global__ __launch_bounds__(kThreads)
 void convT3d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
@@ -357,6 +440,24 @@ hipError_t launch_fused3d_generic(const void *x, const void *w, bool bf16,
     const Div dW = make_div((uint32_t)Wp), dH = make_div((uint32_t)Hp), dD = make_div((uint32_t)Dp),
               dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s);
     const dim3 grid(grid_for(total)), block(kThreads);
+    if (k == 3 && s == 2 && p == 1 && pk == 2 && ps == 2 && Cin * Cout <= 1024) {
+        const size_t lds = (size_t)Cin * Cout * 8 * sizeof(float);   // <= 32 KB
+        // one thread per (n, channel block of 16, pooled voxel)
+        const int64_t cblocks = (Cout + 15) / 16;
+        const int64_t vtotal = N * cblocks * Dp * Hp * Wp;
+        const Div dB = make_div((uint32_t)cblocks);
+        const dim3 vgrid(grid_for(vtotal));
+#define CT_WEFF(T, I)                                                                           \
+        hipLaunchKernelGGL((fused3d_weff_kernel<T, I>), vgrid, block, lds, stream, (const T *)x,    \
+                           (const T *)w, conv_bias, bias, s1, s2, g, (int)Dp, (int)Hp, (int)Wp,     \
+                           dW, dH, dD, dB, (I)vtotal, out)
+        if (bf16 && small_index(vtotal)) CT_WEFF(uint16_t, uint32_t);
+        else if (bf16) CT_WEFF(uint16_t, uint64_t);
+        else if (small_index(vtotal)) CT_WEFF(float, uint32_t);
+        else CT_WEFF(float, uint64_t);
+#undef CT_WEFF
+        return hipGetLastError();
+    }
 #define CT_FUSED(T, I)                                                                          \
     hipLaunchKernelGGL((fused3d_generic_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
                        (const T *)w, conv_bias, bias, s1, s2, inv, g, dW, dH, dD, dC, dS,       \
