@@ -80,6 +80,7 @@ KERNELS = [
     ("convT3d_s2_kernel", "convT3d_s2", "convT3d_s2.hip", 1033106496),
     ("avgpool3d_generic_kernel", "avgpool3d_generic", "generic.hip", 1126023168),
     ("fused3d_generic_kernel", "fused3d_general", "generic.hip", 159388864),
+    ("fused3d_weff_kernel", "fused3d_general", "generic.hip", 159388864),
     ("convT1d_generic_kernel", "convT1d_general", "generic.hip", 2684477696),
     ("convT1d_residue_kernel", "convT1d_general", "generic.hip", 2684477696),
 ]
