@@ -101,7 +101,7 @@ CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pa
  * Geometry: any k >= 1, stride >= 1, pad >= 0, 0 <= out_pad < stride
  * (PyTorch's rule at dilation 1), pool_k >= 1, pool_s >= 1 (0 = pool_k);
  * (x_dtype, w_dtype) = (CT_F32, CT_F32) or (CT_BF16, CT_BF16); accumulation
- * and output are fp32.  Two implementations:
+ * and output are fp32.  Three implementations:
  *   - k = 3, stride = 2, pad = 1, out_pad = 0, pool 2/2 (the page's
  *     geometry): matrix-core kernels that contract the 8 input taps of a
  *     pooled voxel with the grouped (summed) filter.  fp32 for Cin <= 128;
@@ -109,6 +109,10 @@ CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pa
  *     aligned.  The bf16 kernel represents the summed filter as a bf16
  *     hi + lo pair, so its result matches an fp32 computation on the same
  *     bf16 inputs to ~2^-17 relative per term.
+ *   - the same conv and pool geometry with out_pad 0 or 1 otherwise (e.g.
+ *     out_pad = 1, fp32 Cin > 128, bf16 shapes the matrix-core kernel does
+ *     not take), when Cin * Cout <= 1024: the same effective-filter sum on
+ *     the vector ALUs, taps past the far edge reading 0.
  *   - anything else: a general gather kernel on the vector ALUs (one thread
  *     per pooled voxel summing the pool window of transposed-convolution
  *     values), fp32 arithmetic on the (exactly widened) inputs.
