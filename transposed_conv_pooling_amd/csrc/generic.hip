@@ -94,9 +94,9 @@ __device__ __forceinline__ Taps axis_taps(int o, int k, const Div &ds, int pad, 
 // group are issued before its fmas (a loop over a run-time count would wait
 // on each pair), from clamped addresses that are always valid; a clamped
 // duplicate's fma result is discarded by a select, so the sum and its NaN /
-// infinity behaviour are those of the plain loop.  Used by the 1D kernel (32 channels at
-// its large shape: 60 -> 35 ms); the 3D gather keeps the plain loop, which
-// was faster with 3 channels (1.4 against 2.2 ms).
+// infinity behaviour are those of the plain loop.  Used by the position-ordered 1D
+// kernel; the 3D gather keeps the plain loop, which was faster with 3
+// channels (1.4 against 2.2 ms).
 template <int G = 4, typename T>
 __device__ __forceinline__ float dot_ci(const T *__restrict__ xn, int64_t xs, int64_t xo,
                                         const T *__restrict__ w, int64_t ws, int64_t wo, int Cin,
@@ -361,37 +361,49 @@ void convT1d_generic_kernel(const T *__restrict__ x, const T *__restrict__ w,
     }
 }
 
-// The same sum with a wave per (n, co, residue r of o modulo the stride, 64
-// consecutive j): lane l computes o = r + s*(64*chunk + l).  Every lane of a
-// wave then has the same valid taps (o + p - dil*k is a multiple of s for all
-// of them or for none), and a tap's inputs are consecutive across the lanes.
-// Consecutive waves take the next output channel, then the next residue, so
-// the input segment of a chunk is reused from cache by all of them (ordered
-// by output position instead, the large 1D shape re-read its input 67 times
-// from HBM).  Sums run in the same order as in convT1d_generic_kernel.
+// The same sum with a wave per (n, block of 16 output channels, residue r of
+// o modulo the stride, 64 consecutive j): lane l computes o = r + s*(64*chunk
+// + l) for the block's channels.  Every lane of a wave then has the same valid
+// taps (o + p - dil*k is a multiple of s for all of them or for none), a tap's
+// inputs are consecutive across the lanes, and each input load feeds 16
+// channels.  The weights are staged once per workgroup in LDS as
+// [ci][k][co], so a wave reads the same entries on every lane.  Consecutive
+// waves take the next channel block, then the next residue, and the workgroup
+// order is XCD-aware, so the input segment of a chunk is reused from one L2
+// (ordered by output position instead, the large 1D shape re-read its input
+// 67 times from HBM).  Sums run in the same order as in
+// convT1d_generic_kernel.
 template <typename T, typename I>
 __global__ __launch_bounds__(kThreads)
 void convT1d_residue_kernel(const T *__restrict__ x, const T *__restrict__ w,
                             const float *__restrict__ bias, int Cin, int L, int Cout, int K,
-                            int p, int dil, int s, int Lo, Div dCout, Div dS, Div dChunks,
+                            int p, int dil, int s, int Lo, Div dCb, Div dS, Div dChunks,
                             I total, float *__restrict__ y)
 {
+    constexpr int kCB = 16;
+    extern __shared__ float wl[];              // [Cin][K][Cout]
+    for (int e = threadIdx.x; e < Cin * K * Cout; e += kThreads) {
+        const int co = e % Cout, ck = e / Cout;            // ck = ci*K + k
+        const int ci = ck / K, kk = ck - ci * K;
+        wl[e] = ld(w, ((int64_t)ci * Cout + co) * K + kk);
+    }
+    __syncthreads();
     // the grid stride is a multiple of 64, so e >> 6 is the same on every
-    // lane of a wave and (co, r, chunk) are wave-uniform.  Neighbouring
-    // logical workgroups (the next output channels over the same inputs, and
-    // the other residues of the same output lines) run on one XCD, so they
-    // share its L2.
+    // lane of a wave and (block, r, chunk) are wave-uniform
     const I b = (I)xcd_remap(blockIdx.x, gridDim.x);
     for (I e = b * kThreads + threadIdx.x; e < total; e += (I)gridDim.x * kThreads) {
         const int lane = (int)(e & 63);
         I t = e >> 6;
-        const int co = __builtin_amdgcn_readfirstlane(peel(t, dCout));
+        const int cb = __builtin_amdgcn_readfirstlane(peel(t, dCb));
         const int r = __builtin_amdgcn_readfirstlane(peel(t, dS));
         const int ch = __builtin_amdgcn_readfirstlane(peel(t, dChunks));
+        const int co0 = cb * kCB;
         const int j = ch * 64 + lane;
         const int64_t o = (int64_t)r + (int64_t)s * j;
         const T *xn = x + (int64_t)t * Cin * L;
-        float acc = 0.0f;
+        float acc[kCB];
+#pragma unroll
+        for (int q = 0; q < kCB; ++q) acc[q] = 0.0f;
         for (int kk = 0; kk < K; ++kk) {
             // input (o + p - dil*kk) / s = c0/s + j when c0 = r + p - dil*kk
             // is a multiple of s (the same for every lane; |c0| < 2^31 is
@@ -399,15 +411,29 @@ void convT1d_residue_kernel(const T *__restrict__ x, const T *__restrict__ w,
             const int c0 = r + p - dil * kk;
             if (c0 % s != 0) continue;
             const int64_t i = (int64_t)(c0 / s) + j;
-            if (i >= 0 && i < L) {
-                // 16 channels' loads in flight per wait when there are enough
-                if (Cin >= 16)
-                    acc = dot_ci<16>(xn, (int64_t)L, i, w, (int64_t)Cout * K, (int64_t)co * K + kk, Cin, acc);
-                else
-                    acc = dot_ci<4>(xn, (int64_t)L, i, w, (int64_t)Cout * K, (int64_t)co * K + kk, Cin, acc);
+            if (i < 0 || i >= L) continue;
+            // eight channels' loads per wait
+            for (int ci0 = 0; ci0 < Cin; ci0 += 8) {
+                float xv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) xv[u] = ld(xn, (int64_t)min(ci0 + u, Cin - 1) * L + i);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (ci0 + u >= Cin) break;             // same for every lane
+                    // channels past Cout read the block's first channel (never stored)
+                    const float *wr = wl + ((ci0 + u) * K + kk) * Cout;
+#pragma unroll
+                    for (int q = 0; q < kCB; ++q)
+                        acc[q] = __builtin_fmaf(xv[u], wr[co0 + q < Cout ? co0 + q : co0], acc[q]);
+                }
             }
         }
-        if (o < Lo) y[((int64_t)t * Cout + co) * Lo + o] = acc + (bias ? bias[co] : 0.0f);
+        if (o < Lo) {
+            float *yo = y + ((int64_t)t * Cout + co0) * Lo + o;
+#pragma unroll
+            for (int q = 0; q < kCB; ++q)
+                if (co0 + q < Cout) yo[(int64_t)q * Lo] = acc[q] + (bias ? bias[co0 + q] : 0.0f);
+        }
     }
 }
 
@@ -528,18 +554,21 @@ hipError_t launch_convT1d_generic(const void *x, const void *w, bool bf16, const
 {
     const int64_t Lo = (L - 1) * s - 2 * p + (int64_t)dil * (K - 1) + op + 1;
     const dim3 block(kThreads);
-    if (s <= 8 && Lo >= 64 * (int64_t)s && p + (int64_t)dil * (K - 1) + s < (int64_t(1) << 31)) {
-        // waves over (n, chunk of 64 j, residue, co); at most 63 idle lanes
-        // per (n, residue, co) with these bounds
+    const size_t wbytes = (size_t)Cin * K * Cout * sizeof(float);
+    if (s <= 8 && Lo >= 64 * (int64_t)s && p + (int64_t)dil * (K - 1) + s < (int64_t(1) << 31) &&
+        wbytes <= 48 * 1024) {
+        // waves over (n, chunk of 64 j, residue, block of 16 channels); at
+        // most 63 idle lanes per (n, residue, block) with these bounds
         const int64_t chunks = ((Lo + s - 1) / s + 63) / 64;
-        const int64_t total = N * chunks * s * Cout * 64;
-        const Div dC = make_div((uint32_t)Cout), dS = make_div((uint32_t)s),
+        const int64_t cblocks = (Cout + 15) / 16;
+        const int64_t total = N * chunks * s * cblocks * 64;
+        const Div dB = make_div((uint32_t)cblocks), dS = make_div((uint32_t)s),
                   dK = make_div((uint32_t)chunks);
         const dim3 grid(grid_for(total));
 #define CT_C1R(T, I)                                                                            \
-        hipLaunchKernelGGL((convT1d_residue_kernel<T, I>), grid, block, 0, stream, (const T *)x,    \
-                           (const T *)w, bias, (int)Cin, (int)L, (int)Cout, K, p, dil, s, (int)Lo,  \
-                           dC, dS, dK, (I)total, y)
+        hipLaunchKernelGGL((convT1d_residue_kernel<T, I>), grid, block, wbytes, stream,            \
+                           (const T *)x, (const T *)w, bias, (int)Cin, (int)L, (int)Cout, K, p,    \
+                           dil, s, (int)Lo, dB, dS, dK, (I)total, y)
         if (bf16 && small_index(total)) CT_C1R(uint16_t, uint32_t);
         else if (bf16) CT_C1R(uint16_t, uint64_t);
         else if (small_index(total)) CT_C1R(float, uint32_t);
