@@ -101,3 +101,21 @@ def test_more_than_one_gpu_exits_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "exactly one GPU" in r.stdout + r.stderr
+
+
+def test_every_traced_kernel_maps_to_an_op():
+    """Each kernel named in the committed kernel-trace summaries resolves to an
+    op, a source file and its algorithmic bytes (a renamed or new kernel that
+    the table misses would drop out of the traffic and roofline figures)."""
+    import re
+    names = set()
+    for f in ("bench_kernel_trace.md", "extra_ops_kernel_trace.md"):
+        text = open(os.path.join(bench.ROOT, "profiles", f)).read()
+        names |= set(re.findall(r"\(`(ct::[^`]+)`\)", text))
+    assert names, "no kernel names found in the trace summaries"
+    for n in sorted(names):
+        key = bench.kernel_key(n)
+        assert key is not None, n
+        op, src, nbytes = key
+        assert op and nbytes > 0 and os.path.exists(
+            os.path.join(bench.ROOT, "transposed_conv_pooling_amd", "csrc", src)), (n, key)
