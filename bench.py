@@ -14,6 +14,13 @@ Prints ONE JSON line: value = algorithmic HBM bytes of a step / step time
 most time (timed live with HIP events on the launch stream), and the CPU oracle
 timed on a bounded sample of the same workloads.
 
+Every op is cold by construction: it cycles through enough copies of its
+input and output buffers (at least 4, more than 512 MB in all) that no call
+finds them in the 256 MB Infinity Cache; `ms_warm` repeats one buffer set.
+Beside the 8 TB/s peak, each op's GB/s is also given as a fraction of a plain
+1 GiB device copy measured in the same run (`copy_GB_s`).  The small fused
+workload [2,3,8,16,16] is timed per call (launch-bound) outside the step.
+
   python bench.py [--steps K] [--warmup W] [--ops a,b] [--no-cpu-baseline]
   python bench.py --ops copy        # plain 1 GiB device copy (counter calibration)
   python bench.py --ops fused3d_f32,unfused3d_f32   # fusion vs materialising the
@@ -21,6 +28,8 @@ timed on a bounded sample of the same workloads.
   python bench.py --summarize-trace DIR              # rocprofv3 --kernel-trace CSVs -> table
   python bench.py --summarize-counters FETCH WRITE   # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
                                     # CSVs -> table + profiles/traffic.json
+  python bench.py --summarize-pmc DIR [DIR ...]      # any rocprofv3 --pmc CSVs -> table +
+                                    # profiles/counters.json (MFMA busy, VALU/SALU per MFMA)
 """
 from __future__ import annotations
 
@@ -114,12 +123,39 @@ def measured_traffic(op):
 
 
 # ---------------------------------------------------------------- workloads --
+COLD_BYTES = 512 << 20     # twice the 256 MB Infinity Cache
+
+
+def rotation_count(set_bytes):
+    """Buffer sets an op cycles through so that no call finds its inputs or
+    outputs left in the 256 MB Infinity Cache by an earlier call: at least 4
+    sets and more than 512 MB in all, or one set when a single set is larger."""
+    if set_bytes > COLD_BYTES:
+        return 1
+    return max(4, COLD_BYTES // set_bytes + 1)
+
+
 class Op:
-    def __init__(self, name, run, alg_bytes, flops, bound, peak, inputs, oracle_sample):
-        self.name, self.run, self.alg_bytes, self.flops = name, run, alg_bytes, flops
+    """One operation of the step.  call(bufs) launches it on one buffer set;
+    run() launches it on the next set in rotation (cold by construction),
+    run_warm() always on the first set (inputs and outputs cache-resident
+    when they fit)."""
+
+    def __init__(self, name, call, sets, alg_bytes, flops, bound, peak, inputs, oracle_sample):
+        self.name, self.call, self.sets = name, call, sets
+        self.alg_bytes, self.flops = alg_bytes, flops
         self.bound, self.peak = bound, peak
         self.inputs = inputs
         self.oracle_sample = oracle_sample    # () -> (seconds, fraction of the op)
+        self._i = 0
+
+    def run(self):
+        bufs = self.sets[self._i % len(self.sets)]
+        self._i += 1
+        self.call(*bufs)
+
+    def run_warm(self):
+        self.call(*self.sets[0])
         # arithmetic type of the products: the bf16 contractions multiply bf16
         # operands on the matrix cores (fp32 accumulation); every other op,
         # bf16 pooling included, computes in fp32
@@ -142,6 +178,13 @@ def make_ops(names, dev):
     def nbytes(*ts):
         return int(sum(t.numel() * t.element_size() for t in ts))
 
+    def rotate(*ts):
+        """Buffer sets [(t0, t1, ...)]: the given tensors first, then copies
+        (inputs) or fresh allocations (outputs share shapes) up to the
+        rotation count of their total size."""
+        n = rotation_count(nbytes(*ts))
+        return [tuple(ts)] + [tuple(t.clone() for t in ts) for _ in range(n - 1)]
+
     if "fused3d_f32" in names:
         wl = synth.WORKLOADS["c2"]
         log(f"inputs: {wl.description}")
@@ -149,7 +192,7 @@ def make_ops(names, dev):
         x, w, b = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "bias"))
         out = torch.empty((128, 16, 15, 31, 31), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, b=b, out=out):
+        def call(x, out, w=w, b=b):
             ct.ct_convT3d_scale_pool_bias(x, w, None, b, 0.5, 1.0, out=out)
 
         def sample(t=t):
@@ -158,7 +201,7 @@ def make_ops(names, dev):
             oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
             return time.perf_counter() - t0, 1.0, "all 128 batch items"
 
-        ops.append(Op("fused3d_f32", run, nbytes(x, w, b, out),
+        ops.append(Op("fused3d_f32", call, rotate(x, out), nbytes(x, w, b, out),
                       2 * out.numel() * 3 * 8, "hbm", HBM_PEAK_GBS,
                       [wl.description], sample))
 
@@ -169,7 +212,7 @@ def make_ops(names, dev):
         x = torch.from_numpy(xh).to(dev)
         out = torch.empty((16, 32, 64, 64, 128), dtype=torch.float32, device=dev)
 
-        def run(x=x, out=out):
+        def call(x, out):
             ct.ct_avgpool3d(x, 3, 2, 1, True, out=out)
 
         def sample(xh=xh):
@@ -179,7 +222,7 @@ def make_ops(names, dev):
             oracle.avgpool3d(xh.reshape(512, 128, 128, 256)[:k], 3, 2, 1, True)
             return time.perf_counter() - t0, k / 512.0, f"{k} of 512 (n,c) slices"
 
-        ops.append(Op("avgpool3d", run, nbytes(x, out), 27 * out.numel(), "hbm",
+        ops.append(Op("avgpool3d", call, rotate(x, out), nbytes(x, out), 27 * out.numel(), "hbm",
                       HBM_PEAK_GBS, [wl.description], sample))
 
     if "convT1d" in names:
@@ -189,7 +232,7 @@ def make_ops(names, dev):
         x, w = torch.from_numpy(t["x"]).to(dev), torch.from_numpy(t["w"]).to(dev)
         out = torch.empty((32, 64, 131084), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, out=out):
+        def call(x, out, w=w):
             ct.ct_convT1d(x, w, None, 1, 0, 3, out=out)
 
         def sample(t=t):
@@ -200,7 +243,7 @@ def make_ops(names, dev):
             return time.perf_counter() - t0, n / 32.0, f"{n} of 32 batch items"
 
         flops = 2 * 32 * 32 * 131072 * 5 * 64
-        ops.append(Op("convT1d", run, nbytes(x, w, out), flops, "mfma",
+        ops.append(Op("convT1d", call, rotate(x, out), nbytes(x, w, out), flops, "mfma",
                       MFMA_F32_PEAK_TFLOPS, [wl.description], sample))
 
     if "fused3d_bf16" in names:
@@ -212,7 +255,7 @@ def make_ops(names, dev):
         b = torch.from_numpy(t["bias"]).to(dev)
         out = torch.empty((16, 64, 15, 31, 31), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, b=b, out=out):
+        def call(x, out, w=w, b=b):
             ct.ct_convT3d_scale_pool_bias(x, w, None, b, 0.5, 1.0, out=out)
 
         def sample(t=t):
@@ -221,7 +264,7 @@ def make_ops(names, dev):
             oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
             return time.perf_counter() - t0, 1.0, "all 16 batch items"
 
-        ops.append(Op("fused3d_bf16", run, nbytes(x, w, b, out), 2 * out.numel() * 32 * 8,
+        ops.append(Op("fused3d_bf16", call, rotate(x, out), nbytes(x, w, b, out), 2 * out.numel() * 32 * 8,
                       "hbm", HBM_PEAK_GBS, [wl.description], sample))
 
     if "convT1d_bf16" in names:
@@ -234,7 +277,7 @@ def make_ops(names, dev):
         w = torch.from_numpy(wb.reshape(t["w"].shape).view(np.int16)).to(dev).view(torch.bfloat16)
         out = torch.empty((32, 64, 131084), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, out=out):
+        def call(x, out, w=w):
             ct.ct_convT1d(x, w, None, 1, 0, 3, out=out)
 
         def sample(xb=xb, wb=wb, shape=t["x"].shape, wshape=t["w"].shape):
@@ -247,7 +290,7 @@ def make_ops(names, dev):
             return time.perf_counter() - t0, n / 32.0, f"{n} of 32 batch items"
 
         flops = 2 * 32 * 32 * 131072 * 5 * 64
-        ops.append(Op("convT1d_bf16", run, nbytes(x, w, out), flops, "hbm", HBM_PEAK_GBS,
+        ops.append(Op("convT1d_bf16", call, rotate(x, out), nbytes(x, w, out), flops, "hbm", HBM_PEAK_GBS,
                       [bf16_label(wl)], sample))
 
     if "avgpool3d_bf16" in names:
@@ -258,7 +301,7 @@ def make_ops(names, dev):
         x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
         out = torch.empty((16, 32, 64, 64, 128), dtype=torch.bfloat16, device=dev)
 
-        def run(x=x, out=out):
+        def call(x, out):
             ct.ct_avgpool3d(x, 3, 2, 1, True, out=out)
 
         def sample(xb=xb):
@@ -269,7 +312,7 @@ def make_ops(names, dev):
             oracle.avgpool3d(xf, 3, 2, 1, True)
             return time.perf_counter() - t0, k / 512.0, f"{k} of 512 (n,c) slices"
 
-        ops.append(Op("avgpool3d_bf16", run, nbytes(x, out), 27 * out.numel(), "hbm",
+        ops.append(Op("avgpool3d_bf16", call, rotate(x, out), nbytes(x, out), 27 * out.numel(), "hbm",
                       HBM_PEAK_GBS, [bf16_label(wl)], sample))
 
     if "unfused3d_f32" in names:
@@ -284,7 +327,7 @@ def make_ops(names, dev):
         y = torch.empty((128, 16, 31, 63, 63), dtype=torch.float32, device=dev)
         out = torch.empty((128, 16, 15, 31, 31), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, y=y, out=out):
+        def call(x, y, out, w=w):
             ct.ct_convT3d(x, w, None, 2, 1, 0, out=y)
             ct.ct_avgpool3d(y, 2, 2, 0, True, out=out)
 
@@ -295,7 +338,7 @@ def make_ops(names, dev):
             oracle.avgpool3d(oracle.convT3d(t["x"][:n], t["w"], None, 2, 1, 0), 2, 2, 0, True)
             return time.perf_counter() - t0, n / 128.0, f"{n} of 128 batch items"
 
-        ops.append(Op("unfused3d_f32", run, nbytes(x, w, y, y, out), 2 * y.numel() * 3 * 27 // 8,
+        ops.append(Op("unfused3d_f32", call, rotate(x, y, out), nbytes(x, w, y, y, out), 2 * y.numel() * 3 * 27 // 8,
                       "hbm", HBM_PEAK_GBS, [wl.description + ", unfused"], sample))
 
     if "fused3d_general" in names:
@@ -307,7 +350,7 @@ def make_ops(names, dev):
         x, w, cb, b = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "conv_bias", "bias"))
         out = torch.empty((128, 16, 16, 32, 32), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, cb=cb, b=b, out=out):
+        def call(x, out, w=w, cb=cb, b=b):
             ct.ct_convT3d_scale_pool_bias(x, w, cb, b, 0.5, 1.0, 2, 1, 1, out=out)
 
         def sample(t=t):
@@ -318,7 +361,7 @@ def make_ops(names, dev):
             return time.perf_counter() - t0, n / 128.0, f"{n} of 128 batch items"
 
         # every weight once per pooled output and input channel: 27 products per ci
-        ops.append(Op("fused3d_general", run, nbytes(x, w, cb, b, out), 2 * out.numel() * 3 * 27,
+        ops.append(Op("fused3d_general", call, rotate(x, out), nbytes(x, w, cb, b, out), 2 * out.numel() * 3 * 27,
                       "hbm", HBM_PEAK_GBS, [wl.description + ", conv bias, output_padding=1"], sample))
 
     if "avgpool3d_nopad" in names:
@@ -330,7 +373,7 @@ def make_ops(names, dev):
         x = torch.from_numpy(xh).to(dev)
         out = torch.empty((16, 32, 64, 64, 128), dtype=torch.float32, device=dev)
 
-        def run(x=x, out=out):
+        def call(x, out):
             ct.ct_avgpool3d(x, 3, 2, 1, False, out=out)
 
         def sample(xh=xh):
@@ -340,7 +383,7 @@ def make_ops(names, dev):
             oracle.avgpool3d(xh.reshape(512, 128, 128, 256)[:k][:, None], 3, 2, 1, False)
             return time.perf_counter() - t0, k / 512.0, f"{k} of 512 (n,c) slices"
 
-        ops.append(Op("avgpool3d_nopad", run, nbytes(x, out), 27 * out.numel(), "hbm",
+        ops.append(Op("avgpool3d_nopad", call, rotate(x, out), nbytes(x, out), 27 * out.numel(), "hbm",
                       HBM_PEAK_GBS, [wl.description + ", count_include_pad=False"], sample))
 
     if "convT1d_general" in names:
@@ -352,7 +395,7 @@ def make_ops(names, dev):
         x, w, bg = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "bias"))
         out = torch.empty((32, 64, 262154), dtype=torch.float32, device=dev)
 
-        def run(x=x, w=w, bg=bg, out=out):
+        def call(x, out, w=w, bg=bg):
             ct.ct_convT1d(x, w, bg, 2, 1, 3, 1, out=out)
 
         def sample(t=t):
@@ -364,7 +407,7 @@ def make_ops(names, dev):
 
         # every input-weight product once, as at stride 1
         flops = 2 * 32 * 32 * 131072 * 5 * 64
-        ops.append(Op("convT1d_general", run, nbytes(x, w, bg, out), flops, "hbm", HBM_PEAK_GBS,
+        ops.append(Op("convT1d_general", call, rotate(x, out), nbytes(x, w, bg, out), flops, "hbm", HBM_PEAK_GBS,
                       [wl.description + ", stride 2, pad 1, output_padding 1, bias"], sample))
 
     if "copy" in names:
@@ -372,10 +415,10 @@ def make_ops(names, dev):
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
 
-        def run(src=src, dst=dst):
+        def call(src, dst):
             dst.copy_(src)
 
-        ops.append(Op("copy", run, 2 * 4 * n, 0, "hbm", HBM_PEAK_GBS,
+        ops.append(Op("copy", call, [(src, dst)], 2 * 4 * n, 0, "hbm", HBM_PEAK_GBS,
                       ["device copy 1 GiB fp32"], None))
     return ops
 
@@ -457,17 +500,160 @@ def summarize_counters(fetch_path, write_path, dst=None):
     print(f"\nwrote {os.path.relpath(dst, ROOT)}")
 
 
+def summarize_pmc(paths, dst=None):
+    """Mean per dispatch of every counter in `rocprofv3 --pmc` runs (one or
+    more output folders), per kernel of the bench, with figures derived from
+    them where present: MfmaUtil (percent of SIMD cycles the matrix pipe was
+    busy, rocprofv3's derived counter), VALU and SALU instructions per MFMA
+    instruction, and GRBM_GUI_ACTIVE cycles per microsecond of dispatch.
+    Writes profiles/counters.json (with a hash of each kernel's source) and
+    prints a markdown table."""
+    vals, durs = {}, {}
+    for path in paths:
+        for r in _csv_rows(path):
+            if "Counter_Name" not in r:
+                continue
+            k = kernel_key(r["Kernel_Name"])
+            if not k:
+                continue
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            durs.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(d)
+    out = {}
+    names = sorted({c for v in vals.values() for c in v})
+    print("| kernel | " + " | ".join(names) + " | VALU / MFMA | SALU / MFMA | GRBM cycles / us |")
+    print("|---|" + "---|" * (len(names) + 3))
+    for (key, src, alg), cs in sorted(vals.items(), key=lambda kv: kv[0][0]):
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        rec = {"counters": mean, "source": src, "source_sha256_16": source_hash(None, src)}
+        mf = mean.get("SQ_INSTS_MFMA")
+        if mf:
+            if "SQ_INSTS_VALU" in mean:
+                rec["valu_per_mfma"] = mean["SQ_INSTS_VALU"] / mf
+            if "SQ_INSTS_SALU" in mean:
+                rec["salu_per_mfma"] = mean["SQ_INSTS_SALU"] / mf
+        if "GRBM_GUI_ACTIVE" in mean:
+            dd = durs[(key, src, alg)]["GRBM_GUI_ACTIVE"]
+            rec["grbm_cycles_per_us"] = mean["GRBM_GUI_ACTIVE"] / (sum(dd) / len(dd))
+        out[key + " | " + src] = rec
+        cells = [f"{mean[c]:.4g}" if c in mean else "-" for c in names]
+        extra = [f"{rec[f]:.3g}" if f in rec else "-" for f in
+                 ("valu_per_mfma", "salu_per_mfma", "grbm_cycles_per_us")]
+        print(f"| {key} (`{src}`) | " + " | ".join(cells + extra) + " |")
+    dst = dst or os.path.join(ROOT, "profiles", "counters.json")
+    json.dump(out, open(dst, "w"), indent=1)
+    print(f"\nwrote {os.path.relpath(dst, ROOT)}")
+
+
+def time_copy(torch, dev, stream, reps=20):
+    """GB/s (read + write bytes) of a plain 1 GiB fp32 device copy."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * 4 * n / ms / 1e6, 1)
+
+
+def time_small_fused(torch, dev, stream, reps=200):
+    """Per-call time of the small fused workload [2,3,8,16,16] -> [2,16,7,15,15]
+    (cache-resident, launch-bound): GPU time per call from HIP events around
+    `reps` back-to-back calls, and host time per call (enqueue rate, the
+    same calls timed with a wall clock up to the last enqueue)."""
+    import synth
+    import transposed_conv_pooling_amd as ct
+    wl = synth.WORKLOADS["c1"]
+    t = synth.make_inputs(wl)
+    x, w, bias = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "bias"))
+    out = torch.empty((2, 16, 7, 15, 15), dtype=torch.float32, device=dev)
+    for _ in range(10):
+        ct.ct_convT3d_scale_pool_bias(x, w, None, bias, 0.5, 1.0, out=out)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(reps):
+        ct.ct_convT3d_scale_pool_bias(x, w, None, bias, 0.5, 1.0, out=out)
+    h1 = time.perf_counter()
+    b.record(stream)
+    torch.cuda.synchronize()
+    single = []
+    for _ in range(20):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ct.ct_convT3d_scale_pool_bias(x, w, None, bias, 0.5, 1.0, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        single.append(e0.elapsed_time(e1) * 1e3)
+    alg = int(x.numel() * 4 + w.numel() * 4 + bias.numel() * 4 + out.numel() * 4)
+    return {"workload": wl.description, "us_per_call_back_to_back": round(a.elapsed_time(b) * 1e3 / reps, 2),
+            "us_per_call_isolated": round(float(np.median(single)), 2),
+            "host_us_per_call": round((h1 - h0) * 1e6 / reps, 2), "alg_bytes": alg}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_one_thread():
+    """The oracle on one host thread: the small fused workload (mean of 10
+    runs) and the full-size fp32 fused workload (one run), in ms."""
+    import ctypes
+
+    import oracle
+    import synth
+    gomp = ctypes.CDLL("libgomp.so.1")
+    before = oracle.num_threads()
+    gomp.omp_set_num_threads(1)
+    try:
+        res = {}
+        t = synth.make_inputs(synth.WORKLOADS["c1"])
+        t0 = time.perf_counter()
+        for _ in range(10):
+            oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
+        res["fused_small_c1"] = round((time.perf_counter() - t0) * 100, 3)
+        t = synth.make_inputs(synth.WORKLOADS["c2"])
+        t0 = time.perf_counter()
+        oracle.convT3d_scale_pool_bias(t["x"], t["w"], None, t["bias"], 0.5, 1.0)
+        res["fused3d_f32_c2"] = round((time.perf_counter() - t0) * 1e3, 1)
+        res["threads"] = oracle.num_threads()
+    finally:
+        gomp.omp_set_num_threads(before)
+    return res
+
+
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         return summarize_trace(sys.argv[2])
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
         return summarize_counters(sys.argv[2], sys.argv[3])
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        return summarize_pmc(sys.argv[2:])
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--ops", default="fused3d_f32,avgpool3d,convT1d,fused3d_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the per-call timing of the small fused workload")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -511,6 +697,30 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     gpu_ms_per_step = step_start.elapsed_time(step_end) / args.steps
 
+    # warm: the same op back to back on its first buffer set (the fused
+    # workloads then run out of the Infinity Cache); reported beside the
+    # cold, rotated figure that the step uses
+    warm = {}
+    for op in ops:
+        if len(op.sets) == 1:
+            continue
+        evs = []
+        for _ in range(max(args.steps, 10)):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            op.run_warm()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        warm[op.name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # a plain 1 GiB device copy: the bandwidth this machine's HBM gives a simple
+    # stream, the second denominator beside the 8 TB/s peak
+    copy_gbs = None
+    if "copy" not in names:
+        copy_gbs = time_copy(torch, dev, stream)
+
     per_op = {}
     total_bytes = 0
     for op in ops:
@@ -519,6 +729,11 @@ def main():
         d = {"ms": round(avg, 5), "ms_min": round(float(np.min(ms)), 5),
              "alg_bytes": op.alg_bytes, "GB_s": round(op.alg_bytes / avg / 1e6, 1),
              "hbm_frac": round(op.alg_bytes / avg / 1e6 / HBM_PEAK_GBS, 4)}
+        if copy_gbs:
+            d["copy_frac"] = round(op.alg_bytes / avg / 1e6 / copy_gbs, 4)
+        if op.name in warm:
+            d["ms_warm"] = round(warm[op.name], 5)
+        d["buffer_sets"] = len(op.sets)
         if op.flops:
             d["GFLOP_s"] = round(op.flops / avg / 1e6, 1)
         if op.name == "convT1d":
@@ -527,6 +742,10 @@ def main():
         per_op[op.name] = d
         if op.name != "copy":
             total_bytes += op.alg_bytes
+    if "copy" in per_op:
+        copy_gbs = per_op["copy"]["GB_s"]
+
+    small = time_small_fused(torch, dev, stream) if not args.no_small else None
 
     dom = max(ops, key=lambda o: per_op[o.name]["ms"])
     dms = per_op[dom.name]["ms"]
@@ -558,7 +777,9 @@ def main():
             samples.append(f"{op.name}: {what}, {reps} passes in {total:.1f} s")
         cpu = {"value": round(total_bytes / est_s / 1e9, 4), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": "; ".join(samples) + f"; full step extrapolated to {est_s:.1f} s"}
+               "cpu_model": cpu_model(),
+               "sample": "; ".join(samples) + f"; full step extrapolated to {est_s:.1f} s",
+               "one_thread_ms": oracle_one_thread()}
 
     value = total_bytes / (ms_per_step / 1e3) / 1e9 if total_bytes else per_op["copy"]["GB_s"]
     line = {
@@ -579,6 +800,8 @@ def main():
                    "ops": {o.name: o.inputs[0] for o in ops}},
         "ops": per_op,
         "roofline": roof,
+        "copy_GB_s": copy_gbs,
+        "small_fused_c1": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

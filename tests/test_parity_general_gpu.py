@@ -280,23 +280,6 @@ def test_conv1d_general(dev, case):
     assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, str(case))
 
 
-def test_conv1d_bf16_c4_shape_sampled(dev):
-    """The [32,32,131072] workload with bf16 inputs and weights on the bf16
-    matrix-core kernel; batch items 0, 13 and 31 recomputed by the oracle from
-    the same bf16 values, plus finiteness."""
-    wl = synth.WORKLOADS["c4"]
-    log(wl.description + " in bf16")
-    t = synth.make_inputs(wl)
-    xb, wb = bf16_round(t["x"]), bf16_round(t["w"])
-    out = torch.full((32, 64, 131084), float("nan"), dtype=torch.float32, device=dev)
-    ct.ct_convT1d(to_dev(xb, dev, "bf16"), to_dev(wb, dev, "bf16"), None, 1, 0, 3, out=out)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(out).all())
-    for n in (0, 13, 31):
-        ref = oracle.convT1d(xb[n:n + 1], wb, None, 1, 0, 3)
-        assert_close(out[n:n + 1].cpu().numpy(), ref, F32_TOL, f"c4 bf16 n={n}")
-
-
 def test_conv1d_bf16_misaligned_x_takes_general_path(dev):
     x = bf16_round(synth.normal(91, 0, (1, 32, 64)))
     w = bf16_round(synth.uniform(91, 1, (32, 8, 5), -0.1, 0.1))
@@ -306,57 +289,3 @@ def test_conv1d_bf16_misaligned_x_takes_general_path(dev):
     ct.ct_convT1d(buf[1:].view(1, 32, 64), to_dev(w, dev, "bf16"), None, 1, 0, 3, out=out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), oracle.convT1d(x, w, None, 1, 0, 3), F32_TOL, "misaligned")
-
-
-# ------------------------------------------- general ops at full size ----
-# The general kernels in the launch configuration the bench times, checked on
-# whole batch items / slices the oracle recomputes.
-
-def test_fused_general_full_size_sampled(dev):
-    """[128,3,16,32,32] with a conv bias and output_padding=1 ([128,16,16,32,32]
-    out, effective-filter gather): batch items 0, 77 and 127 against the oracle."""
-    wl = synth.WORKLOADS["c2"]
-    t = synth.make_inputs(wl, conv_bias=True)
-    log(wl.description + ", conv bias, output_padding=1")
-    g = {k: torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "conv_bias", "bias")}
-    out = torch.full((128, 16, 16, 32, 32), float("nan"), dtype=torch.float32, device=dev)
-    ct.ct_convT3d_scale_pool_bias(g["x"], g["w"], g["conv_bias"], g["bias"], 0.5, 1.0, 2, 1, 1, out=out)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(out).all())
-    for n in (0, 77, 127):
-        ref = oracle.convT3d_scale_pool_bias(t["x"][n:n + 1], t["w"], t["conv_bias"], t["bias"],
-                                             0.5, 1.0, 2, 1, 1)
-        assert_close(out[n:n + 1].cpu().numpy(), ref, F32_TOL, f"fused general item {n}")
-
-
-def test_pool_nopad_full_size_sampled(dev):
-    """[16,32,128,128,256] with count_include_pad=False on the streaming kernel:
-    4 whole (n, c) slices against the oracle, plus global finiteness."""
-    wl = synth.WORKLOADS["c3"]
-    log(wl.description + ", count_include_pad=False")
-    x = synth.normal(wl.seed, synth.STREAM_X, wl.x_shape)
-    xg = torch.from_numpy(x).to(dev)
-    out = torch.full((16, 32, 64, 64, 128), float("nan"), dtype=torch.float32, device=dev)
-    ct.ct_avgpool3d(xg, 3, 2, 1, False, out=out)
-    torch.cuda.synchronize()
-    del xg
-    assert bool(torch.isfinite(out).all())
-    for (n, c) in [(0, 0), (5, 17), (10, 3), (15, 31)]:
-        ref = oracle.avgpool3d(x[n, c], 3, 2, 1, False)
-        assert_close(out[n, c].cpu().numpy(), ref, F32_TOL, f"nopad slice {(n, c)}")
-
-
-def test_conv1d_general_full_size_sampled(dev):
-    """[32,32,131072] at stride 2, pad 1, output_padding 1, dilation 3, with a
-    bias ([32,64,262154] out, residue-ordered gather): items 0, 19 and 31."""
-    wl = synth.WORKLOADS["c4"]
-    t = synth.make_inputs(wl, conv_bias=True)
-    log(wl.description + ", stride 2, pad 1, output_padding 1, bias")
-    x, w, b = (torch.from_numpy(t[k]).to(dev) for k in ("x", "w", "bias"))
-    out = torch.full((32, 64, 262154), float("nan"), dtype=torch.float32, device=dev)
-    ct.ct_convT1d(x, w, b, 2, 1, 3, 1, out=out)
-    torch.cuda.synchronize()
-    assert bool(torch.isfinite(out).all())
-    for n in (0, 19, 31):
-        ref = oracle.convT1d(t["x"][n:n + 1], t["w"], t["bias"], 2, 1, 3, 1)
-        assert_close(out[n:n + 1].cpu().numpy(), ref, F32_TOL, f"conv1d general item {n}")

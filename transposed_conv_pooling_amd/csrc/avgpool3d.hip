@@ -126,6 +126,11 @@ constexpr int kOwn = 2 * kTH;                // input rows a wave loads per plan
 constexpr int kGroupRows = kVWaves * kTH;    // output rows per workgroup
 constexpr int kGroupIn = 2 * kGroupRows;     // input rows per workgroup
 constexpr unsigned kOOB = 0x40000000u;       // past every buffer (planes < 2^30 bytes)
+// The kernel's row table (2 planes x kGroupIn rows x 64 lanes x 8 bytes =
+// 128 KiB of static LDS) leaves room for one workgroup per CU (160 KiB).
+constexpr int kVTableBytes = 2 * kGroupIn * 64 * 8;
+constexpr int kVPerCu = (160 * 1024) / kVTableBytes;
+static_assert(kVPerCu >= 1, "row table must fit the LDS");
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void *base, bool valid, int bytes)
 {
@@ -225,6 +230,7 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
                                  int hgroups, int dchunks, int wchunks, int td)
 {
     __shared__ v2f T[2][kGroupIn][64];   // row table, double-buffered by plane
+    static_assert(sizeof(T) == kVTableBytes, "row table size");
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int64_t t = xcd_remap(blockIdx.x, gridDim.x);
@@ -423,51 +429,77 @@ void avgpool3d_k3s2p1_elem_kernel(const E *__restrict__ x, E *__restrict__ out,
 }  // namespace
 
 namespace {
+// Launch shape of the streaming kernels for one call.
+struct PoolPlan {
+    bool vec;          // vector kernel (else the element kernel)
+    int Do, Ho, Wo, hgroups, wchunks, dchunks, td;
+    int64_t nwg;       // workgroups
+    int threads;       // work-items per workgroup
+};
+
+PoolPlan plan_k3s2p1(int es, const void *x, const void *out, int64_t NC, int64_t D, int64_t H,
+                     int64_t W)
+{
+    PoolPlan p;
+    p.Do = (int)((D - 1) / 2 + 1);
+    p.Ho = (int)((H - 1) / 2 + 1);
+    p.Wo = (int)((W - 1) / 2 + 1);
+    p.wchunks = (p.Wo + kTW - 1) / kTW;
+    // vector path: 4 elements per lane load, 2 per lane store, planes < 2^30 bytes
+    p.vec = (W % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) % (4 * es)) == 0) &&
+            ((reinterpret_cast<uintptr_t>(out) % (2 * es)) == 0) && H * W * es < (int64_t)kOOB;
+    if (p.vec) {
+        p.hgroups = (p.Ho + kGroupRows - 1) / kGroupRows;
+        // as few plane chunks as still give every CU as many workgroups as fit
+        // on it at once (one: the 128 KiB row table fills the LDS)
+        const int64_t base = NC * p.hgroups * p.wchunks;
+        const int64_t want = (int64_t)device_cus() * kVPerCu;
+        int64_t dchunks = (want + base - 1) / base;
+        if (dchunks > p.Do) dchunks = p.Do;
+        p.td = (int)((p.Do + dchunks - 1) / dchunks);
+        p.dchunks = (int)((p.Do + p.td - 1) / p.td);
+        p.nwg = base * p.dchunks;
+        p.threads = kVThreads;
+    } else {
+        p.hgroups = (p.Ho + kEWaves * kTH - 1) / (kEWaves * kTH);
+        p.dchunks = (p.Do + kETD - 1) / kETD;
+        p.td = kETD;
+        p.nwg = NC * (int64_t)p.hgroups * p.dchunks * p.wchunks;
+        p.threads = kEThreads;
+    }
+    return p;
+}
+
 template <typename E, bool kIncl>
 hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W, E *out,
                          hipStream_t stream)
 {
-    const int Do = (int)((D - 1) / 2 + 1);
-    const int Ho = (int)((H - 1) / 2 + 1);
-    const int Wo = (int)((W - 1) / 2 + 1);
-    const int wchunks = (Wo + kTW - 1) / kTW;
-    constexpr int ES = (int)sizeof(E);
-    // vector path: 4 elements per lane load, 2 per lane store, planes < 2^30 bytes
-    const bool vec = (W % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) % (4 * ES)) == 0) &&
-                     ((reinterpret_cast<uintptr_t>(out) % (2 * ES)) == 0) &&
-                     H * W * ES < (int64_t)kOOB;
-    if (vec) {
-        const int hgroups = (Ho + kGroupRows - 1) / kGroupRows;
-        // as few plane chunks as still give every CU two workgroups
-        int cus = 256, dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
-        const int64_t base = NC * hgroups * wchunks;
-        int64_t dchunks = (2 * (int64_t)cus + base - 1) / base;
-        if (dchunks > Do) dchunks = Do;
-        const int td = (int)((Do + dchunks - 1) / dchunks);
-        dchunks = (Do + td - 1) / td;
-        const int64_t nwg = base * dchunks;
-        if (wchunks > 1)
-            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true, kIncl>), dim3((unsigned)nwg),
-                               dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do,
-                               Ho, Wo, hgroups, (int)dchunks, wchunks, td);
+    const PoolPlan p = plan_k3s2p1((int)sizeof(E), x, out, NC, D, H, W);
+    if (p.nwg * p.threads > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
+    if (p.vec) {
+        if (p.wchunks > 1)
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true, kIncl>), dim3((unsigned)p.nwg),
+                               dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do,
+                               p.Ho, p.Wo, p.hgroups, p.dchunks, p.wchunks, p.td);
         else
-            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, false, kIncl>), dim3((unsigned)nwg),
-                               dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do,
-                               Ho, Wo, hgroups, (int)dchunks, wchunks, td);
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, false, kIncl>), dim3((unsigned)p.nwg),
+                               dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do,
+                               p.Ho, p.Wo, p.hgroups, p.dchunks, p.wchunks, p.td);
     } else {
-        const int hgroups = (Ho + kEWaves * kTH - 1) / (kEWaves * kTH);
-        const int dchunks = (Do + kETD - 1) / kETD;
-        const int64_t nwg = NC * (int64_t)hgroups * dchunks * wchunks;
-        hipLaunchKernelGGL((avgpool3d_k3s2p1_elem_kernel<E, kIncl>), dim3((unsigned)nwg),
-                           dim3(kEThreads), 0, stream, x, out, (int)D, (int)H, (int)W, Do, Ho,
-                           Wo, hgroups, dchunks, wchunks);
+        hipLaunchKernelGGL((avgpool3d_k3s2p1_elem_kernel<E, kIncl>), dim3((unsigned)p.nwg),
+                           dim3(kEThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do, p.Ho,
+                           p.Wo, p.hgroups, p.dchunks, p.wchunks);
     }
     return hipGetLastError();
 }
 }  // namespace
+
+bool avgpool3d_k3s2p1_fits(bool bf16, const void *x, const void *out, int64_t NC, int64_t D,
+                           int64_t H, int64_t W)
+{
+    const PoolPlan p = plan_k3s2p1(bf16 ? 2 : 4, x, out, NC, D, H, W);
+    return p.nwg * p.threads <= (int64_t)UINT32_MAX;
+}
 
 hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, bool include_pad, int64_t NC,
                                    int64_t D, int64_t H, int64_t W, void *out, hipStream_t stream)

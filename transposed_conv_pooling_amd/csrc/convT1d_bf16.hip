@@ -215,13 +215,7 @@ hipError_t launch_geo(const uint16_t *x, const uint16_t *w, const float *bias, i
     const int tiles_per_n = (int)((Lo + 28 + kTO - 1) / kTO);
     const int64_t ntiles = N * tiles_per_n;
     const void *fn = (const void *)convT1d_bf16_kernel<K, DIL, VEC_OUT>;
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
+    const int cus = device_cus(), per_cu = occupancy(fn, kThreads, 0);
     const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
     int64_t gx = (int64_t)cus * per_cu / gy;
     if (gx < 1) gx = 1;

@@ -380,15 +380,9 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
         typedef WaveGeom<32, 5, 3, kWaveNB, kWaveWW> G;
         const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW>;
         const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = allow_dynamic_lds(fn, lds);
         if (e != hipSuccess) return e;
-        int dev = 0, cus = 256, per_cu = 1;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, G::kThreads, lds) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
+        const int cus = device_cus(), per_cu = occupancy(fn, G::kThreads, lds);
         const int wtiles_per_n = (int)((Lo + G::kTW - 1) / G::kTW);
         const int64_t wtiles = N * wtiles_per_n;
         const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
@@ -400,13 +394,9 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
         return hipGetLastError();
     }
     const size_t lds = convT1d_f32_lds_bytes(Cin, K, dilation);
-    hipError_t e = hipFuncSetAttribute((const void *)convT1d_f32_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = allow_dynamic_lds((const void *)convT1d_f32_kernel, lds);
     if (e != hipSuccess) return e;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
+    const int cus = device_cus();
     const int per_cu = lds <= 80 * 1024 ? 2 : 1;
     int64_t gx = (int64_t)cus * per_cu;
     if (gx > ntiles) gx = ntiles;

@@ -211,9 +211,10 @@ ct_status ct_convT3d_scale_pool_bias(
             fast = fast && Cin <= 128;
         } else {
             const size_t lb = ct::fused3d_bf16_lds_bytes(Cin, W);
-            // (its buffer stores take 32-bit byte offsets within one batch item)
+            // (its buffer stores take 32-bit byte offsets within one batch item,
+            // and masked lanes store at 2^31 - 16, which must lie past the item)
             fast = fast && Cin <= 32 && W % 8 == 0 && aligned(x, 16) && lb != 0 && lb <= kLdsMax &&
-                   oitem <= kI32Max / 4;
+                   oitem * 4 < (int64_t(1) << 31) - 64;
         }
     }
     hipError_t e;
@@ -254,10 +255,11 @@ ct_status ct_convT3d(const void *x, int x_dtype, const void *w, int w_dtype, con
         return fail(CT_EINVAL, "%s: out overlaps an input", fn);
     if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "%s: x and w dtypes must match", fn);
     // The pages' k3 s2 p1 layer with few input channels runs on the parity
-    // kernel (grid of one thread per input voxel); the rest on the general one.
+    // kernel (one work-item per input voxel, a grid below the 2^32 work-items
+    // of one dispatch); the rest on the general one.
     int64_t nvox;
     const bool parity = k == 3 && stride == 2 && pad == 1 && Cin <= 8 &&
-                        prod({N, D, H, W}, &nvox) && nvox <= kI32Max * 64;
+                        prod({N, D, H, W}, &nvox) && nvox <= (int64_t)UINT32_MAX - 1024;
     hipError_t e;
     if (parity)
         e = ct::launch_convT3d_s2(x, w, x_dtype == CT_BF16, bias, N, Cin, D, H, W, Cout, out_pad,
@@ -298,14 +300,10 @@ ct_status avgpool3d_impl(const char *fn, const void *x, bool bf16, int64_t N, in
         return fail(CT_EINVAL, "%s: tensor size overflows", fn);
     if (overlap(out, no, x, nx)) return fail(CT_EINVAL, "%s: out overlaps x", fn);
 
-    // k3 s2 p1 takes the streaming kernels with either divisor
-    bool fast = k == 3 && s == 2 && pad == 1;
-    if (fast) {
-        const int64_t hgroups = (o[1] + 15) / 16, dchunks = (o[0] + 15) / 16,
-                      wchunks = (o[2] + 127) / 128;
-        int64_t nwg;
-        fast = slice <= kI32Max && prod({N, C, hgroups, dchunks, wchunks}, &nwg) && nwg <= kI32Max;
-    }
+    // k3 s2 p1 takes the streaming kernels with either divisor, as long as one
+    // slice is below 2^31 elements and the grid fits one dispatch
+    const bool fast = k == 3 && s == 2 && pad == 1 && slice <= kI32Max &&
+                      ct::avgpool3d_k3s2p1_fits(bf16, x, out, N * C, D, H, W);
     hipError_t e;
     if (fast) {
         e = ct::launch_avgpool3d_k3s2p1(x, bf16, count_include_pad == 1, N * C, D, H, W, out,

@@ -10,6 +10,16 @@
 
 namespace ct {
 
+// Per-device facts, queried once per device and cached (device.hip):
+// compute units of the current device; workgroups of `fn` that fit on one CU
+// with `threads` threads and `lds` bytes of dynamic LDS (at least 1); and
+// hipFuncSetAttribute(MaxDynamicSharedMemorySize) issued only when `lds`
+// exceeds what this device already granted `fn`.
+int current_device();
+int device_cus();
+int occupancy(const void *fn, int threads, size_t lds);
+hipError_t allow_dynamic_lds(const void *fn, size_t lds);
+
 // Fused ConvTranspose3d(k3, s2, p1) -> *s1 -> AvgPool3d(2) -> +bias -> *s2,
 // fp32 x and w.  Output [N, Cout, D-1, H-1, W-1].
 hipError_t launch_fused3d_f32(const float *x, const float *w,
@@ -31,6 +41,11 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w,
 hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, bool include_pad, int64_t NC,
                                    int64_t D, int64_t H, int64_t W, void *out,
                                    hipStream_t stream);
+// Whether that launch's grid (workgroups x work-items per workgroup) stays
+// within the 32-bit work-item count of one dispatch; the streaming kernels
+// have no grid-stride loop, so a larger call takes the general kernel.
+bool avgpool3d_k3s2p1_fits(bool bf16, const void *x, const void *out, int64_t NC, int64_t D,
+                           int64_t H, int64_t W);
 
 // ConvTranspose1d, stride 1, pad 0, any K and dilation, fp32.
 hipError_t launch_convT1d_f32(const float *x, const float *w,

@@ -461,10 +461,7 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w, const float
     if (th == 0 || lds == 0) return hipErrorInvalidValue;
     const int hchunks = (Hp + th - 1) / th;
     const int64_t ntiles = N * Dp * (int64_t)hchunks;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
+    const int cus = device_cus();
     const unsigned gy = (unsigned)((Cout + kCoGroup - 1) / kCoGroup);
     int64_t gx = cus / (int64_t)gy;
     if (gx < 1) gx = 1;
@@ -474,9 +471,7 @@ hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w, const float
 
 #define CT_LAUNCH_BF16(KS, TH, WB)                                                            \
     do {                                                                                      \
-        hipError_t e = hipFuncSetAttribute((const void *)fused3d_bf16_kernel<KS, TH, WB>,         \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,        \
-                                           (int)lds);                                         \
+        hipError_t e = allow_dynamic_lds((const void *)fused3d_bf16_kernel<KS, TH, WB>, lds);   \
         if (e != hipSuccess) return e;                                                        \
         hipLaunchKernelGGL((fused3d_bf16_kernel<KS, TH, WB>), dim3((unsigned)gx, gy),             \
                            dim3(kThreads), lds, stream, (const unsigned short *)x,            \

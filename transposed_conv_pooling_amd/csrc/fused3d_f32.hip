@@ -586,10 +586,8 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
 {
     const int Dp = (int)(D - 1), Hp = (int)(H - 1), Wp = (int)(W - 1);
     const int wblocks = (Wp + 15) / 16;
-    int dev = 0, cus = 256, per_cu = 1;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        cus = 256;
+    const int cus = device_cus();
+    int per_cu = 1;
     const unsigned gy = (unsigned)((Cout + 15) / 16);
 
     if constexpr (KS > 0) {
@@ -604,9 +602,7 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
             const bool vec4 = (W % 4 == 0) && (((uintptr_t)x & 15) == 0);
             const void *fn = vec4 ? (const void *)fused3d_f32_slab_kernel<KS, 4>
                                   : (const void *)fused3d_f32_slab_kernel<KS, 1>;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSlabThreads, lds) != hipSuccess ||
-                per_cu < 1)
-                per_cu = 1;
+            per_cu = occupancy(fn, kSlabThreads, lds);
             int64_t wgs = (int64_t)cus * per_cu / gy;
             if (wgs < 1) wgs = 1;
             if (wgs > ntasks) wgs = ntasks;
@@ -626,9 +622,7 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
     // direct-load path (Cin > 4, or rows too wide for an LDS slab)
     const int64_t nmb = N * Dp * (int64_t)Hp * wblocks;   // < 2^31 (checked by the shim)
     const size_t lds = (size_t)(2 * Cin) * 64 * sizeof(float);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fused3d_f32_kernel<KS>,
-                                                     kThreads, lds) != hipSuccess || per_cu < 1)
-        per_cu = 1;
+    per_cu = occupancy((const void *)fused3d_f32_kernel<KS>, kThreads, lds);
     int64_t waves = (int64_t)cus * per_cu * kWaves / gy;
     const int64_t max_waves = (nmb + kMinMbPerWave - 1) / kMinMbPerWave;
     if (waves > max_waves) waves = max_waves;
