@@ -148,6 +148,10 @@ class Op:
         self.inputs = inputs
         self.oracle_sample = oracle_sample    # () -> (seconds, fraction of the op)
         self._i = 0
+        # arithmetic type of the products: the bf16 contractions multiply bf16
+        # operands on the matrix cores (fp32 accumulation); every other op,
+        # bf16 pooling included, computes in fp32
+        self.arith = "bf16" if name in ("fused3d_bf16", "convT1d_bf16") else "f32"
 
     def run(self):
         bufs = self.sets[self._i % len(self.sets)]
@@ -156,10 +160,6 @@ class Op:
 
     def run_warm(self):
         self.call(*self.sets[0])
-        # arithmetic type of the products: the bf16 contractions multiply bf16
-        # operands on the matrix cores (fp32 accumulation); every other op,
-        # bf16 pooling included, computes in fp32
-        self.arith = "bf16" if name in ("fused3d_bf16", "convT1d_bf16") else "f32"
 
 
 def bf16_label(wl):
