@@ -60,7 +60,7 @@ OP_SOURCES = {
     "avgpool3d_bf16": "avgpool3d.hip",
     "fused3d_general": "generic.hip",
     "avgpool3d_nopad": "avgpool3d.hip",
-    "convT1d_general": "generic.hip",
+    "convT1d_general": "convT1d_f32.hip",
 }
 
 
@@ -83,6 +83,8 @@ KERNELS = [
     ("avgpool3d_k3s2p1_vec_kernel<float, true, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
     ("avgpool3d_k3s2p1_elem_kernel<float, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
     ("avgpool3d_k3s2p1_", "avgpool3d", "avgpool3d.hip", 9663676416),
+    # the stride-2 polyphase kernel first: it shares the fp32 prefix
+    ("convT1d_f32_poly_kernel", "convT1d_general", "convT1d_f32.hip", 2684477696),
     ("convT1d_f32", "convT1d", "convT1d_f32.hip", 1610752000),
     ("fused3d_bf16_kernel", "fused3d_bf16", "fused3d_bf16.hip", 75931904),
     ("convT1d_bf16_kernel", "convT1d_bf16", "convT1d_bf16.hip", 1342296064),
@@ -405,9 +407,11 @@ def make_ops(names, dev):
             oracle.convT1d(t["x"][:n], t["w"], t["bias"], 2, 1, 3, 1)
             return time.perf_counter() - t0, n / 32.0, f"{n} of 32 batch items"
 
-        # every input-weight product once, as at stride 1
+        # every input-weight product once, as at stride 1; on the fp32 matrix
+        # cores (two stride-1 gathers), so bound by their peak
         flops = 2 * 32 * 32 * 131072 * 5 * 64
-        ops.append(Op("convT1d_general", call, rotate(x, out), nbytes(x, w, bg, out), flops, "hbm", HBM_PEAK_GBS,
+        ops.append(Op("convT1d_general", call, rotate(x, out), nbytes(x, w, bg, out), flops, "mfma",
+                      MFMA_F32_PEAK_TFLOPS,
                       [wl.description + ", stride 2, pad 1, output_padding 1, bias"], sample))
 
     if "copy" in names:
@@ -736,8 +740,8 @@ def main():
         d["buffer_sets"] = len(op.sets)
         if op.flops:
             d["GFLOP_s"] = round(op.flops / avg / 1e6, 1)
-        if op.name == "convT1d":
-            d["mfma_frac"] = round(op.flops / avg / 1e9 / MFMA_F32_PEAK_TFLOPS, 4)
+        if op.bound == "mfma":
+            d["mfma_frac"] = round(op.flops / avg / 1e9 / op.peak, 4)
         d["workload"] = op.inputs[0]
         per_op[op.name] = d
         if op.name != "copy":

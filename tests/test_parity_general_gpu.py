@@ -259,6 +259,16 @@ CONV1D_GENERAL = [
     (1, 32, 16, 8, 5, 1, 0, 3, 0, True, "bf16"),      # shortest input
     (3, 32, 64, 1024, 5, 1, 0, 3, 0, True, "bf16"),   # several tiles per item
     (8, 32, 64, 40000, 5, 1, 0, 3, 0, True, "bf16"),  # more tiles than workgroups, ranges across items
+    # stride 2 on the fp32 matrix cores: two stride-1 gathers (residues of
+    # o + pad), pads of both parities, output padding up to 2, ragged tails
+    (1, 32, 64, 4, 5, 2, 0, 3, 0, False, "f32"),      # shortest input
+    (2, 32, 64, 64, 5, 2, 1, 3, 1, True, "f32"),
+    (1, 32, 64, 100, 5, 2, 2, 3, 2, True, "f32"),
+    (1, 32, 70, 520, 5, 2, 3, 3, 0, True, "f32"),     # two output-channel groups, ragged
+    (1, 32, 16, 260, 5, 2, 5, 3, 1, False, "f32"),    # pad past the first tile's halo
+    (1, 32, 64, 8, 5, 2, 9, 3, 2, True, "f32"),       # pad larger than the input
+    (3, 32, 64, 1028, 5, 2, 1, 3, 1, True, "f32"),    # tiles straddling batch items
+    (8, 32, 64, 20004, 5, 2, 1, 3, 1, True, "f32"),   # more tiles than waves: halos carried
 ]
 
 

@@ -31,6 +31,8 @@
 //  * Page's geometry (Cin 32, K 5, dilation 3): the same MFMA tiling with
 //    everything known at compile time, but each wave owns its tiles and a
 //    private strip, so no tile waits at a barrier (convT1d_f32_wave_kernel).
+#include <type_traits>
+
 #include "ct_internal.h"
 
 namespace ct {
@@ -344,6 +346,311 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
     }
 }
 
+// ---------------------------------------------------------------------------
+// Strided transposed convolution as S stride-1 gathers ([p74], passage on
+// the general-stride gather x[(o + pad - dil*k)/stride]): with o + pad =
+// S*q + rho (0 <= rho < S), output o takes exactly the taps k with
+// dil*k = rho (mod S), each from input i = q - delta_k,
+// delta_k = (dil*k - rho)/S >= 0.  So residue class rho is a stride-1
+// dilated gather over q with its own taps and shifts, every class reads the
+// same inputs x[q - delta], and the taps of all classes together are the K
+// taps once each.  On the matrix cores a wave tile is 16*NB consecutive q
+// of one batch item and 64 output channels; for each class the same input
+// strip x[n, :, q0 - HP .. q0 + 16*NB - 1] serves as the B operand at that
+// class's shifts, so a tile runs K*CIN4/4 k-steps in all, as at stride 1.
+// f(std::integral_constant<int, R>) for R = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int K, int DIL, int S>
+struct Poly {
+    static constexpr int count(int rho)
+    {
+        int c = 0;
+        for (int k = 0; k < K; ++k) c += ((DIL * k) % S == rho) ? 1 : 0;
+        return c;
+    }
+    static constexpr int tap(int rho, int idx)        // idx-th tap of class rho
+    {
+        int c = 0;
+        for (int k = 0; k < K; ++k)
+            if ((DIL * k) % S == rho) {
+                if (c == idx) return k;
+                ++c;
+            }
+        return 0;
+    }
+    static constexpr int delta(int rho, int idx) { return (DIL * tap(rho, idx) - rho) / S; }
+    static constexpr int first(int rho)               // taps of the classes before rho
+    {
+        int c = 0;
+        for (int r = 0; r < rho; ++r) c += count(r);
+        return c;
+    }
+    static constexpr int dmax()
+    {
+        int m = 0;
+        for (int k = 0; k < K; ++k) {
+            const int dd = (DIL * k - (DIL * k) % S) / S;
+            m = dd > m ? dd : m;
+        }
+        return m;
+    }
+    static constexpr int kHalo = (dmax() + 3) / 4 * 4;  // strip positions before q0
+};
+
+template <int CIN4, int K, int DIL, int S, int NB, int WW>
+struct PolyGeom {
+    typedef Poly<K, DIL, S> P;
+    static constexpr int kThreads = 64 * WW;
+    static constexpr int kTQ = 16 * NB;                             // q per wave tile
+    static constexpr int kKsteps = CIN4 * K / 4;
+    static constexpr int kTs = kTQ + P::kHalo;                      // strip positions
+    static constexpr int kStr16 = kTs <= 16 ? 16 : (kTs - 16 + 63) / 64 * 64 + 16;
+    static constexpr int kStr48 = kTs <= 48 ? 48 : (kTs - 48 + 63) / 64 * 64 + 48;
+    static constexpr int kStr = kStr16 < kStr48 ? kStr16 : kStr48;
+    static constexpr int kQ = CIN4 * kTs / 4;                       // float4 pieces per strip
+    static constexpr int kQPerLane = (kQ + 63) / 64;
+    static constexpr int kWfrag = 4 * kKsteps * 64;                 // floats
+    static constexpr int kLdsFloats = kWfrag + kCO + WW * CIN4 * kStr;
+};
+
+template <int CIN4, int K, int DIL, int S, int NB, int WW>
+__global__ __launch_bounds__(64 * WW, 1)
+void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restrict__ w,
+                             const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
+                             int pad, int qa4, int tq_per_n, int ntiles, float *__restrict__ y)
+{
+    typedef PolyGeom<CIN4, K, DIL, S, NB, WW> G;
+    typedef Poly<K, DIL, S> P;
+    static_assert(G::kStr >= G::kTs && (G::kStr % 64 == 16 || G::kStr % 64 == 48), "strip row stride");
+    static_assert(G::kQPerLane <= 32, "piece mask");
+    static_assert(G::kLdsFloats * 4 <= 160 * 1024, "LDS of one workgroup");
+    typedef float v4f_ __attribute__((ext_vector_type(4)));
+    constexpr int HP = P::kHalo;
+    extern __shared__ float lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float *wfrag = lds;                                      // [js][lane][m]
+    float *bsh = lds + G::kWfrag;                            // [64] bias of the channel block
+    float *xs = bsh + kCO + wave * CIN4 * G::kStr;           // this wave's [CIN4][kStr]
+    const int cog = blockIdx.y;
+    const int kq = lane >> 4, col = lane & 15;
+
+    // Fragments in class order: k-step js = (first(rho) + idx)*(CIN4/4) + c
+    // holds A[co = 16m + l%16][kappa = l/16] = w[4c + l/16, co, tap(rho, idx)].
+    for (int e = threadIdx.x; e < G::kWfrag; e += G::kThreads) {
+        const int m = e & 3, l = (e >> 2) & 63, js = e >> 8;
+        const int t = js / (CIN4 / 4), c = js % (CIN4 / 4);   // t-th tap in class order
+        int k = 0;
+#pragma unroll
+        for (int rho = 0; rho < S; ++rho)
+#pragma unroll
+            for (int idx = 0; idx < P::count(rho); ++idx)
+                if (P::first(rho) + idx == t) k = P::tap(rho, idx);
+        const int co = cog * kCO + 16 * m + (l & 15);
+        const int ci = 4 * c + (l >> 4);
+        wfrag[e] = (co < Cout && ci < Cin) ? w[((int64_t)ci * Cout + co) * K + k] : 0.0f;
+    }
+    if (threadIdx.x < kCO) {
+        const int co = cog * kCO + threadIdx.x;
+        bsh[threadIdx.x] = (bias && co < Cout) ? bias[co] : 0.0f;
+    }
+
+    // this wave's contiguous tile range (workgroups in XCD-aware order)
+    const int64_t gw = xcd_remap(blockIdx.x, gridDim.x) * WW + wave;
+    const int64_t nw = (int64_t)gridDim.x * WW;
+    const int per = (int)(ntiles / nw), rem = (int)(ntiles % nw);
+    const int t_begin = (int)(gw * per + (gw < rem ? gw : rem));
+    const int t_end = t_begin + per + (gw < rem ? 1 : 0);
+
+    // strip piece q = ci * (kTs/4) + t4 covers inputs q0 - HP + 4*t4 .. +3
+    // (L % 4 == 0 and q0 - HP = 0 mod 4: a piece is wholly inside or outside
+    // [0, L)); as in the stride-1 kernel, a tile that continues the previous
+    // one takes its halo from the previous strip inside LDS.
+    v4f_ pre[G::kQPerLane];
+    unsigned pok = 0, pput = 0;
+    auto fetch = [&](int tile, bool carry) {
+        const int n = tile / tq_per_n;
+        const int q0 = qa4 + (tile - n * tq_per_n) * G::kTQ;
+        const float *xn = x + (int64_t)n * Cin * L;
+#pragma unroll
+        for (int i = 0; i < G::kQPerLane; ++i) {
+            const int qq = lane + 64 * i;
+            const int ci = qq / (G::kTs / 4), t4 = qq % (G::kTs / 4);
+            const int pos = q0 - HP + 4 * t4;
+            const bool mine = qq < G::kQ && !(carry && t4 < HP / 4);
+            const bool ok = mine && ci < Cin && pos >= 0 && pos < L;
+            pre[i] = *reinterpret_cast<const v4f_ *>(ok ? xn + (int64_t)ci * L + pos : x);
+            pok = ok ? pok | (1u << i) : pok & ~(1u << i);
+            pput = mine ? pput | (1u << i) : pput & ~(1u << i);
+        }
+    };
+    if (t_begin < t_end) fetch(t_begin, false);
+    __syncthreads();                                         // weights and bias staged
+
+    const float *xl = xs + kq * G::kStr + HP + col;         // lane's B base (q = q0 + col)
+    const float *al = wfrag + lane * 4;                      // lane's A base
+    for (int tile = t_begin; tile < t_end; ++tile) {
+        const int n = tile / tq_per_n;
+        const int q0 = qa4 + (tile - n * tq_per_n) * G::kTQ;
+        __builtin_amdgcn_wave_barrier();
+        if (HP > 0 && tile > t_begin && tile - n * tq_per_n > 0) {
+            constexpr int kHq = CIN4 * (HP > 0 ? HP / 4 : 1);
+            v4f_ hv[(kHq + 63) / 64];
+#pragma unroll
+            for (int i = 0; i < (kHq + 63) / 64; ++i) {
+                const int qq = lane + 64 * i;
+                const int ci = qq / (HP / 4), u = qq % (HP / 4);
+                hv[i] = *reinterpret_cast<const v4f_ *>(xs + min(ci, CIN4 - 1) * G::kStr + G::kTQ + 4 * u);
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < (kHq + 63) / 64; ++i) {
+                const int qq = lane + 64 * i;
+                const int ci = qq / (HP / 4), u = qq % (HP / 4);
+                if (qq < kHq) *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * u) = hv[i];
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+#pragma unroll
+        for (int i = 0; i < G::kQPerLane; ++i) {
+            const int qq = lane + 64 * i;
+            if ((pput >> i) & 1) {
+                const int ci = qq / (G::kTs / 4), t4 = qq % (G::kTs / 4);
+                *reinterpret_cast<v4f_ *>(xs + ci * G::kStr + 4 * t4) =
+                    ((pok >> i) & 1) ? pre[i] : (v4f_){0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (tile + 1 < t_end) {
+            const int n1 = (tile + 1) / tq_per_n;
+            fetch(tile + 1, n1 == n);
+        }
+
+        const __amdgpu_buffer_rsrc_t yr =
+            __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * Cout * Lo, 0, Cout * Lo * 4, 0x00020000);
+        // D[co][q] (operands not swapped): lane (kq, col) holds channel
+        // 16m + 4kq + r at q = q0 + 16b + col; class rho's value there is
+        // output o = S*q + rho - pad.
+        v4f acc[S][4][NB];
+        static_for<0, S>([&](auto rc) {
+            constexpr int rho = decltype(rc)::value;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float bc = bsh[16 * m + 4 * kq + r];
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) acc[rho][m][b][r] = bc;
+                }
+            constexpr int kSteps = P::count(rho) * (CIN4 / 4);
+            v4f_ fa[2];
+            float fb[2][NB];
+            auto ldf = [&](int st, int buf) {
+                const int idx = st / (CIN4 / 4), c = st % (CIN4 / 4);
+                const int dl = P::delta(rho, idx);
+                fa[buf] = *reinterpret_cast<const v4f_ *>(al + ((P::first(rho) + idx) * (CIN4 / 4) + c) * 256);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) fb[buf][b] = xl[-dl + 4 * c * G::kStr + 16 * b];
+            };
+            ldf(0, 0);
+#pragma unroll
+            for (int st = 0; st < kSteps; ++st) {
+                if (st + 1 < kSteps) ldf(st + 1, (st + 1) & 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        acc[rho][m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[st & 1][m], fb[st & 1][b], acc[rho][m][b], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+
+        // Stores.  With S = 2 the two classes interleave: outputs o and o+1
+        // (o even) are (class 0, class 1) at one q when pad is even, and
+        // (class 1 at q, class 0 at q+1) when pad is odd; the second comes
+        // from the next lane of the 16-lane row (a DPP rotate) or, at the
+        // row's end, from lane 0 of the next q block.  Each such pair is one
+        // 8-byte store (o even and Lo even keep it 8-byte aligned), so 16
+        // lanes write 128 contiguous bytes of one channel.  Tiles whose
+        // outputs reach past either end of the row, and odd Lo, take one
+        // 4-byte store per output instead.
+        static_assert(S == 2, "paired stores are written for stride 2");
+        const bool podd = pad & 1;
+        const int olo = 2 * q0 - pad, ohi = 2 * (q0 + G::kTQ) + 1 - pad;   // tile's output span
+        const bool paired = (Lo % 2 == 0) && olo >= 0 && ohi < Lo;
+        if (paired) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int co = cog * kCO + 16 * m + 4 * kq + r;
+                    const int rowoff = co * Lo;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        const int q = q0 + 16 * b + col;
+                        float v0, v1;
+                        int o;
+                        bool ok = co < Cout;
+                        if (!podd) {
+                            v0 = acc[0][m][b][r];
+                            v1 = acc[1][m][b][r];
+                            o = 2 * q - pad;
+                        } else {
+                            // lane col takes class 0 of q+1: lane col+1, or lane 0 of block b+1
+                            const float nx = __int_as_float(__builtin_amdgcn_update_dpp(
+                                0, __float_as_int(acc[0][m][b][r]), 0x12F, 0xf, 0xf, false));   // row_ror:15
+                            const float nb = b + 1 < NB ? __int_as_float(__builtin_amdgcn_update_dpp(
+                                0, __float_as_int(acc[0][m][b + 1 < NB ? b + 1 : b][r]), 0x12F, 0xf, 0xf, false))
+                                                        : 0.0f;
+                            v0 = acc[1][m][b][r];
+                            v1 = col == 15 ? nb : nx;
+                            o = 2 * q + 1 - pad;
+                            ok = ok && !(b == NB - 1 && col == 15);   // its partner is in the next tile
+                        }
+                        typedef float v2f_ __attribute__((ext_vector_type(2)));
+                        typedef int v2i_ __attribute__((ext_vector_type(2)));
+                        const int off = ok ? (rowoff + o) * 4 : 0x7ffffff0;
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_, (v2f_){v0, v1}), yr, off, 0, 0);
+                    }
+                    if (podd) {
+                        // the unpaired ends: class 0 at q0 (o = 2*q0 - pad) and
+                        // class 1 at the tile's last q
+                        const bool first = col == 0, last = col == 15;
+                        const float v = first ? acc[0][m][0][r] : acc[1][m][NB - 1][r];
+                        const int o = first ? 2 * q0 - pad : 2 * (q0 + G::kTQ - 1) + 1 - pad;
+                        const int off = (co < Cout && (first || last)) ? (rowoff + o) * 4 : 0x7ffffff0;
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, off, 0, 0);
+                    }
+                }
+        } else {
+            static_for<0, S>([&](auto rc) {
+                constexpr int rho = decltype(rc)::value;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int co = cog * kCO + 16 * m + 4 * kq + r;
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            const int o = S * (q0 + 16 * b + col) + rho - pad;
+                            const int off = (co < Cout && o >= 0 && o < Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[rho][m][b][r]), yr, off, 0, 0);
+                        }
+                    }
+            });
+        }
+    }
+}
+
 // The configuration the launcher uses for Cin 32, K 5, dilation 3: 64-output
 // wave tiles, 8 waves (2 per SIMD) per workgroup.  Measured at the
 // [32,32,131072] workload: 710 us, against 720 for 32-output tiles with 12
@@ -404,6 +711,43 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
     hipLaunchKernelGGL(convT1d_f32_kernel, dim3((unsigned)gx, gy), dim3(kThreads), lds, stream,
                        x, w, bias, (int)Cin, cin4, (int)L, (int)Cout, K, dilation, (int)Lo,
                        tiles_per_n, (int)ntiles, (int)str, out);
+    return hipGetLastError();
+}
+
+bool convT1d_f32_poly_supported(int64_t Cin, int K, int stride, int dilation, int64_t L,
+                                const void *x)
+{
+    return Cin == 32 && K == 5 && dilation == 3 && stride == 2 && L % 4 == 0 &&
+           (((uintptr_t)x) & 15) == 0;
+}
+
+hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *bias, int64_t N,
+                                   int64_t Cin, int64_t L, int64_t Cout, int K, int stride,
+                                   int pad, int dilation, int out_pad, float *out,
+                                   hipStream_t stream)
+{
+    if (!convT1d_f32_poly_supported(Cin, K, stride, dilation, L, x)) return hipErrorInvalidValue;
+    constexpr int S = 2;
+    constexpr int NB = 2;      // 32-q tiles: both classes' accumulators stay in registers
+    typedef PolyGeom<32, 5, 3, S, NB, kWaveWW> G;
+    const int64_t Lo = (L - 1) * S - 2 * (int64_t)pad + (int64_t)dilation * (K - 1) + out_pad + 1;
+    // q covers o + pad = S*q + rho for every output: q in [pad/S, ceil((Lo + pad)/S)),
+    // started at a multiple of 4 so that strip pieces stay float4-aligned
+    const int64_t qa4 = ((int64_t)pad / S) & ~int64_t(3);
+    const int64_t qb = (Lo + pad + S - 1) / S;
+    const int tq_per_n = (int)((qb - qa4 + G::kTQ - 1) / G::kTQ);
+    const int64_t ntiles = N * tq_per_n;
+    const void *fn = (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW>;
+    const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
+    hipError_t e = allow_dynamic_lds(fn, lds);
+    if (e != hipSuccess) return e;
+    const int cus = device_cus(), per_cu = occupancy(fn, G::kThreads, lds);
+    const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
+    int64_t gx = (int64_t)cus * per_cu / gy;
+    if (gx < 1) gx = 1;
+    hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW>), dim3((unsigned)gx, gy),
+                       dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
+                       (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
     return hipGetLastError();
 }
 

@@ -385,8 +385,23 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
                     (Cout + 63) / 64 <= 65535 && prod({Cout, Lo, 4}, &item) &&
                     item < (int64_t(1) << 31) - 64;
     }
+    // Stride 2 in fp32 at the page's channel and tap geometry runs as two
+    // stride-1 gathers on the fp32 matrix cores.
+    bool poly = x_dtype == CT_F32 && stride == 2 &&
+                ct::convT1d_f32_poly_supported(Cin, K, stride, dilation, L, x);
+    if (poly) {
+        const int64_t tq = ((Lo + pad + 1) / 2 + 64) / 64 + 1;
+        int64_t ntq, item;
+        poly = Lo <= kI32Max / 2 && pad <= kGenericMaxLen && prod({N, tq}, &ntq) &&
+               ntq <= kI32Max && (Cout + 63) / 64 <= 65535 && prod({Cout, Lo, 4}, &item) &&
+               item < (int64_t(1) << 31) - 64;
+    }
     hipError_t e;
-    if (fast) {
+    if (poly) {
+        e = ct::launch_convT1d_f32_poly((const float *)x, (const float *)w, bias, N, Cin, L, Cout,
+                                        K, stride, pad, dilation, out_pad, out,
+                                        (hipStream_t)stream);
+    } else if (fast) {
         e = ct::launch_convT1d_f32((const float *)x, (const float *)w, bias, N, Cin, L, Cout, K,
                                    dilation, out, (hipStream_t)stream);
     } else if (fast_bf16) {

@@ -53,6 +53,17 @@ hipError_t launch_convT1d_f32(const float *x, const float *w,
                               int64_t L, int64_t Cout, int K, int dilation,
                               float *out, hipStream_t stream);
 
+// ConvTranspose1d with stride 2 (any pad and output padding) as two stride-1
+// gathers on the fp32 matrix cores, where convT1d_f32_poly_supported() holds
+// (fp32, Cin 32, K 5, dilation 3, L % 4 == 0, x 16-byte aligned); output
+// items below 2^31 - 64 bytes.
+bool convT1d_f32_poly_supported(int64_t Cin, int K, int stride, int dilation, int64_t L,
+                                const void *x);
+hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *bias, int64_t N,
+                                   int64_t Cin, int64_t L, int64_t Cout, int K, int stride,
+                                   int pad, int dilation, int out_pad, float *out,
+                                   hipStream_t stream);
+
 // ConvTranspose1d, stride 1, pad 0, bf16 x and w (fp32 accumulation and
 // output) on the bf16 matrix cores, for the geometries where
 // convT1d_bf16_supported() holds (Cin 32, K 5, dilation 3, L a multiple of 8,
