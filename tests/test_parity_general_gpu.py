@@ -76,6 +76,14 @@ FUSED_GENERAL = [
     (2, 3, 16, 4, 5, 13, 3, 2, 1, 0, 2, 2, "bf16"),   # page geometry, bf16 W % 8 != 0
     (2, 3, 16, 9, 17, 33, 3, 2, 1, 1, 2, 2, "f32"),   # output_padding 1 on the effective-filter gather
     (1, 40, 40, 3, 3, 4, 3, 2, 1, 1, 2, 2, "f32"),    # Cin*Cout > 1024: the plain gather
+    # output_padding 1 on the fp32 slab kernel (Cin <= 4): far-edge taps read 0,
+    # float4 rows (W % 4 == 0) and scalar rows, several tasks per workgroup
+    (2, 3, 16, 6, 10, 16, 3, 2, 1, 1, 2, 2, "f32"),
+    (1, 4, 20, 3, 9, 8, 3, 2, 1, 1, 2, 2, "f32"),     # ragged Cout
+    (3, 1, 16, 4, 33, 32, 3, 2, 1, 1, 2, 2, "f32"),
+    (1, 2, 5, 2, 2, 4, 3, 2, 1, 1, 2, 2, "f32"),      # one input plane pair
+    (5, 3, 16, 7, 20, 23, 3, 2, 1, 1, 2, 2, "f32"),   # scalar rows, ragged W
+    (2, 3, 16, 1, 1, 1, 3, 2, 1, 1, 2, 2, "f32"),     # a single input voxel
 ]
 
 

@@ -198,8 +198,11 @@ ct_status ct_convT3d_scale_pool_bias(
         return fail(CT_EUNSUPPORTED, "%s: x and w dtypes must match", fn);
 
     // The pages' geometry (k3 s2 p1, 2-pool) runs on the matrix-core kernels
-    // when their own limits hold; everything else on the general kernel.
-    bool fast = k == 3 && stride == 2 && pad == 1 && out_pad == 0 && pool_k == 2 && ps == 2;
+    // when their own limits hold; with output padding 1 the fp32 slab kernel
+    // takes it (far-edge taps read 0); everything else the general kernels.
+    bool fast = k == 3 && stride == 2 && pad == 1 && pool_k == 2 && ps == 2 &&
+                (out_pad == 0 || (out_pad == 1 && x_dtype == CT_F32 &&
+                                  ct::fused3d_f32_slab_supported(Cin, H, W, 1, (const float *)x)));
     if (fast) {
         const int64_t wblocks = (pd[2] + 15) / 16;
         int64_t nmb, xitem, oitem;
@@ -220,7 +223,7 @@ ct_status ct_convT3d_scale_pool_bias(
     hipError_t e;
     if (fast && x_dtype == CT_F32) {
         e = ct::launch_fused3d_f32((const float *)x, (const float *)w, conv_bias, bias, scale1,
-                                   scale2, N, Cin, D, H, W, Cout, out, (hipStream_t)stream);
+                                   scale2, N, Cin, D, H, W, Cout, out_pad, out, (hipStream_t)stream);
     } else if (fast) {
         e = ct::launch_fused3d_bf16((const uint16_t *)x, (const uint16_t *)w, conv_bias, bias,
                                     scale1, scale2, N, Cin, D, H, W, Cout, out,

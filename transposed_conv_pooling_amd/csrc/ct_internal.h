@@ -20,12 +20,15 @@ int device_cus();
 int occupancy(const void *fn, int threads, size_t lds);
 hipError_t allow_dynamic_lds(const void *fn, size_t lds);
 
-// Fused ConvTranspose3d(k3, s2, p1) -> *s1 -> AvgPool3d(2) -> +bias -> *s2,
-// fp32 x and w.  Output [N, Cout, D-1, H-1, W-1].
+// Fused ConvTranspose3d(k3, s2, p1, output_padding op) -> *s1 ->
+// AvgPool3d(2) -> +bias -> *s2, fp32 x and w.  Output [N, Cout, D-1+op,
+// H-1+op, W-1+op].  op = 1 only where fused3d_f32_slab_supported() holds
+// (Cin <= 4 and an LDS slab fits); op = 0 for any Cin.
+bool fused3d_f32_slab_supported(int64_t Cin, int64_t H, int64_t W, int op, const float *x);
 hipError_t launch_fused3d_f32(const float *x, const float *w,
                               const float *conv_bias, const float *bias,
                               float s1, float s2, int64_t N, int64_t Cin,
-                              int64_t D, int64_t H, int64_t W, int64_t Cout,
+                              int64_t D, int64_t H, int64_t W, int64_t Cout, int op,
                               float *out, hipStream_t stream);
 
 // Same chain with bf16 x and w (fp32 accumulation and output).

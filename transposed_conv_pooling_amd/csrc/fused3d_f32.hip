@@ -302,18 +302,18 @@ __global__ __launch_bounds__(kSlabThreads)
 void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ conv_bias,
                              const float *__restrict__ bias, float s1, float s2,
-                             int Cin, int D, int H, int W, int Cout,
+                             int Cin, int D, int H, int W, int SW, int Cout,
                              int Dp, int Hp, int Wp, int TH, int hchunks, int ntasks,
                              int tasks_per_wg, float *__restrict__ out)
 {
     typedef typename Vec<VEC>::T vec_t;
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int R = TH + 1;                      // input rows per plane in a slab
-    const int sfl = (int)slab_floats(Cin, TH, W);
+    const int sfl = (int)slab_floats(Cin, TH, SW);
     const int STR = (int)stage_stride(TH, Wp);
     float *wfrag = lds;                        // [KS][64]
-    float *slabs = lds + KS * 64;              // 2 x [Cin][2][R][W] (double buffer)
-    float *stage = lds + stage_offset(KS, Cin, TH, W);   // 2 x [16][STR]
+    float *slabs = lds + KS * 64;              // 2 x [Cin][2][R][SW] (double buffer)
+    float *stage = lds + stage_offset(KS, Cin, TH, SW);  // 2 x [16][STR]
     const int lane = threadIdx.x & 63;
     const int wave = uniform(threadIdx.x >> 6);
     const int cob = blockIdx.y;
@@ -334,6 +334,17 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         if (++hc_ == hchunks) { hc_ = 0; if (++d_ == Dp) { d_ = 0; ++n_; } }
     };
 
+    // With output_padding 1 the pooled grid reaches the input's far edges
+    // (Dp = D, Hp = H, Wp = W): the taps x[d+1], x[h+1], x[w+1] past them
+    // read 0 ([p50]'s parity rule with the missing inputs taken as zero).
+    // Slab rows then carry SW - W >= 1 zero columns after the row, zeroed
+    // here in both slab buffers (the loaders write only columns < W); rows
+    // and planes past the input are zero-filled by the loaders.
+    for (int e = threadIdx.x; e < 2 * Cin * 2 * R * (SW - W); e += kSlabThreads) {
+        const int row = e / (SW - W), c = e - row * (SW - W);
+        slabs[row * SW + W + c] = 0.0f;
+    }
+
     // Three roles, one pipeline stage per task, one barrier per stage (after
     // a first barrier that publishes the filter and the first slab).  In
     // stage s the loader waves put slab s+1 into LDS, the compute waves turn
@@ -345,9 +356,9 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         const int ll = threadIdx.x - kThreads;  // 0 .. kLoadThreads-1
         const int WV = W / VEC;
         const int npieces = Cin * 2 * R * WV;
-        // per piece: source offset, and destination offset * 256 + slab row
-        // (a slab fits the LDS budget, so offsets are < 2^23, and R <= 9);
-        // -1 marks "no piece"
+        // per piece: source offset, and destination offset * 256 + plane * 16
+        // + slab row (a slab fits the LDS budget, so offsets are < 2^23, and
+        // R <= 9); -1 marks "no piece"
         int src_off[kSlabPrefetch], dst_row[kSlabPrefetch];
 #pragma unroll
         for (int i = 0; i < kSlabPrefetch; ++i) {
@@ -356,7 +367,7 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             const int r = t % R, ca = t / R;
             const int a = ca & 1, ci = ca >> 1;
             src_off[i] = ci * DHW + a * HW + r * W + v * VEC;
-            dst_row[i] = q < npieces ? (((ca * R + r) * W + v * VEC) << 8) | r : -1;
+            dst_row[i] = q < npieces ? (((ca * R + r) * SW + v * VEC) << 8) | (a << 4) | r : -1;
         }
         // Every fetch issues exactly kSlabPrefetch loads, all from valid
         // addresses (x[0..] for no piece, a row past H or a task past the
@@ -367,7 +378,8 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             const float *xb = x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W;
 #pragma unroll
             for (int i = 0; i < kSlabPrefetch; ++i) {
-                const bool ok = real && dst_row[i] >= 0 && h0 + (dst_row[i] & 255) < H;
+                const bool ok = real && dst_row[i] >= 0 && h0 + (dst_row[i] & 15) < H &&
+                                d_ + ((dst_row[i] >> 4) & 1) < D;
                 pre[i] = *reinterpret_cast<const vec_t *>(ok ? xb + src_off[i] : x);
             }
         };
@@ -378,16 +390,16 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             for (int i = 0; i < kSlabPrefetch; ++i)
                 if (dst_row[i] >= 0)
                     *reinterpret_cast<vec_t *>(buf + (dst_row[i] >> 8)) =
-                        (h0 + (dst_row[i] & 255) < H) ? pre[i] : vec_t{};
+                        (h0 + (dst_row[i] & 15) < H && d_ + ((dst_row[i] >> 4) & 1) < D) ? pre[i] : vec_t{};
             for (int q = ll + kSlabPrefetch * kLoadThreads; q < npieces; q += kLoadThreads) {
                 const int v = q % WV, tt = q / WV;
                 const int r = tt % R, ca = tt / R;
                 vec_t val = vec_t{};
-                if (h0 + r < H)
+                if (h0 + r < H && d_ + (ca & 1) < D)
                     val = *reinterpret_cast<const vec_t *>(
                         x + (int64_t)n_ * Cin * DHW + (int64_t)d_ * HW + (int64_t)h0 * W +
                         (ca >> 1) * DHW + (ca & 1) * HW + r * W + v * VEC);
-                *reinterpret_cast<vec_t *>(buf + (ca * R + r) * W + v * VEC) = val;
+                *reinterpret_cast<vec_t *>(buf + (ca * R + r) * SW + v * VEC) = val;
             }
         };
         vec_t pa[kSlabPrefetch], pb[kSlabPrefetch];
@@ -505,7 +517,7 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
     for (int j = 0; j < KS; ++j) {
         const int kap = 4 * j + kq;
         const int ci = kap >> 3, tap = kap & 7;
-        soff[j] = ((ci * 2 + (tap >> 2)) * R + ((tap >> 1) & 1)) * W + (tap & 1);
+        soff[j] = ((ci * 2 + (tap >> 2)) * R + ((tap >> 1) & 1)) * SW + (tap & 1);
     }
     // The MFMA runs with the operands swapped, D = S^T (16 voxels x 16
     // channels): lane (kq, col) then holds voxels 4kq .. 4kq+3 of its block
@@ -546,7 +558,7 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
                     if (co_ok && wv0 + 4 * kq + r < Wp) dst[r] = __builtin_fmaf(p[r] + q[r], alpha, beta);
             };
             for (int hh = wave; hh < rows; hh += kWaves) {
-                const float *srowA = cur + hh * W;
+                const float *srowA = cur + hh * SW;
                 for (int wb = 0; wb < wblocks; wb += 2) {
                     const int wv0 = wb * 16 + col, wv1 = wv0 + 16;
                     const int wc0 = min(wv0, Wp - 1), wc1 = min(wv1, Wp - 1);
@@ -578,28 +590,44 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
 
 constexpr size_t kSlabLdsMax = 52 * 1024;   // three workgroups per CU
 
+// Pooled rows per slab task and the slab row stride for a geometry, or
+// TH = 0 when no slab fits the LDS budget.  Output padding 1 adds zero
+// columns after each slab row (4, keeping rows 16-byte aligned, when the
+// rows are loaded as float4).
+static void slab_plan(int ks, int64_t Cin, int64_t H, int64_t W, int op, bool vec4, int *TH_out,
+                      int *SW_out)
+{
+    const int Hp = (int)(H - 1 + op), Wp = (int)(W - 1 + op);
+    const int SW = (int)W + (op ? (vec4 ? 4 : 1) : 0);
+    int TH = Hp < 8 ? Hp : 8;
+    auto bytes = [&](int th) { return (size_t)slab_lds_floats(ks, Cin, th, SW, Wp) * sizeof(float); };
+    while (TH > 1 && bytes(TH) > kSlabLdsMax) --TH;
+    *TH_out = bytes(TH) <= kSlabLdsMax ? TH : 0;
+    *SW_out = SW;
+}
+
+static bool slab_vec4(int64_t W, const float *x) { return (W % 4 == 0) && (((uintptr_t)x & 15) == 0); }
+
 template <int KS>
 static hipError_t launch_ks(const float *x, const float *w, const float *conv_bias,
                             const float *bias, float s1, float s2, int64_t N, int64_t Cin,
-                            int64_t D, int64_t H, int64_t W, int64_t Cout, float *out,
+                            int64_t D, int64_t H, int64_t W, int64_t Cout, int op, float *out,
                             hipStream_t stream)
 {
-    const int Dp = (int)(D - 1), Hp = (int)(H - 1), Wp = (int)(W - 1);
+    const int Dp = (int)(D - 1 + op), Hp = (int)(H - 1 + op), Wp = (int)(W - 1 + op);
     const int wblocks = (Wp + 15) / 16;
     const int cus = device_cus();
     int per_cu = 1;
     const unsigned gy = (unsigned)((Cout + 15) / 16);
 
     if constexpr (KS > 0) {
-        // pooled rows per task: up to 8, as many as the LDS budget allows
-        int TH = Hp < 8 ? Hp : 8;
-        auto slab_bytes = [&](int th) { return (size_t)slab_lds_floats(KS, Cin, th, W, Wp) * sizeof(float); };
-        while (TH > 1 && slab_bytes(TH) > kSlabLdsMax) --TH;
-        if (slab_bytes(TH) <= kSlabLdsMax) {
-            const size_t lds = slab_bytes(TH);
+        const bool vec4 = slab_vec4(W, x);
+        int TH, SW;
+        slab_plan(KS, Cin, H, W, op, vec4, &TH, &SW);
+        if (TH > 0) {
+            const size_t lds = (size_t)slab_lds_floats(KS, Cin, TH, SW, Wp) * sizeof(float);
             const int hchunks = (Hp + TH - 1) / TH;
             const int64_t ntasks = N * Dp * (int64_t)hchunks;
-            const bool vec4 = (W % 4 == 0) && (((uintptr_t)x & 15) == 0);
             const void *fn = vec4 ? (const void *)fused3d_f32_slab_kernel<KS, 4>
                                   : (const void *)fused3d_f32_slab_kernel<KS, 1>;
             per_cu = occupancy(fn, kSlabThreads, lds);
@@ -611,14 +639,15 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
             if (vec4)
                 hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 4>), dim3(gx, gy), dim3(kSlabThreads), lds,
                                    stream, x, w, conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H,
-                                   (int)W, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
+                                   (int)W, SW, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
             else
                 hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 1>), dim3(gx, gy), dim3(kSlabThreads), lds,
                                    stream, x, w, conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H,
-                                   (int)W, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
+                                   (int)W, SW, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
             return hipGetLastError();
         }
     }
+    if (op != 0) return hipErrorInvalidValue;    // the direct path has no far-edge taps
     // direct-load path (Cin > 4, or rows too wide for an LDS slab)
     const int64_t nmb = N * Dp * (int64_t)Hp * wblocks;   // < 2^31 (checked by the shim)
     const size_t lds = (size_t)(2 * Cin) * 64 * sizeof(float);
@@ -635,18 +664,26 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
     return hipGetLastError();
 }
 
+bool fused3d_f32_slab_supported(int64_t Cin, int64_t H, int64_t W, int op, const float *x)
+{
+    if (Cin < 1 || Cin > 4) return false;
+    int TH, SW;
+    slab_plan(2 * (int)Cin, Cin, H, W, op, slab_vec4(W, x), &TH, &SW);
+    return TH > 0;
+}
+
 hipError_t launch_fused3d_f32(const float *x, const float *w,
                               const float *conv_bias, const float *bias,
                               float s1, float s2, int64_t N, int64_t Cin,
-                              int64_t D, int64_t H, int64_t W, int64_t Cout,
+                              int64_t D, int64_t H, int64_t W, int64_t Cout, int op,
                               float *out, hipStream_t stream)
 {
     switch (Cin) {
-    case 1: return launch_ks<2>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, out, stream);
-    case 2: return launch_ks<4>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, out, stream);
-    case 3: return launch_ks<6>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, out, stream);
-    case 4: return launch_ks<8>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, out, stream);
-    default: return launch_ks<0>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, out, stream);
+    case 1: return launch_ks<2>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    case 2: return launch_ks<4>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    case 3: return launch_ks<6>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    case 4: return launch_ks<8>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    default: return launch_ks<0>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
     }
 }
 
