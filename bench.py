@@ -25,7 +25,8 @@ workload [2,3,8,16,16] is timed per call (launch-bound) outside the step.
   python bench.py --ops copy        # plain 1 GiB device copy (counter calibration)
   python bench.py --ops fused3d_f32,unfused3d_f32   # fusion vs materialising the
                                     # [128,16,31,63,63] pre-pool tensor, then a 2-pool
-  python bench.py --summarize-trace DIR              # rocprofv3 --kernel-trace CSVs -> table
+  python bench.py --summarize-trace DIR [--ops a,b]  # rocprofv3 --kernel-trace CSVs -> table
+                                    # (--ops: the profiled run's ops, for kernels shared by ops)
   python bench.py --summarize-counters FETCH WRITE   # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
                                     # CSVs -> table + profiles/traffic.json
   python bench.py --summarize-pmc DIR [DIR ...]      # any rocprofv3 --pmc CSVs -> table +
@@ -58,7 +59,7 @@ OP_SOURCES = {
     "unfused3d_f32": "generic.hip",
     "convT1d_bf16": "convT1d_bf16.hip",
     "avgpool3d_bf16": "avgpool3d.hip",
-    "fused3d_general": "generic.hip",
+    "fused3d_general": "fused3d_f32.hip",
     "avgpool3d_nopad": "avgpool3d.hip",
     "convT1d_general": "convT1d_f32.hip",
 }
@@ -75,6 +76,8 @@ ORACLE_MIN_S = 2.5          # seconds of oracle time per op in the CPU baseline
 
 KERNELS = [
     ("fused3d_f32_slab_kernel", "fused3d_f32", "fused3d_f32.hip", 143258752),
+    # the same slab kernel serves the output_padding=1 workload
+    ("fused3d_f32_slab_kernel", "fused3d_general", "fused3d_f32.hip", 159388864),
     # bf16 pool kernels first: the fp32 ones share the name prefix
     ("avgpool3d_k3s2p1_vec_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
     ("avgpool3d_k3s2p1_elem_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
@@ -97,11 +100,29 @@ KERNELS = [
 ]
 
 
-def kernel_key(name):
-    for sub, key, src, nbytes in KERNELS:
-        if sub in name:
-            return key, src, nbytes
-    return None
+def kernel_key(name, ops=None):
+    """(key, source, algorithmic bytes) of a kernel as rocprofv3 names it.  A
+    kernel that serves several ops (the fp32 slab kernel) resolves to the op
+    among `ops`, the ops of the profiled run, when they are given."""
+    hits = [(sub, key, src, nbytes) for sub, key, src, nbytes in KERNELS
+            if sub in name and (ops is None or key not in OP_SOURCES or key in ops)]
+    if not hits:
+        return None
+    if ops is not None and len({h[1] for h in hits if h[0] == hits[0][0] and h[1] in ops}) > 1:
+        AMBIGUOUS.add(name)                  # two profiled ops launch this kernel
+        return None
+    return hits[0][1:]
+
+
+# kernels that two ops of one profiled run share: their dispatches cannot be told
+# apart by name, so the summaries leave them out (profile such ops in runs of their own)
+AMBIGUOUS = set()
+
+
+def _report_ambiguous():
+    for name in sorted(AMBIGUOUS):
+        print(f"\nleft out: `{name}` is launched by more than one of the profiled ops; "
+              "profile those ops in separate runs")
 
 
 def source_hash(op, src=None):
@@ -439,10 +460,10 @@ def _csv_rows(path):
     return rows
 
 
-def summarize_trace(path):
+def summarize_trace(path, ops=None):
     """Markdown table of a `rocprofv3 --kernel-trace` run: per kernel, calls
     and duration statistics in microseconds, and algorithmic GB/s at the
-    average duration."""
+    average duration.  `ops`: the ops of the profiled run (see kernel_key)."""
     durs = {}
     for r in _csv_rows(path):
         if "Kernel_Name" in r and "Start_Timestamp" in r and "End_Timestamp" in r:
@@ -452,7 +473,7 @@ def summarize_trace(path):
     print("| kernel | calls | avg us | min us | max us | share | algorithmic GB/s at avg |")
     print("|---|---|---|---|---|---|---|")
     for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-        k = kernel_key(name)
+        k = kernel_key(name, ops)
         avg = sum(v) / len(v)
         gbs = f"{k[2] / avg / 1e3:.0f}" if k else "-"
         short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
@@ -461,7 +482,7 @@ def summarize_trace(path):
               f"{100 * sum(v) / total:.2f}% | {gbs} |")
 
 
-def summarize_counters(fetch_path, write_path, dst=None):
+def summarize_counters(fetch_path, write_path, dst=None, ops=None):
     """HBM bytes per launch from two `rocprofv3 --pmc` runs (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
     for the bench's 1 GiB device copy; writes profiles/traffic.json (with a
@@ -473,12 +494,14 @@ def summarize_counters(fetch_path, write_path, dst=None):
                 continue
             v = float(r["Counter_Value"])
             if "copyBuffer" in r["Kernel_Name"]:
-                if int(r.get("Grid_Size", 0)) >= 1 << 17:     # the 1 GiB copy, not the uploads
-                    copy.append(v)
+                copy.append(v)
                 continue
-            k = kernel_key(r["Kernel_Name"])
+            k = kernel_key(r["Kernel_Name"], ops)
             if k:
                 vals.setdefault(k, []).append(v)
+        # the 1 GiB copy is the largest copy dispatch; the uploads of the inputs and
+        # the buffer-set clones are smaller copies through the same kernel
+        copy = [v for v in copy if copy and v >= 0.9 * max(copy)]
         return {k: sum(v) / len(v) for k, v in vals.items()}, (sum(copy) / len(copy) if copy else None)
     fetch, fcopy = per_kernel(fetch_path, "FETCH_SIZE")
     write, wcopy = per_kernel(write_path, "WRITE_SIZE")
@@ -500,11 +523,18 @@ def summarize_counters(fetch_path, write_path, dst=None):
         print(f"| {key} | {fetch[(key, src, alg)]:.0f} | {write[(key, src, alg)]:.0f} | {rb:.4g} | "
               f"{wb:.4g} | {rb + wb:.4g} | {alg:.4g} | {(rb + wb) / alg:.3f} |")
     dst = dst or os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(dst):                  # merge with the other runs' kernels
+        try:
+            prev = json.load(open(dst))
+        except (OSError, ValueError):
+            prev = {}
+        prev.update(out)
+        out = prev
     json.dump(out, open(dst, "w"), indent=1)
     print(f"\nwrote {os.path.relpath(dst, ROOT)}")
 
 
-def summarize_pmc(paths, dst=None):
+def summarize_pmc(paths, dst=None, ops=None):
     """Mean per dispatch of every counter in `rocprofv3 --pmc` runs (one or
     more output folders), per kernel of the bench, with figures derived from
     them where present: MfmaUtil (percent of SIMD cycles the matrix pipe was
@@ -517,7 +547,7 @@ def summarize_pmc(paths, dst=None):
         for r in _csv_rows(path):
             if "Counter_Name" not in r:
                 continue
-            k = kernel_key(r["Kernel_Name"])
+            k = kernel_key(r["Kernel_Name"], ops)
             if not k:
                 continue
             vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -643,13 +673,25 @@ def oracle_one_thread():
     return res
 
 
+def _ops_opt(argv):
+    """Strip an `--ops a,b` option from a summary command's arguments."""
+    if "--ops" in argv:
+        i = argv.index("--ops")
+        return argv[:i] + argv[i + 2:], set(argv[i + 1].split(","))
+    return argv, None
+
+
 def main():
-    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
-        return summarize_trace(sys.argv[2])
-    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
-        return summarize_counters(sys.argv[2], sys.argv[3])
-    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
-        return summarize_pmc(sys.argv[2:])
+    if len(sys.argv) > 1 and sys.argv[1] in ("--summarize-trace", "--summarize-counters",
+                                              "--summarize-pmc"):
+        args, ops = _ops_opt(sys.argv[2:])
+        if sys.argv[1] == "--summarize-trace":
+            summarize_trace(args[0], ops)
+        elif sys.argv[1] == "--summarize-counters":
+            summarize_counters(args[0], args[1], ops=ops)
+        else:
+            summarize_pmc(args, ops=ops)
+        return _report_ambiguous()
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

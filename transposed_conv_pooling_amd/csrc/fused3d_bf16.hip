@@ -39,7 +39,8 @@
 //    feeds 4 MFMAs (2 channel blocks x hi/lo).
 //  * Each workgroup walks a contiguous range of tiles in (n, row chunk, d)
 //    order, so consecutive tiles share an input plane and its second read
-//    hits the same XCD's L2.
+//    hits the same XCD's L2; the workgroup index is remapped so that
+//    neighbouring ranges also run on one XCD.
 #include "ct_internal.h"
 
 namespace ct {
@@ -116,7 +117,9 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     const int64_t pplane = (int64_t)Dp * Hp * Wp;
 
     // ---- this workgroup's tiles, and the first slab's loads ---------------
-    const int t_begin = uniform(blockIdx.x * tiles_per_wg);
+    // workgroups of one XCD take consecutive ranges, so the input plane two
+    // neighbouring ranges share is fetched into that XCD's L2 once
+    const int t_begin = uniform((int)xcd_remap(blockIdx.x, gridDim.x) * tiles_per_wg);
     const int t_end = uniform(min(t_begin + tiles_per_wg, ntiles));
     int hp, d, n;
     {
