@@ -57,40 +57,54 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 // Weff^T fragments for output-channel block cob: wfrag[j*64 + l] =
 // Weff[ci, co = cob*16 + l%16, tap] with kappa = 4j + l/16 = ci*8 + tap.
+// A thread takes two entries per pass and issues both entries' 16 weight
+// loads before summing, so with at most 2*kThreads entries (Cin <= 4) the
+// whole filter costs one round trip to memory.
 __device__ __forceinline__ void build_wfrag(const float *__restrict__ w, int Cout, int cob,
                                             int ksteps, float *wfrag)
 {
-    for (int e = threadIdx.x; e < ksteps * 64; e += kThreads) {
-        const int j = e >> 6, l = e & 63;
-        const int co = cob * 16 + (l & 15);
-        const int kap = 4 * j + (l >> 4);
-        // all 8 candidate taps are loaded unconditionally from valid addresses
-        // (a conditional load would be waited on before the next one issues)
-        const int ci = kap >> 3, tap = kap & 7;
-        const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
-        const float *wp = w + ((int64_t)ci * Cout + min(co, Cout - 1)) * 27;
-        // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
-        const int kd0 = a ? 0 : 1, nkd = a ? 1 : 2;
-        const int kh0 = b ? 0 : 1, nkh = b ? 1 : 2;
-        const int kw0 = c ? 0 : 1, nkw = c ? 1 : 2;
-        float t8[8];
+    const int nent = ksteps * 64;
+    for (int e0 = threadIdx.x; e0 < nent; e0 += 2 * kThreads) {
+        float t8[2][8];
+        int nk[2][3];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int u = 0; u < 2; ++u) {
+            // an entry past the end reads entry e0's weights (valid addresses,
+            // so every load is unconditional) and is not written
+            const int e = e0 + u * kThreads < nent ? e0 + u * kThreads : e0;
+            const int j = e >> 6, l = e & 63;
+            const int co = cob * 16 + (l & 15);
+            const int kap = 4 * j + (l >> 4);
+            const int ci = kap >> 3, tap = kap & 7;
+            const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
+            const float *wp = w + ((int64_t)ci * Cout + min(co, Cout - 1)) * 27;
+            // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
+            const int kd0 = a ? 0 : 1, kh0 = b ? 0 : 1, kw0 = c ? 0 : 1;
+            nk[u][0] = a ? 1 : 2; nk[u][1] = b ? 1 : 2; nk[u][2] = c ? 1 : 2;
+            // all 8 candidate taps of the 2x2x2 block starting at (kd0, kh0, kw0)
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    t8[(i * 2 + jj) * 2 + k] = wp[(kd0 + i) * 9 + (kh0 + jj) * 3 + kw0 + k];
-        float v = 0.0f;
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+                    for (int k = 0; k < 2; ++k)
+                        t8[u][(i * 2 + jj) * 2 + k] = wp[(kd0 + i) * 9 + (kh0 + jj) * 3 + kw0 + k];
+        }
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+        for (int u = 0; u < 2; ++u) {
+            const int e = e0 + u * kThreads;
+            if (e >= nent) continue;
+            float v = 0.0f;
 #pragma unroll
-                for (int k = 0; k < 2; ++k)
-                    if (i < nkd && jj < nkh && k < nkw) v += t8[(i * 2 + jj) * 2 + k];
-        if (co >= Cout) v = 0.0f;
-        wfrag[e] = v;
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                    for (int k = 0; k < 2; ++k)
+                        if (i < nk[u][0] && jj < nk[u][1] && k < nk[u][2]) v += t8[u][(i * 2 + jj) * 2 + k];
+            if (cob * 16 + (e & 15) >= Cout) v = 0.0f;
+            wfrag[e] = v;
+        }
     }
 }
 
@@ -264,15 +278,15 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // partial lines in a workgroup are written with plain stores (for L2 to
 // merge with the neighbour's part).  Staging is double-buffered as well:
 // one barrier per task separates a task's compute from its store phase.
-constexpr int kSlabPrefetch = 3;   // slab pieces each loader lane keeps in flight (more
-                                   // would cost the registers of a third workgroup per CU)
+constexpr int kSlabPrefetch = 4;   // slab pieces each loader lane keeps in flight
 constexpr int kLine = 32;          // floats per 128-byte line
-// 4 compute waves, 3 loader waves, 4 store waves.  vmcnt counts a wave's
+// 4 compute waves, 2 loader waves, 2 store waves: 8 waves, so that three
+// workgroups fit a CU's 32 wave slots (with under 64 VGPRs a wave).  vmcnt counts a wave's
 // loads and stores together and retires them in order, so a wave that both
 // stores and prefetches would wait for its earlier stores before each slab;
 // here only the loader waves load and only the store waves store.
-constexpr int kLoadWaves = 3;
-constexpr int kStoreWaves = 4;
+constexpr int kLoadWaves = 2;
+constexpr int kStoreWaves = 2;
 constexpr int kRowsPerStoreWave = 16 / kStoreWaves;       // staging rows per store wave
 constexpr int kLanesPerRow = 64 / kRowsPerStoreWave;      // lanes on one row (16 B each)
 constexpr int kLinesPerStore = kLanesPerRow / 8;          // lines of a row per store instruction
@@ -511,7 +525,18 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
     const int col = lane & 15;
     const int kq = lane >> 4;
     const int wblocks = (Wp + 15) / 16;
+    // The MFMA runs with the operands swapped, D = S^T (16 voxels x 16
+    // channels): lane (kq, col) then holds voxels 4kq .. 4kq+3 of its block
+    // for channel cob*16 + col, four consecutive outputs of one channel.
+    // folded epilogue ((S/8 + cb)*s1 + b)*s2 = S*alpha + beta[co]; the bias
+    // loads go out with the filter's, in the same round trip
+    const float alpha = 0.125f * s1 * s2;
+    const int co_l = cob * 16 + col;
+    const bool co_ok = co_l < Cout;
+    const float cbv = conv_bias && co_ok ? conv_bias[co_l] : 0.0f;
+    const float bv = bias && co_ok ? bias[co_l] : 0.0f;
     build_wfrag(w, Cout, cob, KS, wfrag);
+    const float beta = (cbv * s1 + bv) * s2;
     int soff[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
@@ -519,15 +544,6 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         const int ci = kap >> 3, tap = kap & 7;
         soff[j] = ((ci * 2 + (tap >> 2)) * R + ((tap >> 1) & 1)) * SW + (tap & 1);
     }
-    // The MFMA runs with the operands swapped, D = S^T (16 voxels x 16
-    // channels): lane (kq, col) then holds voxels 4kq .. 4kq+3 of its block
-    // for channel cob*16 + col, four consecutive outputs of one channel.
-    // folded epilogue ((S/8 + cb)*s1 + b)*s2 = S*alpha + beta[co]
-    const float alpha = 0.125f * s1 * s2;
-    const int co_l = cob * 16 + col;
-    const bool co_ok = co_l < Cout;
-    const float beta = ((conv_bias && co_ok ? conv_bias[co_l] : 0.0f) * s1 +
-                        (bias && co_ok ? bias[co_l] : 0.0f)) * s2;
     const int co_off = co_l * (int)pplane;    // per-item output offsets fit in int32 (checked by the shim)
     __syncthreads();                           // filter and first slab visible
     float a[KS];
@@ -549,7 +565,7 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             // row's w-blocks go in pairs, each block's K range split over two
             // accumulators: four independent MFMA chains in flight, with all
             // their LDS reads issued first.  (One row, not two, per pass keeps
-            // every role under 56 VGPRs, so three workgroups fit on a CU.)
+            // every role within 64 VGPRs: three 8-wave workgroups per CU.)
             // (block voxels 4kq+r at w = wv0 + r of the block start wv0)
             auto stage_block = [&](int hh, int wv0, const v4f &p, const v4f &q) {
                 float *dst = srow + hh * Wp + wv0;
@@ -588,7 +604,7 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
 
 }  // namespace
 
-constexpr size_t kSlabLdsMax = 52 * 1024;   // three workgroups per CU
+constexpr size_t kSlabLdsMax = 52 * 1024;   // three workgroups per CU (160 KB of LDS)
 
 // Pooled rows per slab task and the slab row stride for a geometry, or
 // TH = 0 when no slab fits the LDS budget.  Output padding 1 adds zero
