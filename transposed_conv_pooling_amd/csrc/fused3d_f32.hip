@@ -48,6 +48,7 @@ namespace ct {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -280,6 +281,7 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // one barrier per task separates a task's compute from its store phase.
 constexpr int kSlabPrefetch = 4;   // slab pieces each loader lane keeps in flight
 constexpr int kLine = 32;          // floats per 128-byte line
+constexpr int kLineSlack = 2 * kLine;   // LDS floats after the staging sets (see the store waves)
 // 4 compute waves, 2 loader waves, 2 store waves: 8 waves, so that three
 // workgroups fit a CU's 32 wave slots (with under 64 VGPRs a wave).  vmcnt counts a wave's
 // loads and stores together and retires them in order, so a wave that both
@@ -306,20 +308,31 @@ __host__ __device__ inline int64_t stage_offset(int64_t ks, int64_t cin, int64_t
 {
     return (ks * 64 + 2 * slab_floats(cin, th, w) + 3) & ~int64_t(3);
 }
+// (plus a line of slack: the store waves read whole pieces up to a line past
+// a staging row's end, for pieces they then do not store)
 __host__ __device__ inline int64_t slab_lds_floats(int64_t ks, int64_t cin, int64_t th, int64_t w, int64_t wp)
 {
-    return stage_offset(ks, cin, th, w) + 2 * 16 * stage_stride(th, wp);
+    return stage_offset(ks, cin, th, w) + 2 * 16 * stage_stride(th, wp) + kLineSlack;
 }
 
-template <int KS, int VEC>
+// GW > 0: the input width GW, the output padding GOP and the pooled rows per
+// task GTH are compile-time constants (the page's geometries), so that row
+// lengths, strides and trip counts fold into immediates; GW == 0: runtime.
+template <int KS, int VEC, int GW = 0, int GTH = 0, int GOP = 0>
 __global__ __launch_bounds__(kSlabThreads)
 void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ conv_bias,
                              const float *__restrict__ bias, float s1, float s2,
-                             int Cin, int D, int H, int W, int SW, int Cout,
-                             int Dp, int Hp, int Wp, int TH, int hchunks, int ntasks,
+                             int Cin_, int D, int H, int W_, int SW_, int Cout,
+                             int Dp, int Hp, int Wp_, int TH_, int hchunks, int ntasks,
                              int tasks_per_wg, float *__restrict__ out)
 {
+    static_assert(KS > 0, "the slab kernel has a compile-time channel count");
+    const int Cin = KS / 2;
+    const int W = GW > 0 ? GW : W_;
+    const int SW = GW > 0 ? GW + (GOP ? (VEC == 4 ? 4 : 1) : 0) : SW_;
+    const int Wp = GW > 0 ? GW - 1 + GOP : Wp_;
+    const int TH = GW > 0 ? GTH : TH_;
     typedef typename Vec<VEC>::T vec_t;
     extern __shared__ __attribute__((aligned(16))) float lds[];
     const int R = TH + 1;                      // input rows per plane in a slab
@@ -455,9 +468,15 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
         const int j = lane % kLanesPerRow;
         const int sc = (wave - kWaves - kLoadWaves) * kRowsPerStoreWave + lane / kLanesPerRow;
         const bool row_ok = cob * 16 + sc < Cout;
-        const int64_t row_off = (int64_t)(cob * 16 + sc) * pplane;
+        // float offset of this row's channel plane within a batch item's output
+        // (an item's output is below 2^31 bytes, checked by the shim)
+        const int co_off = (cob * 16 + sc) * (int)pplane;
+        const int item_bytes = Cout * (int)pplane * 4;
         // most store instructions a row needs: its whole lines, kLinesPerStore at a time
         const int kmax = ((kLine - 1 + TH * Wp) / kLine + kLinesPerStore - 1) / kLinesPerStore;
+        constexpr int kTail = (kLine + kLanesPerRow - 1) / kLanesPerRow;
+        constexpr int kStep = 4 * kLanesPerRow;                    // floats of a row per instruction
+        constexpr unsigned kOff = 0x80000000u;                     // past any item: dropped
         bool cont = false;
         __syncthreads();
         __syncthreads();                       // stage 0: nothing to store yet
@@ -471,45 +490,62 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
             float *sn = stage + (buf ^ 1) * 16 * STR + sc * STR;
             const int h0 = hs * TH;
             const int len = min(TH, Hp - h0) * Wp;
-            float *first = out + (int64_t)ns * Cout * pplane + row_off + ((int64_t)ds * Hp + h0) * Wp;
+            // stores go through a buffer resource over batch item ns's output;
+            // a lane's row starts at float offset foff of the item
+            const float *item = out + (int64_t)ns * Cout * pplane;
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)item, 0, item_bytes, 0x00020000);
+            const int foff = co_off + (ds * Hp + h0) * Wp;
             // staging positions [start, end) hold task s-1's outputs (and, if
             // continued, the carried line head [0, c0)); whole lines [lo, hi)
             // go out with non-temporal 16-byte stores, the partial head
             // [start, lo) with plain stores, the tail [hi, end) to the next
-            // staging set or, where the stream ends here, to memory
-            const int c0 = (int)(((uintptr_t)first >> 2) & (kLine - 1));
-            float *gl = first - c0;                                   // 128-byte aligned
+            // staging set or, where the stream ends here, to memory.  Position
+            // p is the float at item offset gbase + p (gbase + p >= 0 for
+            // every position that is stored: a carried head belongs to the
+            // previous task of the same item).
+            const int c0 = (int)((((uintptr_t)item >> 2) + (unsigned)foff) & (kLine - 1));
+            const int gbase = foff - c0;                              // 128-byte aligned
             const int end = c0 + len;
             const int start = cont ? 0 : c0;
             const int lo = min((start + kLine - 1) & ~(kLine - 1), end);
             const int hi = max(lo, end & ~(kLine - 1));
             const int nf = row_ok ? (hi - lo) / 4 : 0;             // 16-byte pieces of whole lines
-            constexpr int kTail = (kLine + kLanesPerRow - 1) / kLanesPerRow;
-            constexpr int kStep = 4 * kLanesPerRow;                    // floats of a row per instruction
-            // all reads of a batch (and of the tail) go out before any store,
-            // so the wave waits for LDS once per batch
+            // all reads go out before any store, so the wave waits for LDS once
+            // (reads reach at most 2 lines past a staging row's data, for
+            // pieces that are then not stored: the next row, or the slack at
+            // the end of the LDS allocation)
             float tl[kTail];
 #pragma unroll
-            for (int u = 0; u < kTail; ++u) tl[u] = sr[min(hi + j + kLanesPerRow * u, STR - 1)];
+            for (int u = 0; u < kTail; ++u) tl[u] = sr[hi + j + kLanesPerRow * u];
+            // lo is a line boundary whenever nf > 0; (lo & ~3) keeps the 16-byte
+            // reads aligned when nothing is stored
+            const float *rb = sr + (lo & ~3) + 4 * j;
+            const int ob = (gbase + lo + 4 * j) * 4;
             for (int k0 = 0; k0 < kmax; k0 += 4) {
                 v4f v[4];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)   // lo is a line boundary whenever nf > 0
-                    v[u] = *reinterpret_cast<const v4f *>(sr + min((lo & ~3) + (k0 + u) * kStep + 4 * j, STR - 4));
+                for (int u = 0; u < 4; ++u)   // (pieces past kmax re-read the last one)
+                    v[u] = *reinterpret_cast<const v4f *>(rb + min(k0 + u, kmax - 1) * kStep);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if ((k0 + u) * kLanesPerRow + j < nf)
-                        __builtin_nontemporal_store(v[u], reinterpret_cast<v4f *>(gl + lo + (k0 + u) * kStep + 4 * j));
+                for (int u = 0; u < 4; ++u) {
+                    const bool ok = (k0 + u) * kLanesPerRow + j < nf;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4, v[u]), rs,
+                        ok ? (unsigned)(ob + (k0 + u) * kStep * 4) : kOff, 0, 2 /* non-temporal */);
+                }
             }
             if (row_ok)
-                for (int p = start + j; p < lo; p += kLanesPerRow) gl[p] = sr[p];   // head: partial line
+                for (int p = start + j; p < lo; p += kLanesPerRow)       // head: partial line
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sr[p]), rs, (gbase + p) * 4, 0, 0);
             // tail [hi, end): fewer than 32 floats
 #pragma unroll
             for (int u = 0; u < kTail; ++u) {
                 const int p = hi + j + kLanesPerRow * u;
                 if (p < end) {
                     if (next_same_n) sn[p - hi] = tl[u];                     // carried
-                    else if (row_ok) gl[p] = tl[u];                          // partial line
+                    else if (row_ok)                                           // partial line
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(tl[u]), rs, (gbase + p) * 4, 0, 0);
                 }
             }
             // the next task's row starts with a carried line unless this
@@ -644,23 +680,29 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
             const size_t lds = (size_t)slab_lds_floats(KS, Cin, TH, SW, Wp) * sizeof(float);
             const int hchunks = (Hp + TH - 1) / TH;
             const int64_t ntasks = N * Dp * (int64_t)hchunks;
+            // the page's geometries (W = 32, fp32 rows 16-byte aligned) take
+            // instantiations with the geometry folded in
             const void *fn = vec4 ? (const void *)fused3d_f32_slab_kernel<KS, 4>
                                   : (const void *)fused3d_f32_slab_kernel<KS, 1>;
+            if constexpr (KS == 6) {
+                if (vec4 && W == 32 && op == 0 && TH == 8)
+                    fn = (const void *)fused3d_f32_slab_kernel<KS, 4, 32, 8, 0>;
+                else if (vec4 && W == 32 && op == 1 && TH == 7)
+                    fn = (const void *)fused3d_f32_slab_kernel<KS, 4, 32, 7, 1>;
+            }
             per_cu = occupancy(fn, kSlabThreads, lds);
             int64_t wgs = (int64_t)cus * per_cu / gy;
             if (wgs < 1) wgs = 1;
             if (wgs > ntasks) wgs = ntasks;
             const int per = (int)((ntasks + wgs - 1) / wgs);
             const unsigned gx = (unsigned)((ntasks + per - 1) / per);
-            if (vec4)
-                hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 4>), dim3(gx, gy), dim3(kSlabThreads), lds,
-                                   stream, x, w, conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H,
-                                   (int)W, SW, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
-            else
-                hipLaunchKernelGGL((fused3d_f32_slab_kernel<KS, 1>), dim3(gx, gy), dim3(kSlabThreads), lds,
-                                   stream, x, w, conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H,
-                                   (int)W, SW, (int)Cout, Dp, Hp, Wp, TH, hchunks, (int)ntasks, per, out);
-            return hipGetLastError();
+            int a_cin = (int)Cin, a_d = (int)D, a_h = (int)H, a_w = (int)W, a_sw = SW,
+                a_cout = (int)Cout, a_dp = Dp, a_hp = Hp, a_wp = Wp, a_th = TH, a_hc = hchunks,
+                a_nt = (int)ntasks, a_per = per;
+            void *args[] = {(void *)&x, (void *)&w, (void *)&conv_bias, (void *)&bias, &s1, &s2,
+                            &a_cin, &a_d, &a_h, &a_w, &a_sw, &a_cout, &a_dp, &a_hp, &a_wp, &a_th,
+                            &a_hc, &a_nt, &a_per, (void *)&out};
+            return hipLaunchKernel(fn, dim3(gx, gy), dim3(kSlabThreads), args, lds, stream);
         }
     }
     if (op != 0) return hipErrorInvalidValue;    // the direct path has no far-edge taps
