@@ -22,6 +22,7 @@ Operations (POPCORNBENCH pages, one problem each):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 # torch is imported before libct.so is loaded so that libct.so's libamdhip64.so.7
@@ -90,11 +91,16 @@ def ct_version() -> str:
     return lib.ct_version().decode()
 
 
+# The size helpers are pure functions of their integer arguments: each distinct
+# geometry asks the library once (a ctypes call costs microseconds, which is
+# most of a small workload's time per call).
+@functools.lru_cache(maxsize=4096)
 def ct_convT_out_len(n_in: int, k: int, stride: int = 1, pad: int = 0, out_pad: int = 0,
                      dilation: int = 1) -> int:
     return int(lib.ct_convT_out_len(n_in, k, stride, pad, out_pad, dilation))
 
 
+@functools.lru_cache(maxsize=4096)
 def ct_pool_out_len(n_in: int, k: int, stride: int = 0, pad: int = 0) -> int:
     return int(lib.ct_pool_out_len(n_in, k, stride, pad))
 
@@ -130,9 +136,15 @@ def _dev_ptr(t, name, required=True):
     return t.data_ptr()
 
 
+# the current stream's raw handle without building a Stream object, where this
+# torch build has the accessor
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(t, stream):
-    torch = _torch()
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device())
         stream = torch.cuda.current_stream(t.device)
     if isinstance(stream, int):
         return stream

@@ -421,7 +421,9 @@ struct PolyGeom {
     static constexpr int kLdsFloats = kWfrag + kCO + WW * CIN4 * kStr;
 };
 
-template <int CIN4, int K, int DIL, int S, int NB, int WW>
+// PODD: the parity of pad, which fixes how the two residue classes pair up
+// into 8-byte stores (compile-time, so the store code has no branches on it).
+template <int CIN4, int K, int DIL, int S, int NB, int WW, int PODD>
 __global__ __launch_bounds__(64 * WW, 1)
 void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
@@ -469,6 +471,19 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
     const int per = (int)(ntiles / nw), rem = (int)(ntiles % nw);
     const int t_begin = (int)(gw * per + (gw < rem ? gw : rem));
     const int t_end = t_begin + per + (gw < rem ? 1 : 0);
+
+    // byte offsets of this lane's output rows co = 16m + 4kq + r of the channel
+    // block within a batch item (an item's output is below 2^31 bytes)
+    int rowb[4][4];
+    bool rowok[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int co = cog * kCO + 16 * m + 4 * kq + r;
+            rowok[m][r] = co < Cout;
+            rowb[m][r] = co * Lo * 4;
+        }
 
     // strip piece q = ci * (kTs/4) + t4 covers inputs q0 - HP + 4*t4 .. +3
     // (L % 4 == 0 and q0 - HP = 0 mod 4: a piece is wholly inside or outside
@@ -584,51 +599,57 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
         // outputs reach past either end of the row, and odd Lo, take one
         // 4-byte store per output instead.
         static_assert(S == 2, "paired stores are written for stride 2");
-        const bool podd = pad & 1;
+        constexpr bool podd = PODD != 0;
         const int olo = 2 * q0 - pad, ohi = 2 * (q0 + G::kTQ) + 1 - pad;   // tile's output span
         const bool paired = (Lo % 2 == 0) && olo >= 0 && ohi < Lo;
         if (paired) {
+            typedef float v2f_ __attribute__((ext_vector_type(2)));
+            typedef int v2i_ __attribute__((ext_vector_type(2)));
+            // byte offset of this lane's first pair in row co = 16m + 4kq + r
+            // of the channel block (rowb[m][r] = co*Lo*4, hoisted below), and
+            // an offset past the output for lanes that store nothing (with
+            // the constant per-block offsets added it stays below 2^32 and
+            // above the output's size)
+            constexpr unsigned kOff = 0x80000000u;
+            const int ob = (2 * (q0 + col) + (podd ? 1 : 0) - pad) * 4;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int co = cog * kCO + 16 * m + 4 * kq + r;
-                    const int rowoff = co * Lo;
+                    const unsigned base = rowok[m][r] ? (unsigned)(rowb[m][r] + ob) : kOff;
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        const int q = q0 + 16 * b + col;
                         float v0, v1;
-                        int o;
-                        bool ok = co < Cout;
+                        unsigned off = base + 128u * b;            // 16 q = 32 outputs per block
                         if (!podd) {
                             v0 = acc[0][m][b][r];
                             v1 = acc[1][m][b][r];
-                            o = 2 * q - pad;
                         } else {
                             // lane col takes class 0 of q+1: lane col+1, or lane 0 of block b+1
                             const float nx = __int_as_float(__builtin_amdgcn_update_dpp(
                                 0, __float_as_int(acc[0][m][b][r]), 0x12F, 0xf, 0xf, false));   // row_ror:15
-                            const float nb = b + 1 < NB ? __int_as_float(__builtin_amdgcn_update_dpp(
-                                0, __float_as_int(acc[0][m][b + 1 < NB ? b + 1 : b][r]), 0x12F, 0xf, 0xf, false))
-                                                        : 0.0f;
                             v0 = acc[1][m][b][r];
-                            v1 = col == 15 ? nb : nx;
-                            o = 2 * q + 1 - pad;
-                            ok = ok && !(b == NB - 1 && col == 15);   // its partner is in the next tile
+                            if (b + 1 < NB) {
+                                const float nb = __int_as_float(__builtin_amdgcn_update_dpp(
+                                    0, __float_as_int(acc[0][m][b + 1 < NB ? b + 1 : b][r]), 0x12F, 0xf, 0xf, false));
+                                v1 = col == 15 ? nb : nx;
+                            } else {
+                                v1 = nx;
+                                if (col == 15) off = kOff;         // its partner is in the next tile
+                            }
                         }
-                        typedef float v2f_ __attribute__((ext_vector_type(2)));
-                        typedef int v2i_ __attribute__((ext_vector_type(2)));
-                        const int off = ok ? (rowoff + o) * 4 : 0x7ffffff0;
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_, (v2f_){v0, v1}), yr, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_, (v2f_){v0, v1}), yr,
+                                                              (int)off, 0, 0);
                     }
                     if (podd) {
-                        // the unpaired ends: class 0 at q0 (o = 2*q0 - pad) and
-                        // class 1 at the tile's last q
+                        // the unpaired ends: class 0 at q0 (o = 2*q0 - pad, lane 0)
+                        // and class 1 at the tile's last q (lane 15 of the last block)
                         const bool first = col == 0, last = col == 15;
                         const float v = first ? acc[0][m][0][r] : acc[1][m][NB - 1][r];
-                        const int o = first ? 2 * q0 - pad : 2 * (q0 + G::kTQ - 1) + 1 - pad;
-                        const int off = (co < Cout && (first || last)) ? (rowoff + o) * 4 : 0x7ffffff0;
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, off, 0, 0);
+                        const unsigned off = !rowok[m][r] || !(first || last) ? kOff
+                                             : first ? (unsigned)(rowb[m][r] + (2 * q0 - pad) * 4)
+                                                     : (unsigned)(rowb[m][r] + (2 * (q0 + G::kTQ - 1) + 1 - pad) * 4);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, (int)off, 0, 0);
                     }
                 }
         } else {
@@ -737,7 +758,8 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     const int64_t qb = (Lo + pad + S - 1) / S;
     const int tq_per_n = (int)((qb - qa4 + G::kTQ - 1) / G::kTQ);
     const int64_t ntiles = N * tq_per_n;
-    const void *fn = (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW>;
+    const void *fn = (pad & 1) ? (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 1>
+                               : (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 0>;
     const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
     hipError_t e = allow_dynamic_lds(fn, lds);
     if (e != hipSuccess) return e;
@@ -745,9 +767,14 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
     int64_t gx = (int64_t)cus * per_cu / gy;
     if (gx < 1) gx = 1;
-    hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW>), dim3((unsigned)gx, gy),
-                       dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
-                       (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
+    if (pad & 1)
+        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 1>), dim3((unsigned)gx, gy),
+                           dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
+                           (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
+    else
+        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 0>), dim3((unsigned)gx, gy),
+                           dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
+                           (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
     return hipGetLastError();
 }
 
