@@ -84,6 +84,10 @@ FUSED_GENERAL = [
     (1, 2, 5, 2, 2, 4, 3, 2, 1, 1, 2, 2, "f32"),      # one input plane pair
     (5, 3, 16, 7, 20, 23, 3, 2, 1, 1, 2, 2, "f32"),   # scalar rows, ragged W
     (2, 3, 16, 1, 1, 1, 3, 2, 1, 1, 2, 2, "f32"),     # a single input voxel
+    # Cin 3, W 32 with output padding 1: the compiled-in geometry (7 rows per task)
+    (2, 3, 16, 4, 9, 32, 3, 2, 1, 1, 2, 2, "f32"),
+    (3, 3, 16, 5, 20, 32, 3, 2, 1, 1, 2, 2, "f32"),
+    (1, 3, 24, 3, 7, 32, 3, 2, 1, 1, 2, 2, "f32"),
 ]
 
 

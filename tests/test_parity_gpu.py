@@ -85,6 +85,13 @@ FUSED_SMALL = [
     (3, 4, 40, 5, 19, 13),
     (9, 1, 16, 4, 33, 32),
     (2, 2, 17, 3, 70, 9),
+    # Cin 3, W 32: the instantiation with the page's geometry compiled in (8
+    # pooled rows per task): one exact chunk, a ragged last chunk, ragged Cout
+    # (two channel blocks), and streams carried across batch items
+    (2, 3, 16, 5, 9, 32),
+    (3, 3, 16, 4, 20, 32),
+    (1, 3, 20, 3, 33, 32),
+    (16, 3, 16, 4, 17, 32),
 ]
 
 
