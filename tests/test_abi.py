@@ -211,3 +211,24 @@ def test_python_binding_requires_gpu_tensors():
     x = torch.zeros(1, 1, 4, 4, 4)
     with pytest.raises(ValueError):
         ct.ct_avgpool3d(x, out=torch.zeros(1, 1, 2, 2, 2))
+
+
+def test_forwarding_module_reaches_the_library():
+    """The CPython module _ctcall forwards each compute call to the same C
+    entry point (argument order of ct.h): null buffers come back as CT_EINVAL
+    with the entry point's own message."""
+    call = ct._call
+    assert call is not None, "transposed_conv_pooling_amd._ctcall is not built"
+    cases = [
+        (call.fused, (0, ct.CT_F32, FAKE, ct.CT_F32, 0, 0, 0.5, 1.0, 2, 3, 8, 16, 16, 16,
+                      3, 2, 1, 0, 2, 0, FAKE2, 0), "convT3d_scale_pool_bias"),
+        (call.convT3d, (FAKE, ct.CT_F32, 0, ct.CT_F32, 0, 1, 1, 1, 1, 1, 1, 3, 2, 1, 0, FAKE2, 0),
+         "convT3d"),
+        (call.avgpool3d, (False, FAKE, 1, 1, 2, 2, 4, 3, 2, 1, 1, 0, 0), "avgpool3d"),
+        (call.avgpool3d, (True, 0, 1, 1, 2, 2, 4, 3, 2, 1, 1, FAKE2, 0), "avgpool3d_bf16"),
+        (call.convT1d, (FAKE, ct.CT_F32, FAKE2, ct.CT_F32, 0, 1, 1, 8, 1, 3, 1, 0, 1, 0, 0, 0),
+         "convT1d"),
+    ]
+    for fn, args, name in cases:
+        assert fn(*args) == ct.CT_EINVAL, name
+        assert ct.ct_last_error().startswith(name + ":"), (name, ct.ct_last_error())

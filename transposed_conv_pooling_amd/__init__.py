@@ -72,6 +72,13 @@ def _load():
 
 lib = _load()
 
+# The CPython forwarding module built beside libct.so (same entry points, same
+# argument order); the ctypes functions above serve where it is not built.
+try:
+    from . import _ctcall as _call
+except ImportError:          # pragma: no cover - only a partial build lacks it
+    _call = None
+
 
 class CtError(RuntimeError):
     def __init__(self, status: int, message: str):
@@ -103,6 +110,17 @@ def ct_convT_out_len(n_in: int, k: int, stride: int = 1, pad: int = 0, out_pad: 
 @functools.lru_cache(maxsize=4096)
 def ct_pool_out_len(n_in: int, k: int, stride: int = 0, pad: int = 0) -> int:
     return int(lib.ct_pool_out_len(n_in, k, stride, pad))
+
+
+@functools.lru_cache(maxsize=4096)
+def _fused_dims(D, H, W, k, stride, pad, out_pad, pool_k, pool_s):
+    """Pooled output sizes of the fused chain per spatial axis (0 where empty)."""
+    ps = pool_s if pool_s else pool_k
+    dims = []
+    for n in (D, H, W):
+        o = ct_convT_out_len(n, k, stride, pad, out_pad, 1)
+        dims.append(ct_pool_out_len(o, pool_k, ps, 0) if o > 0 else 0)
+    return tuple(dims)
 
 
 def _check(status: int):
@@ -165,11 +183,7 @@ def ct_convT3d_scale_pool_bias(x, w, conv_bias=None, bias=None, scale1: float = 
     Cin2, Cout, k = w.shape[0], w.shape[1], w.shape[2]
     if Cin2 != Cin or tuple(w.shape[2:]) != (k, k, k):
         raise ValueError(f"weight shape {tuple(w.shape)} does not match input {tuple(x.shape)}")
-    ps = pool_s if pool_s else pool_k
-    dims = []
-    for n in (D, H, W):
-        o = ct_convT_out_len(n, k, stride, pad, out_pad, 1)
-        dims.append(ct_pool_out_len(o, pool_k, ps, 0) if o > 0 else 0)
+    dims = _fused_dims(D, H, W, k, stride, pad, out_pad, pool_k, pool_s)
     if out is None:
         out = torch.empty((N, Cout, *[max(d, 0) for d in dims]), dtype=torch.float32,
                           device=x.device)
@@ -178,11 +192,11 @@ def ct_convT3d_scale_pool_bias(x, w, conv_bias=None, bias=None, scale1: float = 
     for name, b in (("conv_bias", conv_bias), ("bias", bias)):
         if b is not None and (b.dtype != torch.float32 or b.numel() != Cout):
             raise ValueError(f"{name} must be float32 with {Cout} elements")
-    st = lib.ct_convT3d_scale_pool_bias(
-        _dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
-        _dev_ptr(conv_bias, "conv_bias", False), _dev_ptr(bias, "bias", False),
-        float(scale1), float(scale2), N, Cin, D, H, W, Cout, k, stride, pad, out_pad,
-        pool_k, pool_s, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    args = (_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
+            _dev_ptr(conv_bias, "conv_bias", False) or 0, _dev_ptr(bias, "bias", False) or 0,
+            float(scale1), float(scale2), N, Cin, D, H, W, Cout, k, stride, pad, out_pad,
+            pool_k, pool_s, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    st = _call.fused(*args) if _call else lib.ct_convT3d_scale_pool_bias(*args)
     _check(st)
     return out
 
@@ -204,9 +218,10 @@ def ct_convT3d(x, w, bias=None, stride: int = 2, pad: int = 1, out_pad: int = 0,
         raise ValueError(f"out must be float32 {(N, Cout, *dims)}")
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Cout):
         raise ValueError(f"bias must be float32 with {Cout} elements")
-    st = lib.ct_convT3d(_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
-                        _dev_ptr(bias, "bias", False), N, Cin, D, H, W, Cout, k, stride, pad,
-                        out_pad, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    args = (_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
+            _dev_ptr(bias, "bias", False) or 0, N, Cin, D, H, W, Cout, k, stride, pad, out_pad,
+            _dev_ptr(out, "out"), _stream_handle(x, stream))
+    st = _call.convT3d(*args) if _call else lib.ct_convT3d(*args)
     _check(st)
     return out
 
@@ -225,9 +240,12 @@ def ct_avgpool3d(x, k: int = 3, stride: int = 2, pad: int = 1, count_include_pad
         out = torch.empty((N, C, *[max(d, 0) for d in dims]), dtype=dt, device=x.device)
     elif tuple(out.shape) != (N, C, *dims) or out.dtype != dt:
         raise ValueError(f"out must be {dt} {(N, C, *dims)}")
-    fn = lib.ct_avgpool3d if dt == torch.float32 else lib.ct_avgpool3d_bf16
-    st = fn(_dev_ptr(x, "x"), N, C, D, H, W, k, stride, pad,
-            1 if count_include_pad else 0, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    args = (_dev_ptr(x, "x"), N, C, D, H, W, k, stride, pad, 1 if count_include_pad else 0,
+            _dev_ptr(out, "out"), _stream_handle(x, stream))
+    if _call:
+        st = _call.avgpool3d(dt != torch.float32, *args)
+    else:
+        st = (lib.ct_avgpool3d if dt == torch.float32 else lib.ct_avgpool3d_bf16)(*args)
     _check(st)
     return out
 
@@ -248,9 +266,10 @@ def ct_convT1d(x, w, bias=None, stride: int = 1, pad: int = 0, dilation: int = 1
         raise ValueError(f"out must be float32 {(N, Cout, Lo)}")
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Cout):
         raise ValueError(f"bias must be float32 with {Cout} elements")
-    st = lib.ct_convT1d(_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
-                        _dev_ptr(bias, "bias", False), N, Cin, L, Cout, K, stride, pad,
-                        dilation, out_pad, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    args = (_dev_ptr(x, "x"), _dtype_code(x), _dev_ptr(w, "w"), _dtype_code(w),
+            _dev_ptr(bias, "bias", False) or 0, N, Cin, L, Cout, K, stride, pad, dilation,
+            out_pad, _dev_ptr(out, "out"), _stream_handle(x, stream))
+    st = _call.convT1d(*args) if _call else lib.ct_convT1d(*args)
     _check(st)
     return out
 

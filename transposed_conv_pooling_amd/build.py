@@ -58,7 +58,26 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if rc != 0:
         raise RuntimeError("hipcc link failed:\n" + "\n".join(msgs))
     os.replace(tmp, LIB)
+    build_call(verbose)
     return LIB
+
+
+def build_call(verbose: bool = False) -> str:
+    """The CPython module _ctcall (argument forwarding into libct.so), with gcc
+    against this interpreter's headers; libct.so is found next to it."""
+    import sysconfig
+    src = os.path.join(PKG, "_ctcall.c")
+    dst = os.path.join(PKG, "_ctcall" + sysconfig.get_config_var("EXT_SUFFIX"))
+    tmp = dst + ".tmp"
+    cmd = ["gcc", "-O2", "-shared", "-fPIC", "-Wall", "-I", sysconfig.get_paths()["include"],
+           "-I", INCLUDE, "-o", tmp, src, "-L", PKG, "-l:libct.so", "-Wl,-rpath,$ORIGIN"]
+    rc, msgs = _run(cmd, verbose)
+    if verbose and msgs:
+        print("\n".join(msgs))
+    if rc != 0:
+        raise RuntimeError("gcc (_ctcall) failed:\n" + "\n".join(msgs))
+    os.replace(tmp, dst)
+    return dst
 
 
 if __name__ == "__main__":

@@ -312,7 +312,11 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     }
     __syncthreads();
     // A fragments: lane (g, l%16) of channel block cb, k-step j, half h holds
-    // Weff_h[ci0 .. ci0+7][co][tap] with kappa = 32j + 8g = tap*Cin8 + ci0
+    // Weff_h[ci0 .. ci0+7][co][tap] with kappa = 32j + 8g = tap*Cin8 + ci0.
+    // Tap 7 (input offsets 1,1,1) takes the single weight w[ci,co,0,0,0], so
+    // its hi part is exact and its lo part zero: k-steps holding only tap 7
+    // (the last Cin8/32 of them when Cin8 is a multiple of 32) skip the lo pass.
+    constexpr int kLoSteps = (Cin8 % 32 == 0) ? KSTEPS - Cin8 / 32 : KSTEPS;
     bf16x8 A[2][KSTEPS][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -320,6 +324,7 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
         for (int j = 0; j < KSTEPS; ++j)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                if (h == 1 && j >= kLoSteps) continue;
                 const int cl = 16 * (2 * cp + i) + col;
                 const int kap = 32 * j + 8 * g;
                 const int tap = kap / Cin8, ci0 = kap % Cin8;
@@ -398,8 +403,10 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                 const bf16x8 B = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(sb + boff[j]));
                 a0h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][0], B, a0h, 0, 0, 0);
                 a1h = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][0], B, a1h, 0, 0, 0);
-                a0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][1], B, a0l, 0, 0, 0);
-                a1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][1], B, a1l, 0, 0, 0);
+                if (j < kLoSteps) {
+                    a0l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][j][1], B, a0l, 0, 0, 0);
+                    a1l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][j][1], B, a1l, 0, 0, 0);
+                }
             }
             const int opos = obase + hh * Wp + wv;
 #pragma unroll
