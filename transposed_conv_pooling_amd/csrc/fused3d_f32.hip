@@ -283,7 +283,7 @@ constexpr int kSlabPrefetch = 4;   // slab pieces each loader lane keeps in flig
 constexpr int kLine = 32;          // floats per 128-byte line
 constexpr int kLineSlack = 2 * kLine;   // LDS floats after the staging sets (see the store waves)
 // 4 compute waves, 2 loader waves, 2 store waves: 8 waves, so that three
-// workgroups fit a CU's 32 wave slots (with under 64 VGPRs a wave).  vmcnt counts a wave's
+// workgroups fit a CU's 32 wave slots (with at most 64 VGPRs a wave).  vmcnt counts a wave's
 // loads and stores together and retires them in order, so a wave that both
 // stores and prefetches would wait for its earlier stores before each slab;
 // here only the loader waves load and only the store waves store.
@@ -308,8 +308,8 @@ __host__ __device__ inline int64_t stage_offset(int64_t ks, int64_t cin, int64_t
 {
     return (ks * 64 + 2 * slab_floats(cin, th, w) + 3) & ~int64_t(3);
 }
-// (plus a line of slack: the store waves read whole pieces up to a line past
-// a staging row's end, for pieces they then do not store)
+// (plus two lines of slack: the store waves read whole pieces up to two lines
+// past a staging row's end, for pieces they then do not store)
 __host__ __device__ inline int64_t slab_lds_floats(int64_t ks, int64_t cin, int64_t th, int64_t w, int64_t wp)
 {
     return stage_offset(ks, cin, th, w) + 2 * 16 * stage_stride(th, wp) + kLineSlack;
