@@ -15,7 +15,8 @@ most time (timed live with HIP events on the launch stream), and the CPU oracle
 timed on a bounded sample of the same workloads.
 
 Every op is cold by construction: it cycles through enough copies of its
-input and output buffers (at least 4, more than 512 MB in all) that no call
+input and output buffers (at least 4, more than 512 MB in all, and more than
+512 MB of inputs alone) that no call
 finds them in the 256 MB Infinity Cache; `ms_warm` repeats one buffer set.
 Beside the 8 TB/s peak, each op's GB/s is also given as a fraction of a plain
 1 GiB device copy measured in the same run (`copy_GB_s`).  The small fused
@@ -150,13 +151,20 @@ def measured_traffic(op):
 COLD_BYTES = 512 << 20     # twice the 256 MB Infinity Cache
 
 
-def rotation_count(set_bytes):
+def rotation_count(set_bytes, input_bytes=None):
     """Buffer sets an op cycles through so that no call finds its inputs or
-    outputs left in the 256 MB Infinity Cache by an earlier call: at least 4
-    sets and more than 512 MB in all, or one set when a single set is larger."""
+    outputs left in the 256 MB Infinity Cache by an earlier call: one set when
+    a single set's traffic is larger than 512 MB; else at least 4 sets, more
+    than 512 MB in all, and more than 512 MB of the inputs alone (some kernels'
+    non-temporal stores leave no output in the cache, but every input read is
+    cached, so a rotation whose inputs fit the cache would find each input
+    still there when its turn came again)."""
     if set_bytes > COLD_BYTES:
         return 1
-    return max(4, COLD_BYTES // set_bytes + 1)
+    n = max(4, COLD_BYTES // set_bytes + 1)
+    if input_bytes:
+        n = max(n, COLD_BYTES // input_bytes + 1)
+    return n
 
 
 class Op:
@@ -205,8 +213,8 @@ def make_ops(names, dev):
     def rotate(*ts):
         """Buffer sets [(t0, t1, ...)]: the given tensors first, then copies
         (inputs) or fresh allocations (outputs share shapes) up to the
-        rotation count of their total size."""
-        n = rotation_count(nbytes(*ts))
+        rotation count of their total size and of the input t0."""
+        n = rotation_count(nbytes(*ts), nbytes(ts[0]))
         return [tuple(ts)] + [tuple(t.clone() for t in ts) for _ in range(n - 1)]
 
     if "fused3d_f32" in names:

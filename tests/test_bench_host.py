@@ -119,3 +119,16 @@ def test_every_traced_kernel_maps_to_an_op():
         op, src, nbytes = key
         assert op and nbytes > 0 and os.path.exists(
             os.path.join(bench.ROOT, "transposed_conv_pooling_amd", "csrc", src)), (n, key)
+
+
+def test_rotation_keeps_every_call_cold():
+    """Buffer sets per op: a set whose traffic exceeds 512 MB alone is enough;
+    otherwise at least 4 sets, more than 512 MB in all and more than 512 MB of
+    inputs alone (the fused workloads' inputs are 25 MB and 17 MB)."""
+    import bench
+    mb = 1 << 20
+    assert bench.rotation_count(1200 * mb, 25 * mb) == 1
+    assert bench.rotation_count(9600 * mb) == 1
+    for set_mb, in_mb in [(137, 24), (72, 16), (152, 24), (200, 190), (1, 1)]:
+        n = bench.rotation_count(set_mb * mb, in_mb * mb)
+        assert n >= 4 and n * set_mb * mb > bench.COLD_BYTES and n * in_mb * mb > bench.COLD_BYTES
