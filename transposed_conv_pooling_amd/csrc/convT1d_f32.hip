@@ -749,8 +749,14 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
 {
     if (!convT1d_f32_poly_supported(Cin, K, stride, dilation, L, x)) return hipErrorInvalidValue;
     constexpr int S = 2;
-    constexpr int NB = 2;      // 32-q tiles: both classes' accumulators stay in registers
-    typedef PolyGeom<32, 5, 3, S, NB, kWaveWW> G;
+    // 96-q tiles (6 blocks of 16) and 4-wave workgroups: the two classes'
+    // 48 accumulators of a wave (192 registers) live in the accumulation
+    // registers beside 256 vector registers, at one wave per SIMD.  Against
+    // 32-q tiles at two waves per SIMD (no room for more accumulators) the
+    // larger tile spreads each tile's strip handling and store setup over
+    // three times the MFMAs: 1.04 -> 0.91 ms at the page's stride-2 shape.
+    constexpr int NB = 6, WW = 4;
+    typedef PolyGeom<32, 5, 3, S, NB, WW> G;
     const int64_t Lo = (L - 1) * S - 2 * (int64_t)pad + (int64_t)dilation * (K - 1) + out_pad + 1;
     // q covers o + pad = S*q + rho for every output: q in [pad/S, ceil((Lo + pad)/S)),
     // started at a multiple of 4 so that strip pieces stay float4-aligned
@@ -758,8 +764,8 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     const int64_t qb = (Lo + pad + S - 1) / S;
     const int tq_per_n = (int)((qb - qa4 + G::kTQ - 1) / G::kTQ);
     const int64_t ntiles = N * tq_per_n;
-    const void *fn = (pad & 1) ? (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 1>
-                               : (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 0>;
+    const void *fn = (pad & 1) ? (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 1>
+                               : (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 0>;
     const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
     hipError_t e = allow_dynamic_lds(fn, lds);
     if (e != hipSuccess) return e;
@@ -768,11 +774,11 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     int64_t gx = (int64_t)cus * per_cu / gy;
     if (gx < 1) gx = 1;
     if (pad & 1)
-        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 1>), dim3((unsigned)gx, gy),
+        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 1>), dim3((unsigned)gx, gy),
                            dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
                            (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
     else
-        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, kWaveWW, 0>), dim3((unsigned)gx, gy),
+        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 0>), dim3((unsigned)gx, gy),
                            dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
                            (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
     return hipGetLastError();
