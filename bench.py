@@ -781,7 +781,8 @@ def main():
     for op in ops:
         ms = [a.elapsed_time(b) for a, b in ev[op.name]]
         avg = float(np.mean(ms))
-        d = {"ms": round(avg, 5), "ms_min": round(float(np.min(ms)), 5),
+        d = {"ms": round(avg, 5), "ms_median": round(float(np.median(ms)), 5),
+             "ms_min": round(float(np.min(ms)), 5),
              "alg_bytes": op.alg_bytes, "GB_s": round(op.alg_bytes / avg / 1e6, 1),
              "hbm_frac": round(op.alg_bytes / avg / 1e6 / HBM_PEAK_GBS, 4)}
         if copy_gbs:
