@@ -63,7 +63,8 @@ typedef enum {
  *   (in - 1) * stride - 2 * pad + dilation * (k - 1) + out_pad + 1.
  * [p50], passage deriving the ConvTranspose3d output shape (16/32/32 ->
  * 31/63/63); [p74], opening passage (L_out = L + 12 at k5 d3).
- * Pure host arithmetic; may return a value <= 0 for impossible geometry.
+ * Pure host arithmetic, evaluated without overflow; may return a value <= 0
+ * for impossible geometry, and returns -1 when the length lies outside int64.
  */
 CT_API int64_t ct_convT_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad,
                          int64_t out_pad, int64_t dilation);
@@ -72,8 +73,9 @@ CT_API int64_t ct_convT_out_len(int64_t in, int64_t k, int64_t stride, int64_t p
  * Output length of an average pool along one axis, floor mode:
  *   floor((in + 2 * pad - k) / stride) + 1.
  * [p50], passage on AvgPool3d(2) (31 -> 15); [p46], opening passage
- * (128 -> 64, 256 -> 128).  Returns <= 0 when no window fits.
- * stride == 0 means stride = k (PyTorch's default).
+ * (128 -> 64, 256 -> 128).  Returns <= 0 when no window fits, -1 when the
+ * length lies outside int64 (evaluated without overflow).  stride == 0 means
+ * stride = k (PyTorch's default).
  */
 CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad);
 

@@ -63,6 +63,22 @@ def test_size_helpers_match_the_pages():
     assert ct.ct_pool_out_len(1, 3, 2, 0) == 0
 
 
+def test_size_helpers_report_lengths_past_int64():
+    i64max = 2**63 - 1
+    # (in - 1) * stride alone is past int64; exact 128-bit evaluation gives -1
+    assert ct.ct_convT_out_len(2**62, 3, 2**30, 0, 0, 1) == -1
+    assert ct.ct_convT_out_len(2, 2**40, 1, 0, 0, 2**40) == -1
+    # the largest representable length still comes back exactly
+    assert ct.ct_convT_out_len(i64max, 1, 1, 0, 0, 1) == i64max
+    assert ct.ct_convT_out_len(2**62, 1, 2, 0, 0, 1) == 2**63 - 1
+    assert ct.ct_convT_out_len(2**62 + 1, 1, 2, 0, 0, 1) == -1
+    # in + 2 * pad is past int64, the quotient is not
+    assert ct.ct_pool_out_len(i64max, 4, 4, 2**30) == (i64max + 2**31 - 4) // 4 + 1
+    assert ct.ct_pool_out_len(i64max, 1, 1, 2**30) == -1
+    assert ct.ct_pool_out_len(-i64max - 1, 1, 1, 0) == -i64max - 1
+    assert ct.ct_pool_out_len(-i64max - 1, 2, 1, 0) == -1
+
+
 def fused(**kw):
     a = dict(x=FAKE, xd=ct.CT_F32, w=FAKE2, wd=ct.CT_F32, cb=None, b=None, s1=0.5, s2=1.0,
              N=2, Cin=3, D=8, H=16, W=16, Cout=16, k=3, stride=2, pad=1, out_pad=0,

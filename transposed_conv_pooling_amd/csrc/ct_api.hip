@@ -66,13 +66,6 @@ bool overlap(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
-int64_t floor_div(int64_t a, int64_t b)
-{
-    int64_t q = a / b;
-    if ((a % b != 0) && (a < 0)) --q;
-    return q;
-}
-
 int dtype_size(int dt) { return dt == CT_F32 ? 4 : dt == CT_BF16 ? 2 : 0; }
 
 ct_status hip_status(hipError_t e, const char *what)
@@ -133,17 +126,25 @@ ct_status check_convT3d(const char *fn, const void *x, int x_dtype, const void *
 
 extern "C" {
 
+// Both size formulas are evaluated in 128-bit arithmetic, where no product or
+// sum of 64-bit operands overflows; a length outside int64 returns -1.
 int64_t ct_convT_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad,
                          int64_t out_pad, int64_t dilation)
 {
-    return (in - 1) * stride - 2 * pad + dilation * (k - 1) + out_pad + 1;
+    const __int128 r = (__int128)(in - (__int128)1) * stride - (__int128)2 * pad +
+                       (__int128)dilation * (k - (__int128)1) + out_pad + 1;
+    return (r > INT64_MAX || r < INT64_MIN) ? -1 : (int64_t)r;
 }
 
 int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pad)
 {
     if (stride == 0) stride = k;
     if (stride <= 0) return 0;
-    return floor_div(in + 2 * pad - k, stride) + 1;
+    const __int128 num = (__int128)in + (__int128)2 * pad - k;
+    __int128 q = num / stride;
+    if (num % stride != 0 && num < 0) --q;
+    const __int128 r = q + 1;
+    return (r > INT64_MAX || r < INT64_MIN) ? -1 : (int64_t)r;
 }
 
 const char *ct_status_str(int status)
@@ -356,11 +357,11 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
     if (Lo <= 0) return fail(CT_EINVAL, "convT1d: empty output (L_out=%lld)", (long long)Lo);
     if (!aligned(x, xs) || !aligned(w, ws) || !aligned(out, 4) || (bias && !aligned(bias, 4)))
         return fail(CT_EINVAL, "convT1d: misaligned pointer");
-    int64_t nx, nw, no;
+    int64_t nx, nw, no, nb;
     if (!prod({N, Cin, L, (int64_t)xs}, &nx) || !prod({Cin, Cout, (int64_t)K, (int64_t)ws}, &nw) ||
-        !prod({N, Cout, Lo, 4}, &no))
+        !prod({N, Cout, Lo, 4}, &no) || !prod({Cout, 4}, &nb))
         return fail(CT_EINVAL, "convT1d: tensor size overflows");
-    if (overlap(out, no, x, nx) || overlap(out, no, w, nw) || overlap(out, no, bias, Cout * 4))
+    if (overlap(out, no, x, nx) || overlap(out, no, w, nw) || overlap(out, no, bias, nb))
         return fail(CT_EINVAL, "convT1d: out overlaps an input");
     if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "convT1d: x and w dtypes must match");
 
