@@ -19,8 +19,10 @@ input and output buffers (at least 4, more than 512 MB in all, and more than
 512 MB of inputs alone) that no call
 finds them in the 256 MB Infinity Cache; `ms_warm` repeats one buffer set.
 Beside the 8 TB/s peak, each op's GB/s is also given as a fraction of a plain
-1 GiB device copy measured in the same run (`copy_GB_s`).  The small fused
-workload [2,3,8,16,16] is timed per call (launch-bound) outside the step.
+1 GiB device copy measured in the same run (`copy_GB_s`), and `write_GB_s`
+gives the rate of a write-only stream of non-constant data, the ceiling of the
+write-dominated fused ops.  The small fused workload [2,3,8,16,16] is timed
+per call (launch-bound) outside the step.
 
   python bench.py [--steps K] [--warmup W] [--ops a,b] [--no-cpu-baseline]
   python bench.py --ops copy        # plain 1 GiB device copy (counter calibration)
@@ -607,6 +609,32 @@ def time_copy(torch, dev, stream, reps=20):
     return round(2 * 4 * n / ms / 1e6, 1)
 
 
+def time_write(torch, dev, stream, reps=20):
+    """GB/s of a write-only stream of non-constant data: 1 GiB of fp32 written
+    from a 1 MiB cache-resident source broadcast over it (torch's elementwise
+    copy, 16-byte stores).  The write-dominated fused ops are bound by this
+    rate rather than by the copy rate; a constant fill runs faster on this
+    part and is no reference for real data."""
+    n = 1 << 28
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    src = torch.randn(1 << 18, generator=g, device=dev)
+    dst = torch.empty((1024, 1 << 18), dtype=torch.float32, device=dev)
+    view = src.expand(1024, 1 << 18)
+    for _ in range(3):
+        dst.copy_(view)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(view)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(4 * n / ms / 1e6, 1)
+
+
 def time_small_fused(torch, dev, stream, reps=200):
     """Per-call time of the small fused workload [2,3,8,16,16] -> [2,16,7,15,15]
     (cache-resident, launch-bound): GPU time per call from HIP events around
@@ -775,6 +803,7 @@ def main():
     copy_gbs = None
     if "copy" not in names:
         copy_gbs = time_copy(torch, dev, stream)
+    write_gbs = time_write(torch, dev, stream)
 
     per_op = {}
     total_bytes = 0
@@ -857,6 +886,7 @@ def main():
         "ops": per_op,
         "roofline": roof,
         "copy_GB_s": copy_gbs,
+        "write_GB_s": write_gbs,
         "small_fused_c1": small,
         "cpu_baseline": cpu,
     }
