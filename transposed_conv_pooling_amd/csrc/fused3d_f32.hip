@@ -367,9 +367,12 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
     // Slab rows then carry SW - W >= 1 zero columns after the row, zeroed
     // here in both slab buffers (the loaders write only columns < W); rows
     // and planes past the input are zero-filled by the loaders.
-    for (int e = threadIdx.x; e < 2 * Cin * 2 * R * (SW - W); e += kSlabThreads) {
-        const int row = e / (SW - W), c = e - row * (SW - W);
-        slabs[row * SW + W + c] = 0.0f;
+    if (SW > W) {
+        const int zc = SW - W;                 // zero columns per slab row
+        for (int e = threadIdx.x; e < 2 * Cin * 2 * R * zc; e += kSlabThreads) {
+            const int row = e / zc, c = e - row * zc;
+            slabs[row * SW + W + c] = 0.0f;
+        }
     }
 
     // Three roles, one pipeline stage per task, one barrier per stage (after
