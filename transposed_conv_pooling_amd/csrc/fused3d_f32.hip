@@ -328,6 +328,7 @@ void fused3d_f32_slab_kernel(const float *__restrict__ x, const float *__restric
                              int tasks_per_wg, float *__restrict__ out)
 {
     static_assert(KS > 0, "the slab kernel has a compile-time channel count");
+    (void)Cin_;                                // equal to KS / 2, passed for the launch record
     const int Cin = KS / 2;
     const int W = GW > 0 ? GW : W_;
     const int SW = GW > 0 ? GW + (GOP ? (VEC == 4 ? 4 : 1) : 0) : SW_;
