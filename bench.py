@@ -798,7 +798,7 @@ def main():
         torch.cuda.synchronize()
         warm[op.name] = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
-    # a plain 1 GiB device copy: the bandwidth this box's HBM gives a simple
+    # a plain 1 GiB device copy: the bandwidth this machine's HBM gives a simple
     # stream, the second denominator beside the 8 TB/s peak
     copy_gbs = None
     if "copy" not in names:
