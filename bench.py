@@ -639,7 +639,8 @@ def time_small_fused(torch, dev, stream, reps=200):
     """Per-call time of the small fused workload [2,3,8,16,16] -> [2,16,7,15,15]
     (cache-resident, launch-bound): GPU time per call from HIP events around
     `reps` back-to-back calls, and host time per call (enqueue rate, the
-    same calls timed with a wall clock up to the last enqueue)."""
+    same calls timed with a wall clock up to the last enqueue); isolated calls
+    (synchronised around each); and calls replayed from a HIP graph."""
     import synth
     import transposed_conv_pooling_amd as ct
     wl = synth.WORKLOADS["c1"]
@@ -658,6 +659,7 @@ def time_small_fused(torch, dev, stream, reps=200):
     h1 = time.perf_counter()
     b.record(stream)
     torch.cuda.synchronize()
+    back_to_back_us = a.elapsed_time(b) * 1e3 / reps
     single = []
     for _ in range(20):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -667,9 +669,25 @@ def time_small_fused(torch, dev, stream, reps=200):
         e1.record(stream)
         torch.cuda.synchronize()
         single.append(e0.elapsed_time(e1) * 1e3)
+    # the same call captured 100 times in one HIP graph and replayed: the
+    # launches then cost the host nothing, and the GPU time per call remains
+    n_graph = 100
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_graph):
+            ct.ct_convT3d_scale_pool_bias(x, w, None, bias, 0.5, 1.0, out=out)
+    g.replay()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(10):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    graph_us = a.elapsed_time(b) * 1e3 / (10 * n_graph)
     alg = int(x.numel() * 4 + w.numel() * 4 + bias.numel() * 4 + out.numel() * 4)
-    return {"workload": wl.description, "us_per_call_back_to_back": round(a.elapsed_time(b) * 1e3 / reps, 2),
+    return {"workload": wl.description, "us_per_call_back_to_back": round(back_to_back_us, 2),
             "us_per_call_isolated": round(float(np.median(single)), 2),
+            "us_per_call_graph": round(graph_us, 2),
             "host_us_per_call": round((h1 - h0) * 1e6 / reps, 2), "alg_bytes": alg}
 
 

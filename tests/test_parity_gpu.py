@@ -111,6 +111,30 @@ def test_fused_f32_small(dev, shape, with_cb):
     assert_close(got, ref, F32_TOL, f"fused {shape}")
 
 
+# fp32 calls below 48 blocks of 16 outputs x 16 channels per CU (12,288
+# blocks on the 256 CUs of an MI355X) run on the direct kernel, so most shapes
+# above exercise that one.  The slab pipeline gets the same shapes (Cin <= 4)
+# with the batch scaled past that size: staged rows carried across row chunks,
+# planes and batch items, ragged last chunks, scalar rows (W % 4 != 0) and
+# ragged channel blocks.
+SLAB_BLOCKS = 48 * 256
+
+
+def slab_shape(shape):
+    N, Cin, Cout, D, H, W = shape
+    per_item = (D - 1) * (H - 1) * ((W - 1 + 15) // 16) * ((Cout + 15) // 16)
+    return (max(N, -(-SLAB_BLOCKS // per_item)),) + tuple(shape[1:])
+
+
+FUSED_SLAB = [slab_shape(s) for s in FUSED_SMALL if s[1] <= 4]
+
+
+@pytest.mark.parametrize("shape", FUSED_SLAB, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("with_cb", [False, True], ids=["nocb", "cb"])
+def test_fused_f32_slab(dev, shape, with_cb):
+    test_fused_f32_small(dev, shape, with_cb)
+
+
 def test_fused_f32_other_scales_no_bias(dev):
     x = synth.uniform(77, 0, (2, 3, 6, 9, 21), 0.0, 1.0)      # the page's torch.rand inputs
     w = synth.uniform(77, 1, (3, 5, 3, 3, 3), -0.2, 0.2)

@@ -41,7 +41,8 @@
 //  * The next M-block's 8*Cin input taps are loaded before the current
 //    block's MFMAs, so one block's load latency overlaps another's math.
 // Cin > 4 takes the same structure with a runtime k-step loop and the
-// fragments read from LDS.
+// fragments read from LDS.  This direct kernel also serves small calls with
+// Cin <= 4; larger ones take the slab pipeline below.
 #include "ct_internal.h"
 
 namespace ct {
@@ -680,7 +681,13 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
         const bool vec4 = slab_vec4(W, x);
         int TH, SW;
         slab_plan(KS, Cin, H, W, op, vec4, &TH, &SW);
-        if (TH > 0) {
+        // Small calls (fewer than 48 blocks of 16 outputs x 16 channels per CU)
+        // finish sooner on the direct kernel, which has no pipeline to fill:
+        // the small page workload [2,3,8,16,16] takes 4.3 against 5.0 us per
+        // call replayed from a graph, and the two meet near 48 blocks per CU.
+        const int64_t blocks = N * Dp * (int64_t)Hp * wblocks * gy;
+        const bool small = op == 0 && blocks < 48 * (int64_t)cus;
+        if (TH > 0 && !small) {
             const size_t lds = (size_t)slab_lds_floats(KS, Cin, TH, SW, Wp) * sizeof(float);
             const int hchunks = (Hp + TH - 1) / TH;
             const int64_t ntasks = N * Dp * (int64_t)hchunks;
@@ -710,7 +717,7 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
         }
     }
     if (op != 0) return hipErrorInvalidValue;    // the direct path has no far-edge taps
-    // direct-load path (Cin > 4, or rows too wide for an LDS slab)
+    // direct-load path (Cin > 4, rows too wide for an LDS slab, or a small call)
     const int64_t nmb = N * Dp * (int64_t)Hp * wblocks;   // < 2^31 (checked by the shim)
     const size_t lds = (size_t)(2 * Cin) * 64 * sizeof(float);
     per_cu = occupancy((const void *)fused3d_f32_kernel<KS>, kThreads, lds);
