@@ -20,12 +20,16 @@
  *     of the current device).  The caller owns every buffer, allocates the
  *     output, and keeps all buffers alive until the work on `stream` is done.
  *     The library allocates no device memory and keeps no state besides a
- *     per-thread error string.
+ *     per-thread error string and per-device facts it queries once and
+ *     caches (compute-unit count, kernel occupancies, granted LDS sizes).
  *   - fp32 pointers must be 4-byte aligned, bf16 pointers 2-byte aligned.
  *     The output must not overlap any input.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
  *     enqueued; nothing synchronises.  A device fault surfaces at the
- *     caller's next synchronisation, not in the return value.
+ *     caller's next synchronisation, not in the return value.  After the
+ *     first call of an operation on a device, a call enqueues nothing but
+ *     kernel launches (no allocation, memset or copy), so it may be captured
+ *     in a HIP graph on `stream` and replayed.
  *   - Every call returns a ct_status.  All argument checks run before any HIP
  *     call, so a rejected call touches neither the GPU nor the HIP runtime.
  *     ct_last_error() gives a human-readable reason for the last non-OK
