@@ -23,7 +23,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_close, bf16_tensor_to_f32, log, nan_like, opt, to_dev
+from gpu_util import assert_close, bf16_round, bf16_tensor_to_f32, log, nan_like, opt, to_dev
 
 torch = pytest.importorskip("torch")
 import transposed_conv_pooling_amd as ct  # noqa: E402
@@ -157,3 +157,23 @@ def test_fused_outpad1_full_every_item(dev):
     compare_items(got, lambda i, j: oracle.convT3d_scale_pool_bias(
         t["x"][i:j], t["w"], t["conv_bias"], t["bias"], 0.5, 1.0, 2, 1, 1), 128, 32,
         [F32_TOL], "fused output_padding=1")
+
+
+def test_fused_bf16_direct_full_every_item(dev):
+    """The bf16 chain at the wide workload's size where the bf16 kernel does not
+    apply (W = 31, output_padding = 1 and a conv bias): the direct kernel with
+    the taps widened to fp32, every element against the oracle."""
+    N, Cin, Cout, D, H, W = 16, 32, 64, 16, 32, 31
+    log(f"fused bf16 direct [{N},{Cin},{D},{H},{W}] -> Cout {Cout}, output_padding 1, conv bias")
+    x = bf16_round(synth.normal(0x5EED0015, 0, (N, Cin, D, H, W)))
+    bound = 1.0 / np.sqrt(Cin * 27)
+    w = bf16_round(synth.uniform(0x5EED0015, 1, (Cin, Cout, 3, 3, 3), -bound, bound))
+    b = synth.normal(0x5EED0015, 2, (Cout,))
+    cb = synth.normal(0x5EED0015, 3, (Cout,))
+    out = nan_like((N, Cout, D, H, W), dev)
+    ct.ct_convT3d_scale_pool_bias(to_dev(x, dev, "bf16"), to_dev(w, dev, "bf16"), opt(cb, dev),
+                                  opt(b, dev), 0.5, 1.0, 2, 1, 1, out=out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    compare_items(got, lambda i, j: oracle.convT3d_scale_pool_bias(
+        x[i:j], w, cb, b, 0.5, 1.0, 2, 1, 1), N, 16, [BF16_TOL, TIGHT_TOL], "bf16 direct")

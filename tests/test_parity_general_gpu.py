@@ -64,7 +64,7 @@ def opt(a, dev):
 FUSED_GENERAL = [
     # N, Cin, Cout, D, H, W, k, stride, pad, out_pad, pool_k, pool_s, dtype
     (2, 3, 16, 5, 7, 9, 3, 2, 1, 1, 2, 2, "f32"),     # output_padding 1
-    (2, 3, 16, 5, 7, 9, 3, 2, 1, 1, 2, 2, "bf16"),
+    (2, 3, 16, 5, 7, 9, 3, 2, 1, 1, 2, 2, "bf16"),  # bf16 with output padding: the direct kernel
     (1, 4, 6, 4, 5, 6, 4, 2, 1, 0, 2, 2, "f32"),      # even kernel
     (1, 3, 5, 4, 6, 7, 3, 1, 0, 0, 3, 2, "f32"),      # stride 1, 3-pool with stride 2
     (2, 2, 3, 3, 4, 5, 5, 3, 2, 2, 2, 1, "f32"),      # overlapping pool windows
@@ -72,10 +72,12 @@ FUSED_GENERAL = [
     (1, 2, 3, 4, 5, 6, 1, 1, 0, 0, 1, 1, "f32"),      # 1x1x1 conv, identity pool
     (1, 3, 4, 3, 4, 5, 3, 2, 1, 0, 3, 3, "bf16"),
     (1, 130, 4, 3, 3, 5, 3, 2, 1, 0, 2, 2, "f32"),    # page geometry, Cin beyond the MFMA path
-    (1, 40, 8, 3, 4, 8, 3, 2, 1, 0, 2, 2, "bf16"),    # page geometry, bf16 Cin > 32
-    (2, 3, 16, 4, 5, 13, 3, 2, 1, 0, 2, 2, "bf16"),   # page geometry, bf16 W % 8 != 0
-    (2, 3, 16, 9, 17, 33, 3, 2, 1, 1, 2, 2, "f32"),   # output_padding 1 on the effective-filter gather
-    (1, 40, 40, 3, 3, 4, 3, 2, 1, 1, 2, 2, "f32"),    # Cin*Cout > 1024: the plain gather
+    (1, 40, 8, 3, 4, 8, 3, 2, 1, 0, 2, 2, "bf16"),    # page geometry, bf16 Cin > 32: direct kernel
+    (2, 3, 16, 4, 5, 13, 3, 2, 1, 0, 2, 2, "bf16"),   # page geometry, bf16 W % 8 != 0: direct kernel
+    (2, 3, 16, 9, 17, 33, 3, 2, 1, 1, 2, 2, "f32"),   # output_padding 1, scalar slab rows (W % 4 != 0)
+    (1, 40, 40, 3, 3, 4, 3, 2, 1, 1, 2, 2, "f32"),    # output_padding 1, Cin > 4: the direct kernel
+    (1, 130, 4, 3, 3, 5, 3, 2, 1, 1, 2, 2, "f32"),    # Cin > 128: the effective-filter gather
+    (1, 130, 40, 3, 3, 5, 3, 2, 1, 0, 2, 2, "f32"),   # Cin*Cout > 1024 as well: the plain gather
     # output_padding 1 on the fp32 slab kernel (Cin <= 4): far-edge taps read 0,
     # float4 rows (W % 4 == 0) and scalar rows, several tasks per workgroup
     (2, 3, 16, 6, 10, 16, 3, 2, 1, 1, 2, 2, "f32"),
@@ -113,7 +115,7 @@ def test_fused_general(dev, case):
     assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, str(case))
 
 
-def test_fused_bf16_misaligned_x_takes_general_path(dev):
+def test_fused_bf16_misaligned_x_takes_direct_path(dev):
     shape = (1, 8, 3, 4, 16)
     x = bf16_round(synth.normal(71, 0, shape))
     w = bf16_round(synth.uniform(71, 1, (8, 16, 3, 3, 3), -0.1, 0.1))

@@ -198,37 +198,44 @@ ct_status ct_convT3d_scale_pool_bias(
     if (x_dtype != w_dtype)
         return fail(CT_EUNSUPPORTED, "%s: x and w dtypes must match", fn);
 
-    // The pages' geometry (k3 s2 p1, 2-pool) runs on the matrix-core kernels
-    // when their own limits hold; with output padding 1 the fp32 slab kernel
-    // takes it (far-edge taps read 0); everything else the general kernels.
-    bool fast = k == 3 && stride == 2 && pad == 1 && pool_k == 2 && ps == 2 &&
-                (out_pad == 0 || (out_pad == 1 && x_dtype == CT_F32 &&
-                                  ct::fused3d_f32_slab_supported(Cin, H, W, 1, (const float *)x)));
-    if (fast) {
+    // The pages' geometry (k3 s2 p1, 2-pool; output padding 0 or 1) runs on
+    // the matrix-core kernels when their index limits hold: fp32 on the slab
+    // or direct fp32 kernel, bf16 on the bf16 kernel where it applies (no
+    // output padding, Cin <= 32, W % 8 == 0, 16-byte aligned x) and on the
+    // direct kernel with the taps widened to fp32 otherwise.  The bf16 kernel
+    // works in 64-channel groups, so the first layer's own shape (Cin <= 4,
+    // Cout <= 16) is faster on the direct kernel too (53 against 74 us at
+    // [128,3,16,32,32] -> 16 channels).  Everything else runs on the general
+    // kernels.
+    bool page = k == 3 && stride == 2 && pad == 1 && pool_k == 2 && ps == 2 && out_pad <= 1;
+    bool bf16_fast = false;
+    if (page) {
         const int64_t wblocks = (pd[2] + 15) / 16;
         int64_t nmb, xitem, oitem;
-        fast = prod({N, pd[0], pd[1], wblocks}, &nmb) && nmb <= kI32Max / 8 &&
+        page = prod({N, pd[0], pd[1], wblocks}, &nmb) && nmb <= kI32Max / 8 &&
                prod({Cin, D, H, W}, &xitem) && xitem <= kI32Max &&
                prod({Cout, pd[0], pd[1], pd[2]}, &oitem) && oitem <= kI32Max &&
-               Cout <= 65535 * 16;
-        if (x_dtype == CT_F32) {
-            fast = fast && Cin <= 128;
-        } else {
+               Cout <= 65535 * 16 && Cin <= 128;
+        if (page && x_dtype == CT_BF16 && out_pad == 0) {
             const size_t lb = ct::fused3d_bf16_lds_bytes(Cin, W);
             // (its buffer stores take 32-bit byte offsets within one batch item,
             // and masked lanes store at 2^31 - 16, which must lie past the item)
-            fast = fast && Cin <= 32 && W % 8 == 0 && aligned(x, 16) && lb != 0 && lb <= kLdsMax &&
-                   oitem * 4 < (int64_t(1) << 31) - 64;
+            bf16_fast = Cin <= 32 && W % 8 == 0 && aligned(x, 16) && lb != 0 && lb <= kLdsMax &&
+                        oitem * 4 < (int64_t(1) << 31) - 64 && !(Cin <= 4 && Cout <= 16);
         }
     }
     hipError_t e;
-    if (fast && x_dtype == CT_F32) {
+    if (page && x_dtype == CT_F32) {
         e = ct::launch_fused3d_f32((const float *)x, (const float *)w, conv_bias, bias, scale1,
                                    scale2, N, Cin, D, H, W, Cout, out_pad, out, (hipStream_t)stream);
-    } else if (fast) {
+    } else if (bf16_fast) {
         e = ct::launch_fused3d_bf16((const uint16_t *)x, (const uint16_t *)w, conv_bias, bias,
                                     scale1, scale2, N, Cin, D, H, W, Cout, out,
                                     (hipStream_t)stream);
+    } else if (page) {
+        e = ct::launch_fused3d_direct_bf16((const uint16_t *)x, (const uint16_t *)w, conv_bias, bias,
+                                           scale1, scale2, N, Cin, D, H, W, Cout, out_pad, out,
+                                           (hipStream_t)stream);
     } else {
         if (pool_k > kGenericMaxTap)
             return fail(CT_EUNSUPPORTED, "%s: pool_k > %d is not implemented", fn, kGenericMaxTap);

@@ -22,14 +22,22 @@ hipError_t allow_dynamic_lds(const void *fn, size_t lds);
 
 // Fused ConvTranspose3d(k3, s2, p1, output_padding op) -> *s1 ->
 // AvgPool3d(2) -> +bias -> *s2, fp32 x and w.  Output [N, Cout, D-1+op,
-// H-1+op, W-1+op].  op = 1 only where fused3d_f32_slab_supported() holds
-// (Cin <= 4 and an LDS slab fits); op = 0 for any Cin.
-bool fused3d_f32_slab_supported(int64_t Cin, int64_t H, int64_t W, int op, const float *x);
+// H-1+op, W-1+op], op 0 or 1, Cin up to 128 (the slab kernel for Cin <= 4
+// when an LDS slab fits and the call is not small, else the direct kernel).
 hipError_t launch_fused3d_f32(const float *x, const float *w,
                               const float *conv_bias, const float *bias,
                               float s1, float s2, int64_t N, int64_t Cin,
                               int64_t D, int64_t H, int64_t W, int64_t Cout, int op,
                               float *out, hipStream_t stream);
+
+// The direct fp32 kernel of the same chain for bf16 x and w, the taps
+// widened exactly to fp32 (any Cin up to 128, output padding 0 or 1, no
+// alignment beyond 2 bytes); the bf16 kernel below is the fast path.
+hipError_t launch_fused3d_direct_bf16(const uint16_t *x, const uint16_t *w,
+                                      const float *conv_bias, const float *bias, float s1,
+                                      float s2, int64_t N, int64_t Cin, int64_t D, int64_t H,
+                                      int64_t W, int64_t Cout, int op, float *out,
+                                      hipStream_t stream);
 
 // Same chain with bf16 x and w (fp32 accumulation and output).
 hipError_t launch_fused3d_bf16(const uint16_t *x, const uint16_t *w,

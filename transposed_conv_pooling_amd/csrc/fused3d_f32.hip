@@ -62,7 +62,13 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // A thread takes two entries per pass and issues both entries' 16 weight
 // loads before summing, so with at most 2*kThreads entries (Cin <= 4) the
 // whole filter costs one round trip to memory.
-__device__ __forceinline__ void build_wfrag(const float *__restrict__ w, int Cout, int cob,
+// One element of x or w as fp32: fp32 data as is, bf16 data (its 16-bit
+// pattern) widened exactly.
+__device__ __forceinline__ float ld_elem(const float *p) { return *p; }
+__device__ __forceinline__ float ld_elem(const uint16_t *p) { return __uint_as_float((unsigned)*p << 16); }
+
+template <typename E>
+__device__ __forceinline__ void build_wfrag(const E *__restrict__ w, int Cout, int cob,
                                             int ksteps, float *wfrag)
 {
     const int nent = ksteps * 64;
@@ -79,7 +85,7 @@ __device__ __forceinline__ void build_wfrag(const float *__restrict__ w, int Cou
             const int kap = 4 * j + (l >> 4);
             const int ci = kap >> 3, tap = kap & 7;
             const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
-            const float *wp = w + ((int64_t)ci * Cout + min(co, Cout - 1)) * 27;
+            const E *wp = w + ((int64_t)ci * Cout + min(co, Cout - 1)) * 27;
             // per axis: input offset 0 takes taps {1,2}, offset 1 takes tap {0}
             const int kd0 = a ? 0 : 1, kh0 = b ? 0 : 1, kw0 = c ? 0 : 1;
             nk[u][0] = a ? 1 : 2; nk[u][1] = b ? 1 : 2; nk[u][2] = c ? 1 : 2;
@@ -90,7 +96,7 @@ __device__ __forceinline__ void build_wfrag(const float *__restrict__ w, int Cou
                 for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                     for (int k = 0; k < 2; ++k)
-                        t8[u][(i * 2 + jj) * 2 + k] = wp[(kd0 + i) * 9 + (kh0 + jj) * 3 + kw0 + k];
+                        t8[u][(i * 2 + jj) * 2 + k] = ld_elem(wp + (kd0 + i) * 9 + (kh0 + jj) * 3 + kw0 + k);
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -126,9 +132,13 @@ __device__ __forceinline__ void advance(Pos &p, int wblocks, int Hp, int Dp)
 }
 
 // KS > 0: 2*Cin k-steps known at compile time; KS == 0: runtime Cin.
-template <int KS>
+// E: element type of x and w (fp32, or bf16 bit patterns widened exactly).
+// With output padding 1 the pooled grid reaches the input's far edges
+// (Dp = D, Hp = H, Wp = W) and a tap past an edge reads 0 ([p50]'s parity
+// rule with the missing inputs taken as zero).
+template <int KS, typename E>
 __global__ __launch_bounds__(kThreads)
-void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w,
+void fused3d_f32_kernel(const E *__restrict__ x, const E *__restrict__ w,
                         const float *__restrict__ conv_bias,
                         const float *__restrict__ bias, float s1, float s2,
                         int Cin, int D, int H, int W, int Cout,
@@ -176,22 +186,32 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
         p.d = uniform(t % Dp);
         p.n = uniform(t / Dp);
     }
+    // which of a lane's taps (a, b, c) are past the far edges: the plane,
+    // row and column offsets must stay below D, H and W
+    auto tap_ok = [&](const Pos &q, int wv, int tap) {
+        return q.d + (tap >> 2) < D && q.h + ((tap >> 1) & 1) < H && wv + (tap & 1) < W;
+    };
 
     if constexpr (KS > 0) {
         float a[KS];
-        int off[KS];
+        int off[KS], tp[KS];
 #pragma unroll
         for (int j = 0; j < KS; ++j) {
             a[j] = wfrag[j * 64 + lane];
             const int kap = 4 * j + kq;
             const int ci = kap >> 3, tap = kap & 7;
+            tp[j] = tap;
             off[j] = ci * DHW + (tap >> 2) * HW + ((tap >> 1) & 1) * W + (tap & 1);
         }
         auto load = [&](const Pos &q, float *v) {
             const int wv = min(q.wb * 16 + col, Wp - 1);   // masked lanes read a valid tap
-            const float *xb = x + (int64_t)q.n * Cin * DHW + (int64_t)q.d * HW + q.h * W + wv;
+            const E *xb = x + (int64_t)q.n * Cin * DHW + (int64_t)q.d * HW + q.h * W + wv;
 #pragma unroll
-            for (int j = 0; j < KS; ++j) v[j] = xb[off[j]];
+            for (int j = 0; j < KS; ++j) {
+                const bool ok = tap_ok(q, wv, tp[j]);
+                const float t = ld_elem(ok ? xb + off[j] : x);
+                v[j] = ok ? t : 0.0f;
+            }
         };
         float cur[KS], nxt[KS];
         load(p, cur);
@@ -225,7 +245,7 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
         for (int mb = mb_begin; mb < mb_end; ++mb) {
             const int wv0 = p.wb * 16 + col;
             const int wv = min(wv0, Wp - 1);
-            const float *xb = x + (int64_t)p.n * Cin * DHW + (int64_t)p.d * HW + p.h * W + wv;
+            const E *xb = x + (int64_t)p.n * Cin * DHW + (int64_t)p.d * HW + p.h * W + wv;
             v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
             for (int j0 = 0; j0 < ksteps; j0 += kChunk) {
                 float xv[kChunk];
@@ -234,8 +254,11 @@ void fused3d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
                     const int kap = 4 * (j0 + jj) + kq;
                     const int ci = kap >> 3, tap = kap & 7;
                     const int cic = min(ci, Cin - 1);          // valid address; masked below
-                    const float v = xb[(int64_t)cic * DHW + (tap >> 2) * HW + ((tap >> 1) & 1) * W + (tap & 1)];
-                    xv[jj] = (j0 + jj < ksteps) ? v : 0.0f;
+                    const bool ok = j0 + jj < ksteps && tap_ok(p, wv, tap);
+                    const float v = ld_elem(ok ? xb + (int64_t)cic * DHW + (tap >> 2) * HW +
+                                                     ((tap >> 1) & 1) * W + (tap & 1)
+                                               : x);
+                    xv[jj] = ok ? v : 0.0f;
                 }
 #pragma unroll
                 for (int jj = 0; jj < kChunk; ++jj)
@@ -665,6 +688,32 @@ static void slab_plan(int ks, int64_t Cin, int64_t H, int64_t W, int op, bool ve
 
 static bool slab_vec4(int64_t W, const float *x) { return (W % 4 == 0) && (((uintptr_t)x & 15) == 0); }
 
+// The direct kernel: waves walk contiguous ranges of 16-voxel blocks and
+// load their taps straight from memory (Cin > 4, rows too wide for an LDS
+// slab, a small call, or bf16 data the bf16 kernel does not take).
+template <int KS, typename E>
+static hipError_t launch_direct(const E *x, const E *w, const float *conv_bias, const float *bias,
+                                float s1, float s2, int64_t N, int64_t Cin, int64_t D, int64_t H,
+                                int64_t W, int64_t Cout, int op, float *out, hipStream_t stream)
+{
+    const int Dp = (int)(D - 1 + op), Hp = (int)(H - 1 + op), Wp = (int)(W - 1 + op);
+    const int wblocks = (Wp + 15) / 16;
+    const unsigned gy = (unsigned)((Cout + 15) / 16);
+    const int64_t nmb = N * Dp * (int64_t)Hp * wblocks;   // < 2^31 (checked by the shim)
+    const size_t lds = (size_t)(2 * Cin) * 64 * sizeof(float);
+    const int per_cu = occupancy((const void *)fused3d_f32_kernel<KS, E>, kThreads, lds);
+    int64_t waves = (int64_t)device_cus() * per_cu * kWaves / gy;
+    const int64_t max_waves = (nmb + kMinMbPerWave - 1) / kMinMbPerWave;
+    if (waves > max_waves) waves = max_waves;
+    if (waves < kWaves) waves = kWaves;
+    const int per = (int)((nmb + waves - 1) / waves);
+    const unsigned gx = (unsigned)(((nmb + per - 1) / per + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((fused3d_f32_kernel<KS, E>), dim3(gx, gy), dim3(kThreads), lds, stream, x, w,
+                       conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H, (int)W, (int)Cout,
+                       Dp, Hp, Wp, wblocks, (int)nmb, per, out);
+    return hipGetLastError();
+}
+
 template <int KS>
 static hipError_t launch_ks(const float *x, const float *w, const float *conv_bias,
                             const float *bias, float s1, float s2, int64_t N, int64_t Cin,
@@ -716,29 +765,8 @@ static hipError_t launch_ks(const float *x, const float *w, const float *conv_bi
             return hipLaunchKernel(fn, dim3(gx, gy), dim3(kSlabThreads), args, lds, stream);
         }
     }
-    if (op != 0) return hipErrorInvalidValue;    // the direct path has no far-edge taps
-    // direct-load path (Cin > 4, rows too wide for an LDS slab, or a small call)
-    const int64_t nmb = N * Dp * (int64_t)Hp * wblocks;   // < 2^31 (checked by the shim)
-    const size_t lds = (size_t)(2 * Cin) * 64 * sizeof(float);
-    per_cu = occupancy((const void *)fused3d_f32_kernel<KS>, kThreads, lds);
-    int64_t waves = (int64_t)cus * per_cu * kWaves / gy;
-    const int64_t max_waves = (nmb + kMinMbPerWave - 1) / kMinMbPerWave;
-    if (waves > max_waves) waves = max_waves;
-    if (waves < kWaves) waves = kWaves;
-    const int per = (int)((nmb + waves - 1) / waves);
-    const unsigned gx = (unsigned)(((nmb + per - 1) / per + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(fused3d_f32_kernel<KS>, dim3(gx, gy), dim3(kThreads), lds, stream, x, w,
-                       conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H, (int)W, (int)Cout,
-                       Dp, Hp, Wp, wblocks, (int)nmb, per, out);
-    return hipGetLastError();
-}
-
-bool fused3d_f32_slab_supported(int64_t Cin, int64_t H, int64_t W, int op, const float *x)
-{
-    if (Cin < 1 || Cin > 4) return false;
-    int TH, SW;
-    slab_plan(2 * (int)Cin, Cin, H, W, op, slab_vec4(W, x), &TH, &SW);
-    return TH > 0;
+    return launch_direct<KS, float>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out,
+                                    stream);
 }
 
 hipError_t launch_fused3d_f32(const float *x, const float *w,
@@ -753,6 +781,21 @@ hipError_t launch_fused3d_f32(const float *x, const float *w,
     case 3: return launch_ks<6>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
     case 4: return launch_ks<8>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
     default: return launch_ks<0>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    }
+}
+
+hipError_t launch_fused3d_direct_bf16(const uint16_t *x, const uint16_t *w,
+                                      const float *conv_bias, const float *bias, float s1,
+                                      float s2, int64_t N, int64_t Cin, int64_t D, int64_t H,
+                                      int64_t W, int64_t Cout, int op, float *out,
+                                      hipStream_t stream)
+{
+    switch (Cin) {
+    case 1: return launch_direct<2>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    case 2: return launch_direct<4>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    case 3: return launch_direct<6>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    case 4: return launch_direct<8>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
+    default: return launch_direct<0>(x, w, conv_bias, bias, s1, s2, N, Cin, D, H, W, Cout, op, out, stream);
     }
 }
 
