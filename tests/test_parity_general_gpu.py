@@ -283,6 +283,17 @@ CONV1D_GENERAL = [
     (1, 32, 64, 8, 5, 2, 9, 3, 2, True, "f32"),       # pad larger than the input
     (3, 32, 64, 1028, 5, 2, 1, 3, 1, True, "f32"),    # tiles straddling batch items
     (8, 32, 64, 20004, 5, 2, 1, 3, 1, True, "f32"),   # more tiles than waves: halos carried
+    # stride 1 with a pad or output padding on the fp32 matrix cores (the
+    # unpadded kernel over a shifted output window; output length % 4 == 0):
+    # pads of every residue mod 4, "same" padding, pad past the halo
+    (2, 32, 64, 300, 5, 1, 2, 3, 0, True, "f32"),
+    (1, 32, 70, 520, 5, 1, 1, 3, 2, True, "f32"),     # odd pad, two channel groups, ragged
+    (2, 32, 64, 296, 5, 1, 6, 3, 0, False, "f32"),    # "same": output length = input length
+    (1, 32, 16, 260, 5, 1, 3, 3, 2, True, "f32"),
+    (1, 32, 64, 8, 5, 1, 5, 3, 2, True, "f32"),       # pad larger than half the input
+    (3, 32, 64, 1028, 5, 1, 4, 3, 0, True, "f32"),    # tiles straddling batch items
+    (8, 32, 64, 20004, 5, 1, 7, 3, 2, True, "f32"),   # more tiles than waves: halos carried
+    (1, 32, 64, 100, 5, 1, 1, 3, 0, True, "f32"),     # output length % 4 != 0: the general kernel
 ]
 
 

@@ -154,12 +154,15 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 // workgroup barrier.  Several waves per SIMD, out of phase with each other,
 // keep the matrix pipe busy while any one of them stages its next strip or
 // issues its stores.  Neighbouring tiles both read the strip halo.
-template <int CIN4, int K, int DIL, int NB, int WW>
+// HP: strip positions before a tile's first output: DIL*(K-1) without
+// padding; with a pad the strip is shifted by the pad rounded up to a
+// multiple of 4 (so its float4 pieces stay aligned) and needs up to 3 more.
+template <int CIN4, int K, int DIL, int NB, int WW, int HP = DIL * (K - 1)>
 struct WaveGeom {
     static constexpr int kThreads = 64 * WW;
     static constexpr int kTW = 16 * NB;                             // outputs per wave tile
     static constexpr int kKsteps = CIN4 * K / 4;
-    static constexpr int kHalo = DIL * (K - 1);
+    static constexpr int kHalo = HP;
     static constexpr int kTs = kTW + kHalo;                         // strip positions
     // row stride >= kTs with stride mod 64 in {16, 48} words: the four
     // 16-lane groups of a B-fragment read (rows kq = 0..3) hit disjoint banks
@@ -172,13 +175,21 @@ struct WaveGeom {
     static constexpr int kLdsFloats = kWfrag + kCO + WW * CIN4 * kStr;
 };
 
-template <int CIN4, int K, int DIL, int NB, int WW>
+// Stride 1 with padding: output o of the padded call is output o + pad of
+// the unpadded one (output padding only extends the window at the end), so
+// the kernel runs unchanged over tiles of o with the input strip of a tile
+// starting at o0 + shift - HP, shift = pad rounded up to a multiple of 4
+// (HP > DIL*(K-1) instantiations only; the unpadded one folds both to 0).
+template <int CIN4, int K, int DIL, int NB, int WW, int HP = DIL * (K - 1)>
 __global__ __launch_bounds__(64 * WW, 1)
 void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
-                             int tiles_per_n, int ntiles, float *__restrict__ y)
+                             int tiles_per_n, int ntiles, int pad_arg, float *__restrict__ y)
 {
-    typedef WaveGeom<CIN4, K, DIL, NB, WW> G;
+    typedef WaveGeom<CIN4, K, DIL, NB, WW, HP> G;
+    static_assert(HP % 4 == 0 && HP >= DIL * (K - 1), "strip halo");
+    const int pad = HP == DIL * (K - 1) ? 0 : pad_arg;
+    const int shift = (pad + 3) & ~3;                        // strip offset, a multiple of 4
     static_assert(G::kStr >= G::kTs && (G::kStr % 64 == 16 || G::kStr % 64 == 48), "strip row stride");
     static_assert(G::kHalo % 4 == 0, "halo in whole float4 pieces");
     static_assert(G::kQPerLane <= 32, "piece mask");
@@ -225,12 +236,12 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
     auto fetch = [&](int tile, bool carry) {
         const int n = tile / tiles_per_n;
         const int o0 = (tile - n * tiles_per_n) * G::kTW;
-        const float *xb = x + (int64_t)n * Cin * L + (o0 - G::kHalo);
+        const float *xb = x + (int64_t)n * Cin * L + (o0 + shift - G::kHalo);
 #pragma unroll
         for (int i = 0; i < G::kQPerLane; ++i) {
             const int q = lane + 64 * i;
             const int ci = q / (G::kTs / 4), t4 = q % (G::kTs / 4);
-            const int pos = o0 - G::kHalo + 4 * t4;
+            const int pos = o0 + shift - G::kHalo + 4 * t4;
             const bool mine = q < G::kQ && !(carry && t4 < G::kHalo / 4);
             const bool ok = mine && ci < Cin && pos >= 0 && pos < L;
             pre[i] = *reinterpret_cast<const v4f_ *>(ok ? xb + ci * L + 4 * t4 : x);
@@ -241,7 +252,9 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
     if (t_begin < t_end) fetch(t_begin, false);
     __syncthreads();                                         // weights and bias staged
 
-    const float *xl = xs + kq * G::kStr + G::kHalo + col;   // lane's B base
+    // lane's B base: strip index of input o + pad - DIL*k is
+    // o - o0 + HP - (shift - pad) - DIL*k
+    const float *xl = xs + kq * G::kStr + G::kHalo - (shift - pad) + col;
     const float *al = wfrag + lane * 4;                      // lane's A base
     for (int tile = t_begin; tile < t_end; ++tile) {
         const int n = tile / tiles_per_n;
@@ -692,35 +705,54 @@ size_t convT1d_f32_lds_bytes(int64_t Cin, int K, int dilation)
     return (size_t)(4 * ksteps * 64 + cin4 * str) * sizeof(float);
 }
 
+bool convT1d_f32_wave_supported(int64_t Cin, int K, int dilation, int64_t L, int64_t Lo,
+                                const void *x, const void *out)
+{
+    return Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 && Lo % 4 == 0 &&
+           (((uintptr_t)x) & 15) == 0 && (((uintptr_t)out) & 15) == 0;
+}
+
+namespace {
+template <int HP>
+hipError_t launch_wave(const float *x, const float *w, const float *bias, int64_t N, int64_t Cin,
+                       int64_t L, int64_t Cout, int64_t Lo, int pad, float *out, hipStream_t stream)
+{
+    typedef WaveGeom<32, 5, 3, kWaveNB, kWaveWW, HP> G;
+    const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW, HP>;
+    const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
+    hipError_t e = allow_dynamic_lds(fn, lds);
+    if (e != hipSuccess) return e;
+    const int cus = device_cus(), per_cu = occupancy(fn, G::kThreads, lds);
+    const int wtiles_per_n = (int)((Lo + G::kTW - 1) / G::kTW);
+    const int64_t wtiles = N * wtiles_per_n;
+    const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
+    int64_t gx = (int64_t)cus * per_cu / gy;
+    if (gx < 1) gx = 1;
+    hipLaunchKernelGGL((convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW, HP>), dim3((unsigned)gx, gy),
+                       dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
+                       (int)Lo, wtiles_per_n, (int)wtiles, pad, out);
+    return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
                               int64_t N, int64_t Cin, int64_t L, int64_t Cout,
-                              int K, int dilation, float *out, hipStream_t stream)
+                              int K, int dilation, int pad, int out_pad, float *out,
+                              hipStream_t stream)
 {
     const int cin4 = (int)((Cin + 3) & ~int64_t(3));
-    const int64_t Lo = L + (int64_t)dilation * (K - 1);
+    const int64_t Lo = L + (int64_t)dilation * (K - 1) - 2 * (int64_t)pad + out_pad;
+    if (convT1d_f32_wave_supported(Cin, K, dilation, L, Lo, x, out)) {
+        if (pad == 0 && out_pad == 0)
+            return launch_wave<12>(x, w, bias, N, Cin, L, Cout, Lo, 0, out, stream);
+        return launch_wave<16>(x, w, bias, N, Cin, L, Cout, Lo, pad, out, stream);
+    }
+    if (pad != 0 || out_pad != 0) return hipErrorInvalidValue;   // the tile kernel has no shift
     const int tiles_per_n = (int)((Lo + kTO - 1) / kTO);
     const int64_t ntiles = N * tiles_per_n;
     const int64_t ts = kTO + (int64_t)dilation * (K - 1);
     int64_t str = ((ts + 63) / 64) * 64 + 16;
     if (str - 64 >= ts) str -= 64;
-    if (cin4 == 32 && Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 &&
-        (((uintptr_t)x) & 15) == 0 && (((uintptr_t)out) & 15) == 0) {
-        typedef WaveGeom<32, 5, 3, kWaveNB, kWaveWW> G;
-        const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW>;
-        const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
-        hipError_t e = allow_dynamic_lds(fn, lds);
-        if (e != hipSuccess) return e;
-        const int cus = device_cus(), per_cu = occupancy(fn, G::kThreads, lds);
-        const int wtiles_per_n = (int)((Lo + G::kTW - 1) / G::kTW);
-        const int64_t wtiles = N * wtiles_per_n;
-        const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
-        int64_t gx = (int64_t)cus * per_cu / gy;
-        if (gx < 1) gx = 1;
-        hipLaunchKernelGGL((convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW>), dim3((unsigned)gx, gy),
-                           dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
-                           (int)Lo, wtiles_per_n, (int)wtiles, out);
-        return hipGetLastError();
-    }
     const size_t lds = convT1d_f32_lds_bytes(Cin, K, dilation);
     hipError_t e = allow_dynamic_lds((const void *)convT1d_f32_kernel, lds);
     if (e != hipSuccess) return e;

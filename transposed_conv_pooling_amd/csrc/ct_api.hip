@@ -372,9 +372,13 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
         return fail(CT_EINVAL, "convT1d: out overlaps an input");
     if (x_dtype != w_dtype) return fail(CT_EUNSUPPORTED, "convT1d: x and w dtypes must match");
 
-    // Stride 1, pad 0 in fp32 runs on the fp32 matrix-core kernel when its
-    // tiles fit; everything else not caught below on the general kernel.
-    bool fast = x_dtype == CT_F32 && stride == 1 && pad == 0 && out_pad == 0;
+    // Stride 1 in fp32 runs on the fp32 matrix-core kernels when their tiles
+    // fit: without padding for any channels, taps and dilation, and with a pad
+    // or output padding at the page's channels and taps (a shifted output
+    // window); everything else not caught below on the general kernel.
+    bool fast = x_dtype == CT_F32 && stride == 1 &&
+                ((pad == 0 && out_pad == 0) ||
+                 ct::convT1d_f32_wave_supported(Cin, K, dilation, L, Lo, x, out));
     if (fast) {
         const int64_t tiles = (Lo + 255) / 256;
         int64_t ntiles;
@@ -414,7 +418,7 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
                                         (hipStream_t)stream);
     } else if (fast) {
         e = ct::launch_convT1d_f32((const float *)x, (const float *)w, bias, N, Cin, L, Cout, K,
-                                   dilation, out, (hipStream_t)stream);
+                                   dilation, pad, out_pad, out, (hipStream_t)stream);
     } else if (fast_bf16) {
         e = ct::launch_convT1d_bf16((const uint16_t *)x, (const uint16_t *)w, bias, N, L, Cout, K,
                                     dilation, out, (hipStream_t)stream);

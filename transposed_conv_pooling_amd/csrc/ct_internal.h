@@ -58,11 +58,16 @@ hipError_t launch_avgpool3d_k3s2p1(const void *x, bool bf16, bool include_pad, i
 bool avgpool3d_k3s2p1_fits(bool bf16, const void *x, const void *out, int64_t NC, int64_t D,
                            int64_t H, int64_t W);
 
-// ConvTranspose1d, stride 1, pad 0, any K and dilation, fp32.
+// ConvTranspose1d, stride 1, fp32: pad 0 and no output padding for any K and
+// dilation the LDS holds; with a pad or output padding only where
+// convT1d_f32_wave_supported() holds (Cin 32, K 5, dilation 3, L and the
+// output length multiples of 4, x and out 16-byte aligned).
+bool convT1d_f32_wave_supported(int64_t Cin, int K, int dilation, int64_t L, int64_t Lo,
+                                const void *x, const void *out);
 hipError_t launch_convT1d_f32(const float *x, const float *w,
                               const float *bias, int64_t N, int64_t Cin,
-                              int64_t L, int64_t Cout, int K, int dilation,
-                              float *out, hipStream_t stream);
+                              int64_t L, int64_t Cout, int K, int dilation, int pad,
+                              int out_pad, float *out, hipStream_t stream);
 
 // ConvTranspose1d with stride 2 (any pad and output padding) as two stride-1
 // gathers on the fp32 matrix cores, where convT1d_f32_poly_supported() holds
