@@ -133,10 +133,11 @@ __device__ __forceinline__ void advance(Pos &p, int wblocks, int Hp, int Dp)
 
 // KS > 0: 2*Cin k-steps known at compile time; KS == 0: runtime Cin.
 // E: element type of x and w (fp32, or bf16 bit patterns widened exactly).
-// With output padding 1 the pooled grid reaches the input's far edges
+// OP: output padding 1: the pooled grid reaches the input's far edges
 // (Dp = D, Hp = H, Wp = W) and a tap past an edge reads 0 ([p50]'s parity
-// rule with the missing inputs taken as zero).
-template <int KS, typename E>
+// rule with the missing inputs taken as zero); without it every tap is in
+// bounds and the loads carry no masks.
+template <int KS, typename E, bool OP>
 __global__ __launch_bounds__(kThreads)
 void fused3d_f32_kernel(const E *__restrict__ x, const E *__restrict__ w,
                         const float *__restrict__ conv_bias,
@@ -189,7 +190,7 @@ void fused3d_f32_kernel(const E *__restrict__ x, const E *__restrict__ w,
     // which of a lane's taps (a, b, c) are past the far edges: the plane,
     // row and column offsets must stay below D, H and W
     auto tap_ok = [&](const Pos &q, int wv, int tap) {
-        return q.d + (tap >> 2) < D && q.h + ((tap >> 1) & 1) < H && wv + (tap & 1) < W;
+        return !OP || (q.d + (tap >> 2) < D && q.h + ((tap >> 1) & 1) < H && wv + (tap & 1) < W);
     };
 
     if constexpr (KS > 0) {
@@ -696,22 +697,26 @@ static hipError_t launch_direct(const E *x, const E *w, const float *conv_bias, 
                                 float s1, float s2, int64_t N, int64_t Cin, int64_t D, int64_t H,
                                 int64_t W, int64_t Cout, int op, float *out, hipStream_t stream)
 {
+    const void *fn = op ? (const void *)fused3d_f32_kernel<KS, E, true>
+                        : (const void *)fused3d_f32_kernel<KS, E, false>;
     const int Dp = (int)(D - 1 + op), Hp = (int)(H - 1 + op), Wp = (int)(W - 1 + op);
     const int wblocks = (Wp + 15) / 16;
     const unsigned gy = (unsigned)((Cout + 15) / 16);
     const int64_t nmb = N * Dp * (int64_t)Hp * wblocks;   // < 2^31 (checked by the shim)
     const size_t lds = (size_t)(2 * Cin) * 64 * sizeof(float);
-    const int per_cu = occupancy((const void *)fused3d_f32_kernel<KS, E>, kThreads, lds);
+    const int per_cu = occupancy(fn, kThreads, lds);
     int64_t waves = (int64_t)device_cus() * per_cu * kWaves / gy;
     const int64_t max_waves = (nmb + kMinMbPerWave - 1) / kMinMbPerWave;
     if (waves > max_waves) waves = max_waves;
     if (waves < kWaves) waves = kWaves;
     const int per = (int)((nmb + waves - 1) / waves);
     const unsigned gx = (unsigned)(((nmb + per - 1) / per + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL((fused3d_f32_kernel<KS, E>), dim3(gx, gy), dim3(kThreads), lds, stream, x, w,
-                       conv_bias, bias, s1, s2, (int)Cin, (int)D, (int)H, (int)W, (int)Cout,
-                       Dp, Hp, Wp, wblocks, (int)nmb, per, out);
-    return hipGetLastError();
+    int a_cin = (int)Cin, a_d = (int)D, a_h = (int)H, a_w = (int)W, a_cout = (int)Cout, a_dp = Dp,
+        a_hp = Hp, a_wp = Wp, a_wb = wblocks, a_nmb = (int)nmb, a_per = per;
+    void *args[] = {(void *)&x, (void *)&w, (void *)&conv_bias, (void *)&bias, &s1, &s2, &a_cin,
+                    &a_d, &a_h, &a_w, &a_cout, &a_dp, &a_hp, &a_wp, &a_wb, &a_nmb, &a_per,
+                    (void *)&out};
+    return hipLaunchKernel(fn, dim3(gx, gy), dim3(kThreads), args, lds, stream);
 }
 
 template <int KS>
