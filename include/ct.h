@@ -107,18 +107,21 @@ CT_API int64_t ct_pool_out_len(int64_t in, int64_t k, int64_t stride, int64_t pa
  * Geometry: any k >= 1, stride >= 1, pad >= 0, 0 <= out_pad < stride
  * (PyTorch's rule at dilation 1), pool_k >= 1, pool_s >= 1 (0 = pool_k);
  * (x_dtype, w_dtype) = (CT_F32, CT_F32) or (CT_BF16, CT_BF16); accumulation
- * and output are fp32.  Three implementations:
- *   - k = 3, stride = 2, pad = 1, out_pad = 0, pool 2/2 (the page's
- *     geometry): matrix-core kernels that contract the 8 input taps of a
- *     pooled voxel with the grouped (summed) filter.  fp32 for Cin <= 128;
- *     bf16 for Cin <= 32, W a multiple of 8 up to 4096 and x 16-byte
- *     aligned.  The bf16 kernel represents the summed filter as a bf16
- *     hi + lo pair, so its result matches an fp32 computation on the same
- *     bf16 inputs to ~2^-17 relative per term.
- *   - the same conv and pool geometry with out_pad 0 or 1 otherwise (e.g.
- *     out_pad = 1, fp32 Cin > 128, bf16 shapes the matrix-core kernel does
- *     not take), when Cin * Cout <= 1024: the same effective-filter sum on
- *     the vector ALUs, taps past the far edge reading 0.
+ * and output are fp32.  Implementations:
+ *   - k = 3, stride = 2, pad = 1, pool 2/2 (the page's geometry) with
+ *     out_pad 0 or 1 and Cin <= 128: matrix-core kernels that contract the 8
+ *     input taps of a pooled voxel with the grouped (summed) filter, taps
+ *     past the far edge (out_pad = 1) reading 0.  fp32 runs on an LDS-slab
+ *     pipeline (Cin <= 4, large calls) or a direct kernel that loads its taps
+ *     from memory.  bf16 with out_pad 0, Cin <= 32, W a multiple of 8 up to
+ *     4096 and x 16-byte aligned runs on a bf16 kernel that represents the
+ *     summed filter as a bf16 hi + lo pair (the result matches an fp32
+ *     computation on the same bf16 inputs to ~2^-17 relative per term),
+ *     except Cin <= 4 with Cout <= 16, which, like every other bf16 call at
+ *     this geometry, runs on the direct kernel with the taps widened exactly
+ *     to fp32.
+ *   - the same conv and pool geometry with Cin > 128, when Cin * Cout <=
+ *     1024: the same effective-filter sum on the vector ALUs.
  *   - anything else: a general gather kernel on the vector ALUs (one thread
  *     per pooled voxel summing the pool window of transposed-convolution
  *     values), fp32 arithmetic on the (exactly widened) inputs.
@@ -225,6 +228,15 @@ CT_API ct_status ct_avgpool3d_bf16(const uint16_t *x,
  *     multiple of 4) and one input strip (Cin4 rows of 256 +
  *     dilation*(K-1) floats, padded) fit the 160 KiB LDS of one gfx950
  *     workgroup (Cin=32, K=5, dilation 3 needs 74 KiB).
+ *   - fp32 at the page's channels and taps (Cin 32, K 5, dilation 3, L a
+ *     multiple of 4, x and out 16-byte aligned): stride 1 with a pad or
+ *     output padding, when L_out is a multiple of 4, on the same matrix-core
+ *     kernel over a shifted output window; stride 2 with any pad and output
+ *     padding as two stride-1 gathers on the fp32 matrix cores (the residue
+ *     classes of o + pad).
+ *   - bf16 at the page's geometry (Cin 32, K 5, dilation 3, stride 1, pad 0,
+ *     out_pad 0, L a multiple of 8, x 16-byte aligned): an implicit GEMM on
+ *     the bf16 matrix cores with fp32 accumulation.
  *   - anything else: a general gather kernel (one thread per output), fp32
  *     arithmetic on the exactly widened inputs; lengths, Cin, Cout, pad and
  *     dilation*(K-1) up to 2^30, else CT_EUNSUPPORTED.
