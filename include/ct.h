@@ -229,14 +229,17 @@ CT_API ct_status ct_avgpool3d_bf16(const uint16_t *x,
  *     dilation*(K-1) floats, padded) fit the 160 KiB LDS of one gfx950
  *     workgroup (Cin=32, K=5, dilation 3 needs 74 KiB).
  *   - fp32 at the page's channels and taps (Cin 32, K 5, dilation 3, L a
- *     multiple of 4, x and out 16-byte aligned): stride 1 with a pad or
- *     output padding, when L_out is a multiple of 4, on the same matrix-core
- *     kernel over a shifted output window; stride 2 with any pad and output
- *     padding as two stride-1 gathers on the fp32 matrix cores (the residue
- *     classes of o + pad).
- *   - bf16 at the page's geometry (Cin 32, K 5, dilation 3, stride 1, pad 0,
- *     out_pad 0, L a multiple of 8, x 16-byte aligned): an implicit GEMM on
- *     the bf16 matrix cores with fp32 accumulation.
+ *     multiple of 4, x 16-byte aligned): stride 1 with any pad and output
+ *     padding on the same matrix-core kernel over a shifted output window
+ *     (any L_out: when L_out % 4 != 0 or out is not 16-byte aligned, rows
+ *     are stored with 4-byte aligned vectors); stride 2 with any pad and
+ *     output padding as two stride-1 gathers on the fp32 matrix cores (the
+ *     residue classes of o + pad).
+ *   - bf16 at the page's channels and taps (Cin 32, K 5, dilation 3), stride
+ *     1 with any pad and output padding, L a multiple of 8, x 16-byte
+ *     aligned: an implicit GEMM on the bf16 matrix cores with fp32
+ *     accumulation (a pad shifts the output window; any L_out and 4-byte
+ *     aligned out).
  *   - anything else: a general gather kernel (one thread per output), fp32
  *     arithmetic on the exactly widened inputs; lengths, Cin, Cout, pad and
  *     dilation*(K-1) up to 2^30, else CT_EUNSUPPORTED.

@@ -168,15 +168,16 @@ def test_fuzz_pool(dev, i):
 # -------------------------------------------------------- ConvTranspose1d --
 def draw_convT1d(i):
     """A third of the cases at the page's channels and taps (Cin 32, K 5,
-    dilation 3) with stride 1 or 2, the rest any valid geometry."""
+    dilation 3) with stride 1 or 2 and any pad and output padding, the rest
+    any valid geometry."""
     r = rng(4, i)
     while True:
         bf16 = bool(r.integers(0, 3) == 0)
         if i % 3 == 0:
             Cin, K, d = 32, 5, 3
             s = 1 if bf16 else int(r.integers(1, 3))
-            p = 0 if s == 1 else int(r.integers(0, 4))
-            op = 0 if s == 1 else int(r.integers(0, 3))
+            p = int(r.integers(0, 10))
+            op = int(r.integers(0, 3))
             L = int(r.choice([8 * int(r.integers(1, 300)), int(r.integers(1, 2000))]))
         else:
             Cin, K, d = int(r.integers(1, 40)), int(r.integers(1, 7)), int(r.integers(1, 5))

@@ -76,7 +76,8 @@ def case_inputs(name, dev):
         def call(out):
             ct.ct_convT3d(xg, wg, None, stride=2, pad=1, out_pad=0, out=out)
         return call, (2, 7, 7, 9, 11), torch.float32
-    # 1D convs at the page's channels and taps: stride 1 fp32 and bf16, stride 2 fp32
+    # 1D convs at the page's channels and taps: stride 1 fp32 and bf16 (pad 0,
+    # and pad 1 with its output length % 4 != 0), stride 2 fp32
     bf16 = name.endswith("bf16")
     stride = 2 if "s2" in name else 1
     N, Cin, Cout, L = 2, 32, 64, 1024
@@ -85,7 +86,7 @@ def case_inputs(name, dev):
     w = weights(9104, (Cin, Cout, 5), Cin * 5, bf16)
     dt = "bf16" if bf16 else "f32"
     xg, wg = to_dev(x, dev, dt), to_dev(w, dev, dt)
-    pad, op = (1, 1) if stride == 2 else (0, 0)
+    pad, op = (1, 1) if stride == 2 else (1, 0) if "p1" in name else (0, 0)
     Lo = ct.ct_convT_out_len(L, 5, stride, pad, op, 3)
 
     def call(out):
@@ -94,7 +95,7 @@ def case_inputs(name, dev):
 
 
 CASES = ["fused_f32", "fused_bf16", "fused_general", "pool_f32", "pool_bf16", "convT3d",
-         "conv1d_f32", "conv1d_s2_f32", "conv1d_bf16"]
+         "conv1d_f32", "conv1d_s2_f32", "conv1d_bf16", "conv1d_p1_f32", "conv1d_p1_bf16"]
 
 
 @pytest.mark.parametrize("name", CASES)

@@ -293,7 +293,30 @@ CONV1D_GENERAL = [
     (1, 32, 64, 8, 5, 1, 5, 3, 2, True, "f32"),       # pad larger than half the input
     (3, 32, 64, 1028, 5, 1, 4, 3, 0, True, "f32"),    # tiles straddling batch items
     (8, 32, 64, 20004, 5, 1, 7, 3, 2, True, "f32"),   # more tiles than waves: halos carried
-    (1, 32, 64, 100, 5, 1, 1, 3, 0, True, "f32"),     # output length % 4 != 0: the general kernel
+    # output length % 4 != 0: rows start at 4-byte boundaries, the row end's
+    # partial vector stored element by element
+    (1, 32, 64, 100, 5, 1, 1, 3, 0, True, "f32"),
+    (2, 32, 70, 1000, 5, 1, 1, 3, 0, True, "f32"),    # two channel groups, several tiles
+    (1, 32, 16, 260, 5, 1, 3, 3, 1, False, "f32"),
+    (3, 32, 64, 1028, 5, 1, 0, 3, 1, True, "f32"),    # output padding alone, tiles across items
+    (8, 32, 64, 20004, 5, 1, 0, 3, 2, True, "f32"),   # more tiles than waves
+    (1, 32, 64, 8, 5, 1, 1, 3, 0, True, "f32"),       # one tile
+    # stride 1 with a pad or output padding on the bf16 matrix cores (the
+    # strip shifted by the pad rounded up to 8 positions): pads of several
+    # residues mod 8, output lengths with and without 16-byte row starts
+    (2, 32, 64, 296, 5, 1, 2, 3, 0, True, "bf16"),
+    (1, 32, 70, 520, 5, 1, 1, 3, 2, True, "bf16"),    # two channel groups, ragged
+    (2, 32, 64, 296, 5, 1, 6, 3, 0, False, "bf16"),   # "same": output length = input length
+    (1, 32, 16, 264, 5, 1, 3, 3, 1, True, "bf16"),    # output length % 4 != 0: ragged rows
+    (2, 32, 70, 2000, 5, 1, 1, 3, 0, True, "bf16"),   # ragged rows, two channel groups
+    (8, 32, 64, 40000, 5, 1, 0, 3, 1, True, "bf16"),  # ragged rows, more tiles than workgroups
+    (2, 32, 64, 512, 5, 1, 8, 3, 1, True, "bf16"),    # pad a multiple of 8
+    (1, 32, 64, 2000, 5, 1, 15, 3, 0, True, "bf16"),  # pad past the halo
+    (1, 32, 64, 8, 5, 1, 9, 3, 2, True, "bf16"),      # pad larger than the input
+    (1, 32, 64, 16, 5, 1, 7, 3, 0, True, "bf16"),
+    (1, 32, 64, 1000, 5, 1, 0, 3, 2, True, "bf16"),   # output padding alone
+    (3, 32, 64, 1024, 5, 1, 4, 3, 0, True, "bf16"),   # tiles straddling batch items
+    (8, 32, 64, 40000, 5, 1, 5, 3, 2, True, "bf16"),  # more tiles than workgroups
 ]
 
 
@@ -324,3 +347,27 @@ def test_conv1d_bf16_misaligned_x_takes_general_path(dev):
     ct.ct_convT1d(buf[1:].view(1, 32, 64), to_dev(w, dev, "bf16"), None, 1, 0, 3, out=out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), oracle.convT1d(x, w, None, 1, 0, 3), F32_TOL, "misaligned")
+
+
+@pytest.mark.parametrize("dt,pad,op", [("f32", 0, 0), ("f32", 1, 0), ("bf16", 0, 0), ("bf16", 2, 1)])
+def test_conv1d_out_misaligned(dev, dt, pad, op):
+    """An output that starts 4 bytes past a 16-byte boundary: the matrix-core
+    kernels store its rows with 4-byte aligned vectors (and the row ends'
+    partial vectors element by element); every element matches the oracle and
+    the floats around the output stay untouched."""
+    N, Cin, Cout, L = 2, 32, 40, 1032
+    log(f"conv1d misaligned out {dt} pad {pad} op {op}")
+    x = synth.normal(92, 0, (N, Cin, L))
+    w = synth.uniform(92, 1, (Cin, Cout, 5), -0.08, 0.08)
+    if dt == "bf16":
+        x, w = bf16_round(x), bf16_round(w)
+    b = synth.normal(92, 2, (Cout,))
+    ref = oracle.convT1d(x, w, b, 1, pad, 3, op)
+    n = ref.size
+    buf = torch.full((n + 8,), float("nan"), dtype=torch.float32, device=dev)
+    buf[0], buf[n + 1] = -7.0, -9.0
+    out = buf[1:n + 1].view(ref.shape)
+    ct.ct_convT1d(to_dev(x, dev, dt), to_dev(w, dev, dt), opt(b, dev), 1, pad, 3, op, out=out)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, F32_TOL if dt == "f32" else BF16_TOL, "misaligned out")
+    assert float(buf[0]) == -7.0 and float(buf[n + 1]) == -9.0

@@ -1,6 +1,6 @@
-// convT1d_bf16.hip - dilated ConvTranspose1d (stride 1, pad 0) with bf16
-// inputs and weights as an implicit GEMM on the gfx950 bf16 matrix cores
-// (fp32 accumulation and output).
+// convT1d_bf16.hip - dilated ConvTranspose1d (stride 1, any pad and output
+// padding) with bf16 inputs and weights as an implicit GEMM on the gfx950
+// bf16 matrix cores (fp32 accumulation and output).
 //
 // Method ([p74] "Kimi-K2.6 l1_p74"): with stride 1 and pad 0 the transposed
 // convolution is the gather
@@ -51,23 +51,37 @@ constexpr int kCSW = 20;              // LDS dwords per strip position (16 used)
 constexpr int kLead = 64;             // outputs computed before a tile's first stored one
 constexpr int kOB = 5;                // 16-output blocks per wave: 4 * 5 * 16 = kLead + kTO
 
-template <int K, int DIL>
+// H8: strip positions before a tile's first computed output, a multiple of 8
+// (16-byte pieces): the halo DIL*(K-1) rounded up without padding; with a pad
+// the strip is shifted by the pad rounded up to a multiple of 8 and needs up
+// to 7 more.
+template <int K, int DIL, int H8 = (DIL * (K - 1) + 7) / 8 * 8>
 struct Geo1 {
     static constexpr int kHalo = DIL * (K - 1);
-    static constexpr int kH8 = (kHalo + 7) / 8 * 8;          // halo rounded to 16-byte pieces
+    static constexpr int kH8 = H8;
     static constexpr int kTS = kLead + kTO + kH8;             // strip positions
     static constexpr int kPieces = (kCin / 2) * (kTS / 8);   // (channel pair, 8 positions)
     static constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;
     static constexpr int kLdsBytes = kTS * kCSW * 4;
 };
 
-template <int K, int DIL, bool VEC_OUT>
+// With a pad (stride 1) output o is output o + pad of the unpadded
+// convolution (output padding only extends the window at the end): the strip
+// of a tile starts shift = pad rounded up to a multiple of 8 positions later,
+// and the lanes read it pad - shift positions back (H8 above the unpadded
+// halo; the unpadded instantiation folds pad and shift to 0).
+// RAGGED: output rows may start at any 4-byte boundary (Lo % 4 != 0 or y
+// not 16-byte aligned); otherwise every row starts 16-byte aligned.
+template <int K, int DIL, bool RAGGED, int H8 = (DIL * (K - 1) + 7) / 8 * 8>
 __global__ __launch_bounds__(kThreads, 2)
 void convT1d_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w,
                          const float *__restrict__ bias, int L, int Cout, int Lo, int tiles_per_n,
-                         int ntiles, float *__restrict__ y)
+                         int ntiles, int pad_arg, float *__restrict__ y)
 {
-    typedef Geo1<K, DIL> G;
+    typedef Geo1<K, DIL, H8> G;
+    static_assert(H8 % 8 == 0 && H8 >= DIL * (K - 1), "strip halo");
+    const int pad = H8 == (DIL * (K - 1) + 7) / 8 * 8 ? 0 : pad_arg;
+    const int shift = (pad + 7) & ~7;
     __shared__ __attribute__((aligned(16))) unsigned strip[G::kTS * kCSW];
     __shared__ __attribute__((aligned(16))) uint16_t wfrag[K * 4 * 64 * 8];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -99,7 +113,7 @@ void convT1d_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
     bool pok[G::kPPT];
     auto fetch = [&](int tile) {
         const int n = tile / tiles_per_n;
-        const int s0 = (tile - n * tiles_per_n) * kTO - kLead - G::kH8;
+        const int s0 = (tile - n * tiles_per_n) * kTO - kLead - G::kH8 + shift;
         const uint16_t *xn = x + (int64_t)n * kCin * L;
 #pragma unroll
         for (int i = 0; i < G::kPPT; ++i) {
@@ -127,11 +141,12 @@ void convT1d_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
     };
 
     if ((int)blockIdx.x < ntiles) fetch(blockIdx.x);
-    // lane's A base: strip position kH8 + 80*wave + col (output o0 - kLead +
-    // 80*wave + col), channels 8g..8g+7
-    const unsigned *al = strip + (G::kH8 + 16 * kOB * wave + col) * kCSW + 4 * g;
+    // lane's A base: strip position kH8 - (shift - pad) + 80*wave + col
+    // (input o + pad of output o = o0 - kLead + 80*wave + col), channels
+    // 8g..8g+7
+    const unsigned *al = strip + (G::kH8 - (shift - pad) + 16 * kOB * wave + col) * kCSW + 4 * g;
     const uint16_t *wl = wfrag + lane * 8;        // lane's B fragments
-    const int64_t ybase = (int64_t)(((uintptr_t)y) >> 2);   // y in floats (y is 16-byte aligned)
+    const int64_t ybase = (int64_t)(((uintptr_t)y) >> 2);   // y in floats (y is 4-byte aligned)
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const int n = tile / tiles_per_n;
@@ -163,66 +178,69 @@ void convT1d_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restr
         }
 
         // Row co of the tile is stored over [o0 - sh, o0 + 256 - sh), where sh
-        // (a multiple of 4 floats below 32) moves the segment's start onto a
-        // 128-byte line: segments of neighbouring tiles then never share a
-        // line, so no partly written line goes to memory.  The computed range
+        // (below 32 floats) moves the segment's start onto a 128-byte line:
+        // segments of neighbouring tiles then never share a line, so no
+        // partly written line goes to memory.  The computed range
         // [o0 - kLead, o0 + 256) covers every such segment.
         float *yn = y + (int64_t)n * Cout * Lo;
         // vector stores go through a buffer resource over this item's output
         // (word 3 0x00020000: 32-bit data format, as gfx9-family raw buffers
         // need); the hardware drops a store whose offset lies past the range,
         // so masked lanes need no branch and the wait for the next strip's
-        // loads does not cover these stores
+        // loads does not cover these stores.  With 16-byte aligned rows sh is
+        // a multiple of 4 and a lane's four outputs lie wholly inside or
+        // outside the segment.  Ragged rows take 4-byte aligned 16-byte
+        // stores (which gfx950's vector memory accepts; the compiler emits
+        // them for 4-byte-aligned vectors) and store the 1-3 outputs of a
+        // vector cut by a segment end one by one.
         const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(yn, 0, Cout * Lo * 4, 0x00020000);
         const int ow = o0 - kLead + 16 * kOB * wave + 4 * g;   // lane's first output
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int co = cog * kCO + 16 * cb + col;
-            float *yr = yn + (int64_t)co * Lo;
             int lo = o0, hi = o0 + kTO;
             if (co >= Cout) hi = lo;
-            if (VEC_OUT) {
-                const int sh = (int)((ybase + ((int64_t)n * Cout + co) * Lo) & 31);
-                lo -= sh;
-                hi -= sh;
-            }
+            const int sh = (int)((ybase + ((int64_t)n * Cout + co) * Lo) & 31);
+            lo -= sh;
+            hi -= sh;
             lo = lo > 0 ? lo : 0;
             hi = hi < Lo ? hi : Lo;
 #pragma unroll
             for (int ob = 0; ob < kOB; ++ob) {
                 const int o = ow + 16 * ob;
                 const v4f v = acc[ob][cb] + bv[cb];
-                if (VEC_OUT) {                            // o and Lo multiples of 4
-                    const int off = (o >= lo && o < hi) ? (co * Lo + o) * 4 : 0x7ffffff0;
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yrs, off, 0, 0);
-                } else {
+                const bool whole = o >= lo && (RAGGED ? o + 4 <= hi : o < hi);
+                const int off = whole ? (co * Lo + o) * 4 : 0x7ffffff0;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), yrs, off, 0, 0);
+                if (RAGGED && !whole && o < hi && o + 4 > lo) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (o + r >= lo && o + r < hi) yr[o + r] = v[r];
+                        if (o + r >= lo && o + r < hi)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[r]), yrs,
+                                                                  (co * Lo + o + r) * 4, 0, 0);
                 }
             }
         }
     }
 }
 
-template <int K, int DIL, bool VEC_OUT>
+template <int K, int DIL, bool RAGGED, int H8>
 hipError_t launch_geo(const uint16_t *x, const uint16_t *w, const float *bias, int64_t N,
-                      int64_t L, int64_t Cout, float *out, hipStream_t stream)
+                      int64_t L, int64_t Cout, int64_t Lo, int pad, float *out, hipStream_t stream)
 {
-    const int64_t Lo = L + (int64_t)DIL * (K - 1);
-    // tiles of 256 stored outputs, the last row segment shifted back by up
-    // to 28 floats: one extra tile when Lo is within 28 of a multiple of 256
-    const int tiles_per_n = (int)((Lo + 28 + kTO - 1) / kTO);
+    // tiles of 256 stored outputs, each row segment shifted back by up to
+    // 31 floats: one extra tile when Lo is within 31 of a multiple of 256
+    const int tiles_per_n = (int)((Lo + 31 + kTO - 1) / kTO);
     const int64_t ntiles = N * tiles_per_n;
-    const void *fn = (const void *)convT1d_bf16_kernel<K, DIL, VEC_OUT>;
+    const void *fn = (const void *)convT1d_bf16_kernel<K, DIL, RAGGED, H8>;
     const int cus = device_cus(), per_cu = occupancy(fn, kThreads, 0);
     const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
     int64_t gx = (int64_t)cus * per_cu / gy;
     if (gx < 1) gx = 1;
     if (gx > ntiles) gx = ntiles;
-    hipLaunchKernelGGL((convT1d_bf16_kernel<K, DIL, VEC_OUT>), dim3((unsigned)gx, gy),
+    hipLaunchKernelGGL((convT1d_bf16_kernel<K, DIL, RAGGED, H8>), dim3((unsigned)gx, gy),
                        dim3(kThreads), 0, stream, x, w, bias, (int)L, (int)Cout, (int)Lo,
-                       tiles_per_n, (int)ntiles, out);
+                       tiles_per_n, (int)ntiles, pad, out);
     return hipGetLastError();
 }
 
@@ -235,14 +253,17 @@ bool convT1d_bf16_supported(int64_t Cin, int K, int dilation, int64_t L, const v
 }
 
 hipError_t launch_convT1d_bf16(const uint16_t *x, const uint16_t *w, const float *bias,
-                               int64_t N, int64_t L, int64_t Cout, int K, int dilation,
-                               float *out, hipStream_t stream)
+                               int64_t N, int64_t L, int64_t Cout, int K, int dilation, int pad,
+                               int out_pad, float *out, hipStream_t stream)
 {
     if (K != 5 || dilation != 3) return hipErrorInvalidValue;
-    const int64_t Lo = L + (int64_t)dilation * (K - 1);
-    if (Lo % 4 == 0 && (((uintptr_t)out) & 15) == 0)
-        return launch_geo<5, 3, true>(x, w, bias, N, L, Cout, out, stream);
-    return launch_geo<5, 3, false>(x, w, bias, N, L, Cout, out, stream);
+    const int64_t Lo = L + (int64_t)dilation * (K - 1) - 2 * (int64_t)pad + out_pad;
+    const bool ragged = Lo % 4 != 0 || (((uintptr_t)out) & 15) != 0;
+    if (pad == 0)
+        return ragged ? launch_geo<5, 3, true, 16>(x, w, bias, N, L, Cout, Lo, 0, out, stream)
+                      : launch_geo<5, 3, false, 16>(x, w, bias, N, L, Cout, Lo, 0, out, stream);
+    return ragged ? launch_geo<5, 3, true, 24>(x, w, bias, N, L, Cout, Lo, pad, out, stream)
+                  : launch_geo<5, 3, false, 24>(x, w, bias, N, L, Cout, Lo, pad, out, stream);
 }
 
 }  // namespace ct

@@ -143,9 +143,9 @@ void convT1d_f32_kernel(const float *__restrict__ x, const float *__restrict__ w
 
 // Specialised path for the page's geometry: Cin4, K and the dilation known
 // at compile time, so every LDS address is a per-lane base plus an immediate
-// offset and the k-loop carries no index arithmetic.  Requires L % 4 == 0 and
-// dil*(K-1) % 4 == 0 (whole float4 pieces are either inside or outside
-// [0, L) and [0, Lo)) and 16-byte aligned x and y.
+// offset and the k-loop carries no index arithmetic.  Requires L % 4 == 0
+// (whole float4 pieces of the strip are either inside or outside [0, L)) and
+// a 16-byte aligned x; output rows may start at any 4-byte boundary.
 // Wave-independent path for the same specialised geometry: a workgroup of
 // WW waves shares one copy of the weight fragments (40 KiB of LDS, staged
 // once behind the kernel's only barrier); each wave then walks its own
@@ -180,7 +180,9 @@ struct WaveGeom {
 // the kernel runs unchanged over tiles of o with the input strip of a tile
 // starting at o0 + shift - HP, shift = pad rounded up to a multiple of 4
 // (HP > DIL*(K-1) instantiations only; the unpadded one folds both to 0).
-template <int CIN4, int K, int DIL, int NB, int WW, int HP = DIL * (K - 1)>
+// RAGGED: Lo % 4 != 0 or y not 16-byte aligned (rows start at any 4-byte
+// boundary); the aligned instantiation carries no tail stores.
+template <int CIN4, int K, int DIL, int NB, int WW, int HP = DIL * (K - 1), bool RAGGED = false>
 __global__ __launch_bounds__(64 * WW, 1)
 void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
@@ -337,13 +339,16 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
         }
 
         // 16-byte buffer stores over this batch item's output (word 3
-        // 0x00020000: 32-bit data format): rows start 16-byte aligned and a
-        // lane's four outputs are wholly inside or outside [0, Lo) (Lo % 4 ==
-        // 0); masked lanes store past the range, which the hardware drops, so
-        // no store sits behind a branch and every tile issues the same number
-        // of stores (4*NB, well under the 63 memory operations a wave can have
-        // in flight, so waiting for the next strip's loads never waits for
-        // this tile's stores)
+        // 0x00020000: 32-bit data format) of every lane whose four outputs
+        // lie wholly inside [0, Lo); masked lanes store past the range, which
+        // the hardware drops, so no store sits behind a branch and every tile
+        // issues the same number of stores (4*NB, well under the 63 memory
+        // operations a wave can have in flight, so waiting for the next
+        // strip's loads never waits for this tile's stores).  A row starts
+        // 16-byte aligned only when Lo % 4 == 0 and y is; otherwise the
+        // stores are 4-byte aligned, which gfx950's vector memory accepts
+        // (the compiler emits such 16-byte stores for 4-byte-aligned
+        // vectors).
         const __amdgpu_buffer_rsrc_t yr =
             __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * Cout * Lo, 0, Cout * Lo * 4, 0x00020000);
 #pragma unroll
@@ -352,8 +357,28 @@ void convT1d_f32_wave_kernel(const float *__restrict__ x, const float *__restric
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 const int o = o0 + 16 * b + 4 * kq;
-                const int off = (co < Cout && o < Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;   // past the range
+                const int off = (co < Cout && o + 4 <= Lo) ? (co * Lo + o) * 4 : 0x7ffffff0;   // past the range
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[m][b]), yr, off, 0, 0);
+            }
+        }
+        // Lo % 4 != 0: the last 1-3 outputs of each row belong to a lane
+        // whose vector runs past Lo; only the tile holding the row end (a
+        // wave-uniform test) stores them one by one
+        if (RAGGED && (Lo & 3) != 0 && o0 + G::kTW > (Lo & ~3)) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int co = cog * kCO + 16 * m + col;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int o = o0 + 16 * b + 4 * kq;
+                    if (co < Cout && o < Lo && o + 4 > Lo) {
+#pragma unroll
+                        for (int r = 0; r < 3; ++r)
+                            if (o + r < Lo)
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[m][b][r]), yr,
+                                                                      (co * Lo + o + r) * 4, 0, 0);
+                    }
+                }
             }
         }
     }
@@ -705,20 +730,18 @@ size_t convT1d_f32_lds_bytes(int64_t Cin, int K, int dilation)
     return (size_t)(4 * ksteps * 64 + cin4 * str) * sizeof(float);
 }
 
-bool convT1d_f32_wave_supported(int64_t Cin, int K, int dilation, int64_t L, int64_t Lo,
-                                const void *x, const void *out)
+bool convT1d_f32_wave_supported(int64_t Cin, int K, int dilation, int64_t L, const void *x)
 {
-    return Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 && Lo % 4 == 0 &&
-           (((uintptr_t)x) & 15) == 0 && (((uintptr_t)out) & 15) == 0;
+    return Cin == 32 && K == 5 && dilation == 3 && L % 4 == 0 && (((uintptr_t)x) & 15) == 0;
 }
 
 namespace {
-template <int HP>
+template <int HP, bool RAGGED>
 hipError_t launch_wave(const float *x, const float *w, const float *bias, int64_t N, int64_t Cin,
                        int64_t L, int64_t Cout, int64_t Lo, int pad, float *out, hipStream_t stream)
 {
     typedef WaveGeom<32, 5, 3, kWaveNB, kWaveWW, HP> G;
-    const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW, HP>;
+    const void *fn = (const void *)convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW, HP, RAGGED>;
     const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
     hipError_t e = allow_dynamic_lds(fn, lds);
     if (e != hipSuccess) return e;
@@ -728,7 +751,7 @@ hipError_t launch_wave(const float *x, const float *w, const float *bias, int64_
     const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
     int64_t gx = (int64_t)cus * per_cu / gy;
     if (gx < 1) gx = 1;
-    hipLaunchKernelGGL((convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW, HP>), dim3((unsigned)gx, gy),
+    hipLaunchKernelGGL((convT1d_f32_wave_kernel<32, 5, 3, kWaveNB, kWaveWW, HP, RAGGED>), dim3((unsigned)gx, gy),
                        dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
                        (int)Lo, wtiles_per_n, (int)wtiles, pad, out);
     return hipGetLastError();
@@ -742,10 +765,13 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
 {
     const int cin4 = (int)((Cin + 3) & ~int64_t(3));
     const int64_t Lo = L + (int64_t)dilation * (K - 1) - 2 * (int64_t)pad + out_pad;
-    if (convT1d_f32_wave_supported(Cin, K, dilation, L, Lo, x, out)) {
+    if (convT1d_f32_wave_supported(Cin, K, dilation, L, x)) {
+        const bool ragged = Lo % 4 != 0 || (((uintptr_t)out) & 15) != 0;
         if (pad == 0 && out_pad == 0)
-            return launch_wave<12>(x, w, bias, N, Cin, L, Cout, Lo, 0, out, stream);
-        return launch_wave<16>(x, w, bias, N, Cin, L, Cout, Lo, pad, out, stream);
+            return ragged ? launch_wave<12, true>(x, w, bias, N, Cin, L, Cout, Lo, 0, out, stream)
+                          : launch_wave<12, false>(x, w, bias, N, Cin, L, Cout, Lo, 0, out, stream);
+        return ragged ? launch_wave<16, true>(x, w, bias, N, Cin, L, Cout, Lo, pad, out, stream)
+                      : launch_wave<16, false>(x, w, bias, N, Cin, L, Cout, Lo, pad, out, stream);
     }
     if (pad != 0 || out_pad != 0) return hipErrorInvalidValue;   // the tile kernel has no shift
     const int tiles_per_n = (int)((Lo + kTO - 1) / kTO);

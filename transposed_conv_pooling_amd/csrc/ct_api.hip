@@ -378,25 +378,27 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
     // window); everything else not caught below on the general kernel.
     bool fast = x_dtype == CT_F32 && stride == 1 &&
                 ((pad == 0 && out_pad == 0) ||
-                 ct::convT1d_f32_wave_supported(Cin, K, dilation, L, Lo, x, out));
+                 ct::convT1d_f32_wave_supported(Cin, K, dilation, L, x));
     if (fast) {
         const int64_t tiles = (Lo + 255) / 256;
         int64_t ntiles;
-        fast = Lo <= kI32Max - 256 && prod({N, tiles}, &ntiles) && ntiles <= kI32Max &&
+        fast = Lo <= kI32Max - 256 && L <= kI32Max - 1024 && prod({N, tiles}, &ntiles) &&
+               ntiles <= kI32Max &&
                (Cout + 63) / 64 <= 65535 && Cin <= 4096 && K <= 4096 &&
                (int64_t)dilation * (K - 1) <= 65536 &&
                ct::convT1d_f32_lds_bytes(Cin, K, dilation) <= kLdsMax;
         int64_t item;           // one batch item's output within a 2 GiB buffer range
         fast = fast && prod({Cout, Lo, 4}, &item) && item < (int64_t(1) << 31) - 64;
     }
-    // bf16 at the page's geometry runs on the bf16 matrix-core kernel.
-    bool fast_bf16 = x_dtype == CT_BF16 && stride == 1 && pad == 0 && out_pad == 0 &&
+    // bf16 at the page's geometry, stride 1, runs on the bf16 matrix-core kernel.
+    bool fast_bf16 = x_dtype == CT_BF16 && stride == 1 &&
                      ct::convT1d_bf16_supported(Cin, K, dilation, L, x);
     if (fast_bf16) {
-        const int64_t tiles = (Lo + 28 + 255) / 256;
+        const int64_t tiles = (Lo + 31 + 255) / 256;
         int64_t ntiles;
         int64_t item;           // one batch item's output within a 2 GiB buffer range
-        fast_bf16 = Lo <= kI32Max - 512 && prod({N, tiles}, &ntiles) && ntiles <= kI32Max &&
+        fast_bf16 = Lo <= kI32Max - 512 && L <= kI32Max - 1024 && prod({N, tiles}, &ntiles) &&
+                    ntiles <= kI32Max &&
                     (Cout + 63) / 64 <= 65535 && prod({Cout, Lo, 4}, &item) &&
                     item < (int64_t(1) << 31) - 64;
     }
@@ -421,7 +423,7 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
                                    dilation, pad, out_pad, out, (hipStream_t)stream);
     } else if (fast_bf16) {
         e = ct::launch_convT1d_bf16((const uint16_t *)x, (const uint16_t *)w, bias, N, L, Cout, K,
-                                    dilation, out, (hipStream_t)stream);
+                                    dilation, pad, out_pad, out, (hipStream_t)stream);
     } else {
         if (Lo > kGenericMaxLen || L > kGenericMaxLen || Cin > kGenericMaxLen ||
             Cout > kGenericMaxLen || pad > kGenericMaxLen ||

@@ -60,10 +60,9 @@ bool avgpool3d_k3s2p1_fits(bool bf16, const void *x, const void *out, int64_t NC
 
 // ConvTranspose1d, stride 1, fp32: pad 0 and no output padding for any K and
 // dilation the LDS holds; with a pad or output padding only where
-// convT1d_f32_wave_supported() holds (Cin 32, K 5, dilation 3, L and the
-// output length multiples of 4, x and out 16-byte aligned).
-bool convT1d_f32_wave_supported(int64_t Cin, int K, int dilation, int64_t L, int64_t Lo,
-                                const void *x, const void *out);
+// convT1d_f32_wave_supported() holds (Cin 32, K 5, dilation 3, L a multiple
+// of 4, x 16-byte aligned; any output length and 4-byte aligned out).
+bool convT1d_f32_wave_supported(int64_t Cin, int K, int dilation, int64_t L, const void *x);
 hipError_t launch_convT1d_f32(const float *x, const float *w,
                               const float *bias, int64_t N, int64_t Cin,
                               int64_t L, int64_t Cout, int K, int dilation, int pad,
@@ -80,14 +79,14 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
                                    int pad, int dilation, int out_pad, float *out,
                                    hipStream_t stream);
 
-// ConvTranspose1d, stride 1, pad 0, bf16 x and w (fp32 accumulation and
-// output) on the bf16 matrix cores, for the geometries where
-// convT1d_bf16_supported() holds (Cin 32, K 5, dilation 3, L a multiple of 8,
-// x 16-byte aligned).
+// ConvTranspose1d, stride 1 with any pad and output padding, bf16 x and w
+// (fp32 accumulation and output) on the bf16 matrix cores, for the
+// geometries where convT1d_bf16_supported() holds (Cin 32, K 5, dilation 3,
+// L a multiple of 8, x 16-byte aligned); L below 2^31 - 1024.
 bool convT1d_bf16_supported(int64_t Cin, int K, int dilation, int64_t L, const void *x);
 hipError_t launch_convT1d_bf16(const uint16_t *x, const uint16_t *w, const float *bias,
-                               int64_t N, int64_t L, int64_t Cout, int K, int dilation,
-                               float *out, hipStream_t stream);
+                               int64_t N, int64_t L, int64_t Cout, int K, int dilation, int pad,
+                               int out_pad, float *out, hipStream_t stream);
 
 // ConvTranspose3d(k3, s2, p1), output_padding 0 or 1, 1 <= Cin <= 8, output
 // [N, Cout, 2D-1+op, 2H-1+op, 2W-1+op] materialised; x, w fp32 or bf16.
