@@ -283,6 +283,10 @@ CONV1D_GENERAL = [
     (1, 32, 64, 8, 5, 2, 9, 3, 2, True, "f32"),       # pad larger than the input
     (3, 32, 64, 1028, 5, 2, 1, 3, 1, True, "f32"),    # tiles straddling batch items
     (8, 32, 64, 20004, 5, 2, 1, 3, 1, True, "f32"),   # more tiles than waves: halos carried
+    (8, 32, 64, 20004, 5, 2, 0, 3, 0, True, "f32"),   # even pad over many tiles
+    (4, 32, 64, 20000, 5, 2, 2, 3, 1, False, "f32"),
+    (4, 32, 64, 20000, 5, 2, 3, 3, 0, True, "f32"),   # odd output length: 4-byte aligned pairs
+    (3, 32, 40, 4000, 5, 2, 4, 3, 2, True, "f32"),    # odd output length, even pad
     # stride 1 with a pad or output padding on the fp32 matrix cores (the
     # unpadded kernel over a shifted output window; output length % 4 == 0):
     # pads of every residue mod 4, "same" padding, pad past the halo

@@ -459,9 +459,7 @@ struct PolyGeom {
     static constexpr int kLdsFloats = kWfrag + kCO + WW * CIN4 * kStr;
 };
 
-// PODD: the parity of pad, which fixes how the two residue classes pair up
-// into 8-byte stores (compile-time, so the store code has no branches on it).
-template <int CIN4, int K, int DIL, int S, int NB, int WW, int PODD>
+template <int CIN4, int K, int DIL, int S, int NB, int WW>
 __global__ __launch_bounds__(64 * WW, 1)
 void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restrict__ w,
                              const float *__restrict__ bias, int Cin, int L, int Cout, int Lo,
@@ -510,18 +508,11 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
     const int t_begin = (int)(gw * per + (gw < rem ? gw : rem));
     const int t_end = t_begin + per + (gw < rem ? 1 : 0);
 
-    // byte offsets of this lane's output rows co = 16m + 4kq + r of the channel
-    // block within a batch item (an item's output is below 2^31 bytes)
-    int rowb[4][4];
-    bool rowok[4][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int co = cog * kCO + 16 * m + 4 * kq + r;
-            rowok[m][r] = co < Cout;
-            rowb[m][r] = co * Lo * 4;
-        }
+    // byte offset of this lane's output row co = cog*64 + 4kq within a batch
+    // item (an item's output is below 2^31 bytes; rows 16m + r further on
+    // add a wave-uniform multiple of Lo) and the rows left in the block
+    const int row0b = (cog * kCO + 4 * kq) * Lo * 4;
+    const int rows_left = Cout - cog * kCO - 4 * kq;
 
     // strip piece q = ci * (kTs/4) + t4 covers inputs q0 - HP + 4*t4 .. +3
     // (L % 4 == 0 and q0 - HP = 0 mod 4: a piece is wholly inside or outside
@@ -627,67 +618,46 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
             }
         });
 
-        // Stores.  With S = 2 the two classes interleave: outputs o and o+1
-        // (o even) are (class 0, class 1) at one q when pad is even, and
-        // (class 1 at q, class 0 at q+1) when pad is odd; the second comes
-        // from the next lane of the 16-lane row (a DPP rotate) or, at the
-        // row's end, from lane 0 of the next q block.  Each such pair is one
-        // 8-byte store (o even and Lo even keep it 8-byte aligned), so 16
-        // lanes write 128 contiguous bytes of one channel.  Tiles whose
-        // outputs reach past either end of the row, and odd Lo, take one
-        // 4-byte store per output instead.
+        // Stores.  With S = 2, class 0 at q is output 2q - pad and class 1
+        // at q is output 2q + 1 - pad, so each lane's pair of values is one
+        // 8-byte store and 16 lanes write 128 contiguous bytes of one
+        // channel.  A pair is 8-byte aligned when pad and Lo are even;
+        // otherwise 4-byte aligned, which gfx950's vector memory accepts
+        // (the compiler emits such stores for 4-byte-aligned data).  Tiles
+        // whose outputs reach past either end of the row take one 4-byte
+        // store per output instead.
         static_assert(S == 2, "paired stores are written for stride 2");
-        constexpr bool podd = PODD != 0;
-        const int olo = 2 * q0 - pad, ohi = 2 * (q0 + G::kTQ) + 1 - pad;   // tile's output span
-        const bool paired = (Lo % 2 == 0) && olo >= 0 && ohi < Lo;
+        const int olo = 2 * q0 - pad, ohi = 2 * (q0 + G::kTQ) - 1 - pad;   // tile's first, last output
+        const bool paired = olo >= 0 && ohi < Lo;
         if (paired) {
             typedef float v2f_ __attribute__((ext_vector_type(2)));
             typedef int v2i_ __attribute__((ext_vector_type(2)));
             // byte offset of this lane's first pair in row co = 16m + 4kq + r
-            // of the channel block (rowb[m][r] = co*Lo*4, hoisted below), and
-            // an offset past the output for lanes that store nothing (with
-            // the constant per-block offsets added it stays below 2^32 and
-            // above the output's size)
+            // of the channel block (row0b plus (16m + r) rows), and an offset
+            // past the output for lanes that store nothing (with the
+            // constant per-block offsets added it stays below 2^32 and above
+            // the output's size)
             constexpr unsigned kOff = 0x80000000u;
-            const int ob = (2 * (q0 + col) + (podd ? 1 : 0) - pad) * 4;
+            const int ob = (2 * (q0 + col) - pad) * 4;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const unsigned base = rowok[m][r] ? (unsigned)(rowb[m][r] + ob) : kOff;
+                    const bool rowok = 16 * m + r < rows_left;
+                    const int rowb = row0b + (16 * m + r) * Lo * 4;
+                    const unsigned base = rowok ? (unsigned)(rowb + ob) : kOff;
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        float v0, v1;
-                        unsigned off = base + 128u * b;            // 16 q = 32 outputs per block
-                        if (!podd) {
-                            v0 = acc[0][m][b][r];
-                            v1 = acc[1][m][b][r];
-                        } else {
-                            // lane col takes class 0 of q+1: lane col+1, or lane 0 of block b+1
-                            const float nx = __int_as_float(__builtin_amdgcn_update_dpp(
-                                0, __float_as_int(acc[0][m][b][r]), 0x12F, 0xf, 0xf, false));   // row_ror:15
-                            v0 = acc[1][m][b][r];
-                            if (b + 1 < NB) {
-                                const float nb = __int_as_float(__builtin_amdgcn_update_dpp(
-                                    0, __float_as_int(acc[0][m][b + 1 < NB ? b + 1 : b][r]), 0x12F, 0xf, 0xf, false));
-                                v1 = col == 15 ? nb : nx;
-                            } else {
-                                v1 = nx;
-                                if (col == 15) off = kOff;         // its partner is in the next tile
-                            }
-                        }
+                        // identity DPP moves: the pair goes out through VGPRs
+                        // (taken straight from the accumulators, whose two
+                        // values are not adjacent registers, it made the
+                        // compiler spill 85 registers)
+                        const float v0 = __int_as_float(__builtin_amdgcn_update_dpp(
+                            0, __float_as_int(acc[0][m][b][r]), 0xE4, 0xf, 0xf, false));   // quad_perm:[0,1,2,3]
+                        const float v1 = __int_as_float(__builtin_amdgcn_update_dpp(
+                            0, __float_as_int(acc[1][m][b][r]), 0xE4, 0xf, 0xf, false));
                         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_, (v2f_){v0, v1}), yr,
-                                                              (int)off, 0, 0);
-                    }
-                    if (podd) {
-                        // the unpaired ends: class 0 at q0 (o = 2*q0 - pad, lane 0)
-                        // and class 1 at the tile's last q (lane 15 of the last block)
-                        const bool first = col == 0, last = col == 15;
-                        const float v = first ? acc[0][m][0][r] : acc[1][m][NB - 1][r];
-                        const unsigned off = !rowok[m][r] || !(first || last) ? kOff
-                                             : first ? (unsigned)(rowb[m][r] + (2 * q0 - pad) * 4)
-                                                     : (unsigned)(rowb[m][r] + (2 * (q0 + G::kTQ - 1) + 1 - pad) * 4);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yr, (int)off, 0, 0);
+                                                              (int)(base + 128u * b), 0, 0);   // 16 q = 32 outputs per block
                     }
                 }
         } else {
@@ -822,8 +792,7 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     const int64_t qb = (Lo + pad + S - 1) / S;
     const int tq_per_n = (int)((qb - qa4 + G::kTQ - 1) / G::kTQ);
     const int64_t ntiles = N * tq_per_n;
-    const void *fn = (pad & 1) ? (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 1>
-                               : (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 0>;
+    const void *fn = (const void *)convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW>;
     const size_t lds = (size_t)G::kLdsFloats * sizeof(float);
     hipError_t e = allow_dynamic_lds(fn, lds);
     if (e != hipSuccess) return e;
@@ -831,14 +800,9 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     const unsigned gy = (unsigned)((Cout + kCO - 1) / kCO);
     int64_t gx = (int64_t)cus * per_cu / gy;
     if (gx < 1) gx = 1;
-    if (pad & 1)
-        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 1>), dim3((unsigned)gx, gy),
-                           dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
-                           (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
-    else
-        hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW, 0>), dim3((unsigned)gx, gy),
-                           dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
-                           (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
+    hipLaunchKernelGGL((convT1d_f32_poly_kernel<32, 5, 3, S, NB, WW>), dim3((unsigned)gx, gy),
+                       dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
+                       (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
     return hipGetLastError();
 }
 
