@@ -177,9 +177,11 @@ CT_API ct_status ct_convT3d(const void *x, int x_dtype,
  *
  * Geometry: k >= 1, stride >= 0 (0 = k), 0 <= pad <= k/2 (PyTorch's rule),
  * floor mode.  k = 3, stride 2, pad 1 (either count_include_pad) runs on a
- * separable streaming kernel (per-slice size below 2^31 elements); anything
- * else on a general gather kernel (one thread per output; lengths and
- * stride up to 2^30, k up to 1024, else CT_EUNSUPPORTED).
+ * streaming kernel that reads each input once (per-slice size below 2^31
+ * elements): planes of at most 4096 elements several slices per workgroup
+ * through LDS, larger ones as separable row sums; anything else on a
+ * general gather kernel (one thread per output; lengths and stride up to
+ * 2^30, k up to 1024, else CT_EUNSUPPORTED).
  */
 CT_API ct_status ct_avgpool3d(const float *x,
                        int64_t N, int64_t C, int64_t D, int64_t H, int64_t W,

@@ -205,11 +205,17 @@ POOL_GENERAL = [
     ((1, 1, 1, 1, 1), 1, 2, 0, False),
     ((1, 2, 2, 3, 300), 2, 1, 1, False),
     # the page's window with the valid-tap divisor on the streaming kernels
-    ((2, 5, 9, 10, 16), 3, 2, 1, False),     # vector kernel, one column chunk
-    ((1, 2, 5, 6, 260), 3, 2, 1, False),     # two column chunks
-    ((40, 8, 12, 10, 16), 3, 2, 1, False),   # 320 slices in plane ranges (bf16 staggered starts)
+    ((2, 5, 9, 10, 16), 3, 2, 1, False),     # small-plane kernel
+    ((1, 2, 5, 6, 260), 3, 2, 1, False),
+    ((40, 8, 12, 10, 16), 3, 2, 1, False),   # 320 slices, several per workgroup
     ((1, 1, 1, 1, 4), 3, 2, 1, False),       # length-1 axes: one valid tap
-    ((1, 1, 2, 131, 8), 3, 2, 1, False),     # two row groups
+    ((1, 1, 2, 131, 8), 3, 2, 1, False),
+    ((2, 3, 7, 9, 31), 3, 2, 1, False),      # small-plane kernel, element loads
+    ((2, 5, 9, 70, 64), 3, 2, 1, False),     # vector kernel, one column chunk
+    ((1, 2, 5, 18, 260), 3, 2, 1, False),    # vector kernel, two column chunks
+    ((40, 8, 12, 34, 128), 3, 2, 1, False),  # 320 slices in plane ranges (bf16 staggered starts)
+    ((1, 1, 2, 131, 40), 3, 2, 1, False),    # two row groups
+    ((1, 2, 3, 70, 63), 3, 2, 1, False),     # element kernel
 ]
 
 

@@ -227,20 +227,30 @@ def test_fused_bf16_small(dev, shape, with_cb):
 
 # ------------------------------------------------------------ avgpool3d ----
 POOL_SMALL = [
+    # planes of at most 4096 elements: the small-plane kernel (several
+    # slices per workgroup, 4-element loads when W % 4 == 0, else 1)
     (1, 1, 1, 1, 1),
     (1, 1, 2, 2, 2),
     (2, 3, 9, 10, 13),
     (1, 2, 5, 6, 256),
-    (1, 1, 3, 4, 260),        # two column chunks, vector path
-    (1, 1, 4, 5, 514),        # two column chunks, element path
-    (1, 2, 33, 35, 64),       # several plane chunks and row groups
+    (1, 1, 3, 4, 260),
+    (1, 1, 4, 5, 514),        # element loads, the widest row that fits
+    (1, 2, 33, 35, 64),       # several plane chunks
     (2, 1, 7, 3, 1),
-    (1, 1, 3, 131, 8),        # two row groups: the row above a group comes from memory
-    (1, 1, 2, 140, 264),      # two row groups and two column chunks
-    (1, 1, 5, 258, 520),      # three row groups, three column chunks, ragged last of each
+    (1, 1, 3, 131, 8),
     (4, 25, 40, 6, 8),        # 100 slices: several plane chunks of more than one plane
     (3, 1, 1, 4, 4),          # a single input plane
-    (8, 40, 40, 10, 16),      # 320 slices in ranges of 10 planes: every start offset of a bf16 range
+    (8, 40, 40, 10, 16),      # 320 slices, 10 per workgroup
+    (64, 16, 8, 16, 16),      # 1024 slices of 16 x 16 planes
+    (3, 5, 9, 64, 64),        # one slice per workgroup (4096-element planes)
+    # larger planes: the vector kernel (W % 4 == 0) or the element kernel
+    (1, 1, 3, 20, 260),       # two column chunks, vector path
+    (1, 1, 4, 9, 514),        # two column chunks, element path
+    (1, 2, 33, 135, 64),      # several plane chunks and row groups
+    (1, 1, 3, 131, 40),       # two row groups: the row above a group comes from memory
+    (1, 1, 2, 140, 264),      # two row groups and two column chunks
+    (1, 1, 5, 258, 520),      # three row groups, three column chunks, ragged last of each
+    (8, 40, 20, 34, 128),     # 320 slices in ranges of 10 planes: every start offset of a bf16 range
 ]
 
 
@@ -256,13 +266,14 @@ def test_pool_small(dev, shape):
     assert_close(out.cpu().numpy(), oracle.avgpool3d(x, 3, 2, 1, True), F32_TOL, f"pool {shape}")
 
 
-def test_pool_misaligned_input_takes_element_path(dev):
-    shape = (2, 2, 6, 7, 64)
+@pytest.mark.parametrize("shape", [(2, 2, 6, 7, 64), (2, 2, 6, 70, 64)],
+                         ids=["small-plane element loads", "element kernel"])
+def test_pool_misaligned_input_takes_element_loads(dev, shape):
     x = synth.normal(31, 0, shape)
     buf = torch.empty(x.size + 1, dtype=torch.float32, device=dev)
     buf[1:] = torch.from_numpy(x.reshape(-1)).to(dev)
     xg = buf[1:].view(shape)                        # 4-byte but not 16-byte aligned
-    out = nan_like((2, 2, 3, 4, 32), dev)
+    out = nan_like(shape[:2] + tuple((n - 1) // 2 + 1 for n in shape[2:]), dev)
     ct.ct_avgpool3d(xg, 3, 2, 1, True, out=out)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy(), oracle.avgpool3d(x, 3, 2, 1, True), F32_TOL, "misaligned")
@@ -310,9 +321,10 @@ def test_pool_bf16_small(dev, shape):
                  f"pool bf16 {shape}")
 
 
+@pytest.mark.parametrize("shape", [(2, 2, 6, 7, 64), (2, 2, 6, 70, 64)],
+                         ids=["small-plane element loads", "element kernel"])
 @pytest.mark.parametrize("shift", [1, 2], ids=["2-byte", "4-byte"])
-def test_pool_bf16_misaligned_input_takes_element_path(dev, shift):
-    shape = (2, 2, 6, 7, 64)
+def test_pool_bf16_misaligned_input_takes_element_loads(dev, shift, shape):
     x = bf16_round(synth.normal(33, 0, shape))
     assert_close(pool_bf16(dev, x, shift), oracle.avgpool3d(x, 3, 2, 1, True), POOL_BF16_TOL,
                  f"pool bf16 shifted by {shift}")

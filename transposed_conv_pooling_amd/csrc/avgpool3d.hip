@@ -45,9 +45,13 @@
 //    workgroups start at staggered plane offsets and wrap around, so that
 //    the workgroups running together stream different offsets of their
 //    slices, at the cost of one plane read twice.
-// Other inputs (ragged W, misaligned x or out, planes of 2^30 bytes or more)
-// take the element kernel: one wave per 4 output rows, element-wise masked
-// loads, same arithmetic.
+// Planes of at most 4096 elements (a 64 x 64 plane, or 8 x 512) take the
+// small-plane kernel below instead, which fills its workgroups with several
+// slices.  Other inputs (ragged W, misaligned x or out, planes of 2^30 bytes
+// or more) take the element kernel: one wave per 4 output rows,
+// element-wise masked loads, same arithmetic.
+#include <algorithm>
+
 #include "ct_internal.h"
 
 namespace ct {
@@ -426,13 +430,161 @@ void avgpool3d_k3s2p1_elem_kernel(const E *__restrict__ x, E *__restrict__ out,
     }
 }
 
+// ------------------------------------------------------ small-plane kernel --
+// Planes of at most kSElems elements whose bordered copy fits one LDS buffer.
+// The kernels above give a wave 4 output rows x 128 output columns, which a
+// small plane fills only in part (a 16 x 16 plane: 2 of 16 rows, 4 of 64
+// lanes).  Here a workgroup takes S whole slices and walks output planes
+// [d0, d1): each input plane of the S slices is loaded once (VW consecutive
+// elements per load), widened into an LDS buffer with a zero border (one row
+// above and below, one column left and right), and every output of the S
+// slices sums its 3x3 window there, so no tap needs a bounds test.  Output
+// plane d adds the window sums of input planes 2d-1, 2d and 2d+1; the last
+// is carried to d+1.  The next plane's loads are in flight while a plane is
+// summed; the buffer is double-buffered by plane, one barrier per plane.
+constexpr int kSThreads = 256;
+constexpr int kSElems = 4096;                // elements of one input plane of the S slices
+constexpr int kSOut = 8;                     // outputs per work-item
+constexpr int kSBufBytes = 24 * 1024;        // one LDS plane buffer
+
+// LDS geometry of one slice's plane: rows -1 .. H (zero rows -1 and H),
+// columns at +4 of their index (zero columns 3 and W + 4), so that a row's
+// first element is 16-byte aligned.
+__host__ __device__ constexpr int plane_pitch(int W) { return W + 8; }
+__host__ __device__ constexpr int plane_floats(int H, int W) { return (H + 2) * plane_pitch(W); }
+
+template <typename E, int VW>
+struct Piece;
+template <> struct Piece<float, 4> {
+    typedef v4f raw;
+    static __device__ __forceinline__ raw zero() { return v4f{0.0f, 0.0f, 0.0f, 0.0f}; }
+    static __device__ __forceinline__ raw load(const float *p) { return *reinterpret_cast<const v4f *>(p); }
+    static __device__ __forceinline__ void put(float *d, raw v) { *reinterpret_cast<v4f *>(d) = v; }
+};
+template <> struct Piece<uint16_t, 4> {
+    typedef u32x2 raw;
+    static __device__ __forceinline__ raw zero() { return u32x2{0u, 0u}; }
+    static __device__ __forceinline__ raw load(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
+    static __device__ __forceinline__ void put(float *d, raw v) { *reinterpret_cast<v4f *>(d) = Elem<uint16_t>::widen(v); }
+};
+template <typename E> struct Piece<E, 1> {
+    typedef E raw;
+    static __device__ __forceinline__ raw zero() { return (E)0; }
+    static __device__ __forceinline__ raw load(const E *p) { return *p; }
+    static __device__ __forceinline__ void put(float *d, raw v) { *d = Elem<E>::to_f32(v); }
+};
+
+template <typename E, int VW, bool kIncl>
+__global__ __launch_bounds__(kSThreads)
+void avgpool3d_k3s2p1_plane_kernel(const E *__restrict__ x, E *__restrict__ out, int64_t NC,
+                                   int D, int H, int W, int Do, int Ho, int Wo, int S,
+                                   int dchunks, int td)
+{
+    constexpr int kP = kSElems / VW / kSThreads;      // pieces per work-item
+    typedef Piece<E, VW> PC;
+    extern __shared__ float lds[];                   // [2][S][H + 2][pitch]
+    const int tid = threadIdx.x;
+    const int pitch = plane_pitch(W);
+    const int pf = plane_floats(H, W);
+    const int buf = S * pf;
+    const int sg = (int)(blockIdx.x / dchunks), dc = (int)(blockIdx.x % dchunks);
+    const int64_t s0 = (int64_t)sg * S;
+    const int ns = (int)min((int64_t)S, NC - s0);
+    const int d0 = dc * td, d1 = min(d0 + td, Do);
+    const int64_t HW = (int64_t)H * W, DHW = (int64_t)D * HW;
+
+    // both buffers start zero: the border is never written afterwards
+    for (int i = tid; i < 2 * buf; i += kSThreads) lds[i] = 0.0f;
+
+    // pieces: q = tid + 256*i -> slice q / pps, row r, first column c
+    const int wv = W / VW, pps = H * wv;
+    const E *src[kP];
+    int loff[kP];
+    bool pv[kP];
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+        const int q = tid + kSThreads * i;
+        pv[i] = q < ns * pps;
+        const int sl = pv[i] ? q / pps : 0, e = pv[i] ? q - sl * pps : 0;
+        const int r = e / wv, c = (e - r * wv) * VW;
+        src[i] = x + (s0 + sl) * DHW + (int64_t)r * W + c;
+        loff[i] = sl * pf + (r + 1) * pitch + 4 + c;
+    }
+    // outputs: o = tid + 256*j -> slice, ho, wo; window top-left in LDS
+    const int opp = Ho * Wo;
+    E *dst[kSOut];
+    int lb[kSOut];
+    float chw[kSOut], acc[kSOut];
+    bool ov[kSOut];
+#pragma unroll
+    for (int j = 0; j < kSOut; ++j) {
+        const int o = tid + kSThreads * j;
+        ov[j] = o < ns * opp;
+        const int sl = ov[j] ? o / opp : 0, e = ov[j] ? o - sl * opp : 0;
+        const int ho = e / Wo, wo = e - ho * Wo;
+        dst[j] = out + (s0 + sl) * (int64_t)Do * opp + e;
+        lb[j] = sl * pf + 2 * ho * pitch + 2 * wo + 3;
+        chw[j] = (float)(taps3(ho, H) * taps3(wo, W));
+        acc[j] = 0.0f;
+    }
+
+    typename PC::raw pre[kP];
+    auto load = [&](int p) {
+        const bool pok = p >= 0 && p < D;
+        const int64_t po = pok ? (int64_t)p * HW : 0;
+#pragma unroll
+        for (int i = 0; i < kP; ++i) {
+            const bool ok = pok && pv[i];
+            const typename PC::raw v = PC::load(ok ? src[i] + po : x);
+            pre[i] = ok ? v : PC::zero();
+        }
+    };
+    const int pa = 2 * d0 - 1, pb = 2 * d1 - 1;
+    load(pa);
+    for (int p = pa; p <= pb; ++p) {
+        const int k = p - pa;
+        float *B = lds + (k & 1) * buf;
+        // this buffer was last read two planes ago, before the previous
+        // plane's barrier
+#pragma unroll
+        for (int i = 0; i < kP; ++i)
+            if (pv[i]) PC::put(B + loff[i], pre[i]);
+        if (p < pb) load(p + 1);
+        // keeps the next plane's loads ahead of the barrier
+        asm volatile("" ::: "memory");
+        __syncthreads();
+        const int d = d0 + (k - 2) / 2;               // output plane finished at even k >= 2
+#pragma unroll
+        for (int j = 0; j < kSOut; ++j) {
+            if (!ov[j]) continue;
+            const float *t = B + lb[j];
+            const float s2 = (t[0] + t[1] + t[2]) + (t[pitch] + t[pitch + 1] + t[pitch + 2]) +
+                             (t[2 * pitch] + t[2 * pitch + 1] + t[2 * pitch + 2]);
+            if (k == 0) {
+                acc[j] = s2;
+            } else if (k & 1) {
+                acc[j] += s2;
+            } else {
+                const float sum = acc[j] + s2;
+                const float o = kIncl ? sum * (1.0f / 27.0f)
+                                      : sum * (1.0f / ((float)taps3(d, D) * chw[j]));
+                dst[j][(int64_t)d * opp] = Elem<E>::from_f32(o);
+                acc[j] = s2;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 namespace {
 // Launch shape of the streaming kernels for one call.
 struct PoolPlan {
-    bool vec;          // vector kernel (else the element kernel)
+    bool vec;          // vector kernel
+    bool small;        // small-plane kernel (else, without vec, the element kernel)
     int Do, Ho, Wo, hgroups, wchunks, dchunks, td;
+    int S, vw;         // small-plane kernel: slices per workgroup, elements per load
+    size_t lds;        // small-plane kernel: dynamic LDS bytes
     int64_t nwg;       // workgroups
     int threads;       // work-items per workgroup
 };
@@ -445,6 +597,34 @@ PoolPlan plan_k3s2p1(int es, const void *x, const void *out, int64_t NC, int64_t
     p.Ho = (int)((H - 1) / 2 + 1);
     p.Wo = (int)((W - 1) / 2 + 1);
     p.wchunks = (p.Wo + kTW - 1) / kTW;
+    p.vec = false;
+    p.small = H * W <= kSElems && plane_floats((int)H, (int)W) * 4 <= kSBufBytes &&
+              (int64_t)p.Ho * p.Wo <= (int64_t)kSThreads * kSOut;
+    if (p.small) {
+        // slices per workgroup: as many as the LDS buffer, the loads (kSElems
+        // elements) and the outputs (kSOut per work-item) allow
+        int64_t S = kSBufBytes / (plane_floats((int)H, (int)W) * 4);
+        S = std::min<int64_t>(S, kSElems / (H * W));
+        S = std::min<int64_t>(S, (int64_t)kSThreads * kSOut / ((int64_t)p.Ho * p.Wo));
+        S = std::min<int64_t>(S, NC);
+        p.S = (int)S;
+        p.vw = (W % 4 == 0 && (reinterpret_cast<uintptr_t>(x) % (4 * es)) == 0) ? 4 : 1;
+        p.lds = (size_t)2 * p.S * plane_floats((int)H, (int)W) * sizeof(float);
+        // plane chunks (each re-reads one halo plane) until the grid has about
+        // four workgroups per CU, none shorter than two output planes
+        const int64_t groups = (NC + p.S - 1) / p.S;
+        const int64_t want = (int64_t)device_cus() * 4;
+        int64_t dchunks = (want + groups - 1) / groups;
+        if (dchunks > p.Do) dchunks = p.Do;
+        int64_t td = (p.Do + dchunks - 1) / dchunks;
+        if (td < 2) td = std::min<int64_t>(2, p.Do);
+        p.td = (int)td;
+        p.dchunks = (int)((p.Do + td - 1) / td);
+        p.hgroups = 1;
+        p.nwg = groups * p.dchunks;
+        p.threads = kSThreads;
+        return p;
+    }
     // vector path: 4 elements per lane load, 2 per lane store, planes < 2^30 bytes
     p.vec = (W % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) % (4 * es)) == 0) &&
             ((reinterpret_cast<uintptr_t>(out) % (2 * es)) == 0) && H * W * es < (int64_t)kOOB;
@@ -476,7 +656,20 @@ hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W
 {
     const PoolPlan p = plan_k3s2p1((int)sizeof(E), x, out, NC, D, H, W);
     if (p.nwg * p.threads > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
-    if (p.vec) {
+    if (p.small) {
+        const void *fn = p.vw == 4 ? (const void *)avgpool3d_k3s2p1_plane_kernel<E, 4, kIncl>
+                                   : (const void *)avgpool3d_k3s2p1_plane_kernel<E, 1, kIncl>;
+        hipError_t e = allow_dynamic_lds(fn, p.lds);
+        if (e != hipSuccess) return e;
+        if (p.vw == 4)
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_plane_kernel<E, 4, kIncl>), dim3((unsigned)p.nwg),
+                               dim3(kSThreads), p.lds, stream, x, out, NC, (int)D, (int)H, (int)W,
+                               p.Do, p.Ho, p.Wo, p.S, p.dchunks, p.td);
+        else
+            hipLaunchKernelGGL((avgpool3d_k3s2p1_plane_kernel<E, 1, kIncl>), dim3((unsigned)p.nwg),
+                               dim3(kSThreads), p.lds, stream, x, out, NC, (int)D, (int)H, (int)W,
+                               p.Do, p.Ho, p.Wo, p.S, p.dchunks, p.td);
+    } else if (p.vec) {
         if (p.wchunks > 1)
             hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true, kIncl>), dim3((unsigned)p.nwg),
                                dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do,
