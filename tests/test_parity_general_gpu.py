@@ -216,6 +216,7 @@ POOL_GENERAL = [
     ((40, 8, 12, 34, 128), 3, 2, 1, False),  # 320 slices in plane ranges (bf16 staggered starts)
     ((1, 1, 2, 131, 40), 3, 2, 1, False),    # two row groups
     ((1, 2, 3, 70, 63), 3, 2, 1, False),     # element kernel
+    ((1, 2, 3, 30, 1024), 3, 2, 1, False),   # vector kernel, 4 column groups
 ]
 
 

@@ -251,6 +251,11 @@ POOL_SMALL = [
     (1, 1, 2, 140, 264),      # two row groups and two column chunks
     (1, 1, 5, 258, 520),      # three row groups, three column chunks, ragged last of each
     (8, 40, 20, 34, 128),     # 320 slices in ranges of 10 planes: every start offset of a bf16 range
+    # fewer than 128 rows, several column chunks: the vector kernel's waves
+    # split into 2, 4 or 8 column groups (some past W)
+    (2, 3, 5, 60, 600),       # 2 groups, 3 chunks: one group of the second workgroup idle
+    (1, 2, 3, 30, 1024),      # 4 groups
+    (1, 1, 3, 12, 2100),      # 8 groups, 9 chunks
 ]
 
 

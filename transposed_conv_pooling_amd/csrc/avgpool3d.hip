@@ -150,22 +150,26 @@ struct Rows {
     float lf;
 };
 
-template <typename E, bool kWide>
+// kG: column groups per workgroup; the kVWaves/kG waves of a group share its
+// kGroupIn/kG input rows (wave wv of the group holds rows wv, wv + kVWaves/kG,
+// ... of them).
+template <typename E, bool kWide, int kG>
 __device__ __forceinline__ void issue_plane(Rows<E> &R, const E *xs, int p, bool want, int D, int H,
                                             int W, int rowbase, int wave, int lane,
                                             unsigned laneoff, int c0w)
 {
+    constexpr int kNW = kVWaves / kG;
     const bool ok = want && p >= 0 && p < D;
     constexpr int ES = (int)sizeof(E);
     const __amdgpu_buffer_rsrc_t rs = plane_rsrc(xs + (int64_t)(ok ? p : 0) * H * W, ok, H * W * ES);
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) {
-        const int row = rowbase + wave + kVWaves * k;
+        const int row = rowbase + wave + kNW * k;
         const unsigned roff = row < H ? (unsigned)(row * W * ES) : kOOB;
         R.v[k] = Elem<E>::template load4<2>(rs, roff + laneoff);
     }
     if (kWide) {
-        const int row = rowbase + wave + kVWaves * lane;
+        const int row = rowbase + wave + kNW * lane;
         const unsigned loff = (lane < kOwn && row < H && c0w > 0)
                                   ? (unsigned)((row * W + c0w - 1) * ES) : kOOB;
         R.lf = Elem<E>::load1(rs, loff);
@@ -183,13 +187,13 @@ __device__ __forceinline__ v2f hsum(v4f v, float lf, int lane)
 }
 
 // The wave's rows of one plane, as horizontal sums, into the row table.
-template <typename E, bool kWide>
+template <typename E, bool kWide, int kG>
 __device__ __forceinline__ void put_rows(const Rows<E> &R, v2f (*T)[64], int wave, int lane)
 {
 #pragma unroll
     for (int k = 0; k < kOwn; ++k) {
         const int lf = kWide ? __builtin_amdgcn_readlane(__float_as_int(R.lf), k) : 0;
-        T[wave + kVWaves * k][lane] = hsum<kWide>(Elem<E>::widen(R.v[k]), __int_as_float(lf), lane);
+        T[wave + (kVWaves / kG) * k][lane] = hsum<kWide>(Elem<E>::widen(R.v[k]), __int_as_float(lf), lane);
     }
 }
 
@@ -226,31 +230,41 @@ __device__ __forceinline__ void get_vsums(v2f (*T)[64], const E *xs, int p, int 
 }
 
 // Grid: one workgroup per (slice, plane chunk of td output planes, column
-// chunk, row group of kGroupRows output rows), row groups fastest.
-template <typename E, bool kWide, bool kIncl>
+// chunk, row group of kGroupRows/kG output rows), row groups fastest.  With
+// kG > 1 (planes of fewer than kGroupIn rows) the workgroup's waves form kG
+// groups, each with its own 256-column chunk (wchunks counts groups of kG
+// chunks) and kGroupIn/kG input rows, in its own rows of the row table.
+template <typename E, bool kWide, bool kIncl, int kG = 1>
 __global__ __launch_bounds__(kVThreads)
 void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
                                  int D, int H, int W, int Do, int Ho, int Wo,
                                  int hgroups, int dchunks, int wchunks, int td)
 {
+    static_assert(kG == 1 || kWide, "column groups read the element left of their chunk");
+    constexpr int kNW = kVWaves / kG;             // waves per column group
     __shared__ v2f T[2][kGroupIn][64];   // row table, double-buffered by plane
     static_assert(sizeof(T) == kVTableBytes, "row table size");
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave0 / kNW;                  // column group
+    const int wave = wave0 - grp * kNW;           // wave within the group
     int64_t t = xcd_remap(blockIdx.x, gridDim.x);
     const int64_t blk = t;
     const int hg = (int)(t % hgroups); t /= hgroups;
-    const int wc = (int)(t % wchunks); t /= wchunks;
+    const int wc = (int)(t % wchunks) * kG + grp; t /= wchunks;
     const int dc = (int)(t % dchunks); t /= dchunks;
     const int64_t sl = t;
 
-    const int rowbase = hg * kGroupIn;            // first input row of the workgroup
-    const int h0 = hg * kGroupRows + wave * kTH;  // first output row of the wave
+    const int rowbase = hg * (kGroupIn / kG);     // first input row of the group
+    const int h0 = hg * (kGroupRows / kG) + wave * kTH;   // first output row of the wave
     const int d0 = dc * td;
     const int d1 = min(d0 + td, Do);
     const int c0w = wc * (2 * kTW);
     const int c = c0w + 4 * lane;
     const int wo = wc * kTW + 2 * lane;
+    // the group's rows of the row table
+    v2f (*T0)[64] = T[0] + grp * (kGroupIn / kG);
+    v2f (*T1)[64] = T[1] + grp * (kGroupIn / kG);
     constexpr int ES = (int)sizeof(E);
     const unsigned laneoff = c < W ? (unsigned)(c * ES) : kOOB;
     // Wo is even here (W % 4 == 0), so wo < Wo covers the lane's pair
@@ -262,21 +276,21 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
     // (count_include_pad=False) valid taps along W of the lane's two outputs
     const int cw0 = taps3(wo, W), cw1 = taps3(wo + 1, W);
 
-    // Output planes [pa, pb): input planes go through T[0], T[1], T[0], ...
+    // Output planes [pa, pb): input planes go through T0, T1, T0, ...
     // starting with plane 2*pa-1
     auto run = [&](const int pa, const int pb) {
         Rows<E> A, B;
         v2f carry[kTH];
-        issue_plane<E, kWide>(A, xs, 2 * pa - 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-        issue_plane<E, kWide>(B, xs, 2 * pa, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
-        put_rows<E, kWide>(A, T[0], wave, lane);
+        issue_plane<E, kWide, kG>(A, xs, 2 * pa - 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        issue_plane<E, kWide, kG>(B, xs, 2 * pa, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        put_rows<E, kWide, kG>(A, T0, wave, lane);
         __builtin_amdgcn_sched_barrier(0);
-        issue_plane<E, kWide>(A, xs, 2 * pa + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
+        issue_plane<E, kWide, kG>(A, xs, 2 * pa + 1, true, D, H, W, rowbase, wave, lane, laneoff, c0w);
         // (an empty asm with a memory clobber after each issue keeps the loads
         // ahead of the barrier in get_vsums; without it the compiler sinks them
         // past the barrier and the LDS reads, delaying the next plane)
         asm volatile("" ::: "memory");
-        get_vsums<E, kWide>(T[0], xs, 2 * pa - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
+        get_vsums<E, kWide>(T0, xs, 2 * pa - 1, D, H, W, rowbase, wave, lane, laneoff, c0w, carry);
         // stores past the range, so that the memory-counter state entering the
         // loop matches the one at its back-edge
         const __amdgpu_buffer_rsrc_t none = plane_rsrc(os, false, 0);
@@ -287,18 +301,18 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
         for (int d = pa; d < pb; ++d) {
             const bool more = d + 1 < pb;
             v2f acc[kTH], v[kTH];
-            put_rows<E, kWide>(B, T[1], wave, lane);
+            put_rows<E, kWide, kG>(B, T1, wave, lane);
             __builtin_amdgcn_sched_barrier(0);
-            issue_plane<E, kWide>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+            issue_plane<E, kWide, kG>(B, xs, 2 * d + 2, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
             asm volatile("" ::: "memory");
-            get_vsums<E, kWide>(T[1], xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
+            get_vsums<E, kWide>(T1, xs, 2 * d, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
 #pragma unroll
             for (int i = 0; i < kTH; ++i) acc[i] = carry[i] + v[i];
-            put_rows<E, kWide>(A, T[0], wave, lane);
+            put_rows<E, kWide, kG>(A, T0, wave, lane);
             __builtin_amdgcn_sched_barrier(0);
-            issue_plane<E, kWide>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
+            issue_plane<E, kWide, kG>(A, xs, 2 * d + 3, more, D, H, W, rowbase, wave, lane, laneoff, c0w);
             asm volatile("" ::: "memory");
-            get_vsums<E, kWide>(T[0], xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
+            get_vsums<E, kWide>(T0, xs, 2 * d + 1, D, H, W, rowbase, wave, lane, laneoff, c0w, v);
             const __amdgpu_buffer_rsrc_t ro = plane_rsrc(os + (int64_t)d * Ho * Wo, true, obytes);
 #pragma unroll
             for (int i = 0; i < kTH; ++i) {
@@ -333,7 +347,7 @@ void avgpool3d_k3s2p1_vec_kernel(const E *__restrict__ x, E *__restrict__ out,
             run(d0, d1);
         } else {
             run(d0 + r, d1);
-            __syncthreads();   // the second range's prologue rewrites T[0]
+            __syncthreads();   // the second range's prologue rewrites T0
             run(d0, d0 + r);
         }
     }
@@ -583,6 +597,7 @@ struct PoolPlan {
     bool vec;          // vector kernel
     bool small;        // small-plane kernel (else, without vec, the element kernel)
     int Do, Ho, Wo, hgroups, wchunks, dchunks, td;
+    int G;             // vector kernel: column groups per workgroup
     int S, vw;         // small-plane kernel: slices per workgroup, elements per load
     size_t lds;        // small-plane kernel: dynamic LDS bytes
     int64_t nwg;       // workgroups
@@ -628,8 +643,14 @@ PoolPlan plan_k3s2p1(int es, const void *x, const void *out, int64_t NC, int64_t
     // vector path: 4 elements per lane load, 2 per lane store, planes < 2^30 bytes
     p.vec = (W % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) % (4 * es)) == 0) &&
             ((reinterpret_cast<uintptr_t>(out) % (2 * es)) == 0) && H * W * es < (int64_t)kOOB;
+    p.G = 1;
     if (p.vec) {
-        p.hgroups = (p.Ho + kGroupRows - 1) / kGroupRows;
+        // planes of fewer than kGroupIn rows: split the waves into column
+        // groups of kGroupIn/G rows each (G a power of two up to 8, no more
+        // groups than column chunks)
+        while (p.G < 8 && kGroupIn / (2 * p.G) >= H && p.G < p.wchunks) p.G *= 2;
+        p.wchunks = (p.wchunks + p.G - 1) / p.G;
+        p.hgroups = (p.Ho + kGroupRows / p.G - 1) / (kGroupRows / p.G);
         // as few plane chunks as still give every CU as many workgroups as fit
         // on it at once (one: the 128 KiB row table fills the LDS)
         const int64_t base = NC * p.hgroups * p.wchunks;
@@ -670,14 +691,15 @@ hipError_t launch_k3s2p1(const E *x, int64_t NC, int64_t D, int64_t H, int64_t W
                                dim3(kSThreads), p.lds, stream, x, out, NC, (int)D, (int)H, (int)W,
                                p.Do, p.Ho, p.Wo, p.S, p.dchunks, p.td);
     } else if (p.vec) {
-        if (p.wchunks > 1)
-            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, true, kIncl>), dim3((unsigned)p.nwg),
-                               dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do,
-                               p.Ho, p.Wo, p.hgroups, p.dchunks, p.wchunks, p.td);
-        else
-            hipLaunchKernelGGL((avgpool3d_k3s2p1_vec_kernel<E, false, kIncl>), dim3((unsigned)p.nwg),
-                               dim3(kVThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do,
-                               p.Ho, p.Wo, p.hgroups, p.dchunks, p.wchunks, p.td);
+        const void *fn = p.G == 8   ? (const void *)avgpool3d_k3s2p1_vec_kernel<E, true, kIncl, 8>
+                         : p.G == 4 ? (const void *)avgpool3d_k3s2p1_vec_kernel<E, true, kIncl, 4>
+                         : p.G == 2 ? (const void *)avgpool3d_k3s2p1_vec_kernel<E, true, kIncl, 2>
+                         : p.wchunks > 1 ? (const void *)avgpool3d_k3s2p1_vec_kernel<E, true, kIncl, 1>
+                                         : (const void *)avgpool3d_k3s2p1_vec_kernel<E, false, kIncl, 1>;
+        int iD = (int)D, iH = (int)H, iW = (int)W;
+        int Do_ = p.Do, Ho_ = p.Ho, Wo_ = p.Wo, hg = p.hgroups, dch = p.dchunks, wch = p.wchunks, td = p.td;
+        void *args[] = {(void *)&x, (void *)&out, &iD, &iH, &iW, &Do_, &Ho_, &Wo_, &hg, &dch, &wch, &td};
+        return hipLaunchKernel(fn, dim3((unsigned)p.nwg), dim3(kVThreads), args, 0, stream);
     } else {
         hipLaunchKernelGGL((avgpool3d_k3s2p1_elem_kernel<E, kIncl>), dim3((unsigned)p.nwg),
                            dim3(kEThreads), 0, stream, x, out, (int)D, (int)H, (int)W, p.Do, p.Ho,
