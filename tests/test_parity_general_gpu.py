@@ -131,6 +131,25 @@ def test_fused_bf16_misaligned_x_takes_direct_path(dev):
     assert_close(out.cpu().numpy(), ref, BF16_TOL, "bf16 misaligned")
 
 
+def test_fused_bf16_misaligned_w_takes_chunked_weights(dev):
+    # 32 input channels, 64 output channels, weights 2-byte but not 16-byte
+    # aligned: the filter is formed from the raw weights staged in LDS in
+    # 16-channel chunks instead of the whole-line weight reads
+    shape = (2, 32, 3, 5, 32)
+    x = bf16_round(synth.normal(73, 0, shape))
+    w = bf16_round(synth.uniform(73, 1, (32, 64, 3, 3, 3), -0.03, 0.03))
+    b = synth.normal(73, 2, (64,))
+    buf = torch.empty(w.size + 1, dtype=torch.bfloat16, device=dev)
+    buf[1:] = to_dev(w.reshape(-1), dev, "bf16")
+    wg = buf[1:].view(w.shape)
+    out = torch.full((2, 64, 2, 4, 31), float("nan"), dtype=torch.float32, device=dev)
+    ct.ct_convT3d_scale_pool_bias(to_dev(x, dev, "bf16"), wg, None, opt(b, dev), 0.5, 1.0,
+                                  out=out)
+    torch.cuda.synchronize()
+    ref = oracle.convT3d_scale_pool_bias(x, w, None, b, 0.5, 1.0)
+    assert_close(out.cpu().numpy(), ref, BF16_TOL, "bf16 misaligned w")
+
+
 # ------------------------------------------------- standalone ConvTranspose3d ----
 CONVT3D = [
     # N, Cin, Cout, D, H, W, k, stride, pad, out_pad, bias, dtype

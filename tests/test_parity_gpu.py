@@ -200,6 +200,12 @@ FUSED_BF16 = [
     # direct weights, but the slab is larger than the raw-weight region, so
     # the first slab is staged after the fragments are loaded
     (1, 32, 64, 2, 3, 128),
+    # 25..32 input channels, Cout a multiple of 64: weights read as whole
+    # lines in two 16-channel halves; two and three 64-channel groups, input
+    # channels padded from 27 and 29
+    (2, 32, 128, 3, 5, 32),
+    (2, 27, 192, 2, 4, 24),
+    (3, 29, 64, 4, 11, 32),
 ]
 
 

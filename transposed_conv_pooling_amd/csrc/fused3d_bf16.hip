@@ -27,9 +27,12 @@
 //    (blockIdx.y).  Prologue: every thread forms Weff and its hi/lo split
 //    for its (ci, co) pairs into a [half][tap][co][ci] table, from which each
 //    wave loads its fragments (2 output-channel blocks x all k-steps x
-//    hi/lo) into registers for the whole kernel.  With one 64-channel group
-//    a thread reads its pairs' 54 weights straight into registers, before
-//    the first slab's loads; otherwise the raw weights are staged in LDS in
+//    hi/lo) into registers for the whole kernel.  With 25..32 input
+//    channels, Cout a multiple of 64 and 16-byte aligned weights, the group's
+//    weights are read as whole lines into an LDS copy (two 16-channel
+//    halves) and the table is written in fragment order; with fewer input
+//    channels and one 64-channel group a thread reads its pairs' 54 weights
+//    straight into registers; otherwise the raw weights are staged in LDS in
 //    16-channel chunks.
 //  * Tile = (n, d, 8 pooled rows): the input slab x[n, :, d..d+1, h0..h0+8, :]
 //    is transposed to [plane][row][w][ci] in a double-buffered LDS slab.  A
@@ -70,8 +73,8 @@ __device__ __forceinline__ unsigned short f32_to_bf16(float f)
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Byte sizes of the LDS regions (shared with the launcher).
-__host__ __device__ inline int raw_bytes() { return kCiChunk * kCoGroup * 27 * 2; }
-__host__ __device__ inline int afrag_bytes(int ksteps) { return 2 * 8 * kCoGroup * (4 * ksteps + 8) * 2; }
+__host__ __device__ constexpr int raw_bytes() { return kCiChunk * kCoGroup * 27 * 2; }
+__host__ __device__ constexpr int afrag_bytes(int ksteps) { return 2 * 8 * kCoGroup * (4 * ksteps + 8) * 2; }
 // one slab: 2 planes x (th + 1) rows x W positions x cs channels (u16)
 __host__ __device__ inline int slab_bytes(int th, int W, int cs) { return 2 * (th + 1) * W * cs * 2; }
 // The epilogue constants sit after the larger of the prologue regions and the
@@ -236,50 +239,161 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
     // weights return first; the filter is formed straight from registers.
     constexpr int kCouples = Cin8 * kCoGroup / 2;
     constexpr int kCouplesPerThread = (kCouples + kThreads - 1) / kThreads;
-    const bool direct_w = (Cout == kCoGroup) && ((((uintptr_t)w) & 3) == 0);
-    unsigned wd[kCouplesPerThread][27];
+    // Line path (Cin8 = 32, Cout a multiple of 64, 16-byte aligned w): the
+    // group's 32 x 64 x 27 weights are read as whole 128-byte lines (16 bytes
+    // a lane, consecutive lanes consecutive pieces) in two halves of 16 input
+    // channels, copied to LDS, and each thread forms Weff for input channels
+    // (ci, ci+1) of one output channel from aligned dwords of that copy.  The
+    // per-couple reads of the couple path below touch a 128-byte line per
+    // lane and instruction, which held the prologue to ~4.6 us at the page's
+    // wide workload; formed this way the filter is ready ~2 us sooner.  The
+    // hi/lo halves go straight into fragment order, [cb][k-step][half][lane]
+    // x 16 bytes, so each lane's fragments are consecutive 16-byte reads.
+    constexpr bool kLinePath = (Cin8 == 32);
+    constexpr int kRawRow = kCoGroup * 27 + 16;       // u16 per input channel in the copy (+16: banks)
+    constexpr int kRawPieces = 16 * kCoGroup * 27 * 2 / 16;   // 16-byte pieces per half
+    constexpr int kRawPR = (kRawPieces + kThreads - 1) / kThreads;
+    constexpr int kTabBytes = 4 * 8 * 2 * 64 * 16;    // fragment-order table at LDS 0
+    static_assert(!kLinePath || kTabBytes + 16 * kRawRow * 2 <= raw_bytes() + afrag_bytes(8),
+                  "line-path prologue exceeds the prologue regions");
+    const bool direct_w = kLinePath
+                              ? (Cout % kCoGroup == 0) && ((((uintptr_t)w) & 15) == 0)
+                              : (Cout == kCoGroup) && ((((uintptr_t)w) & 3) == 0);
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    unsigned wd[kLinePath ? 1 : kCouplesPerThread][27];
+    u32x4 rw[kLinePath ? 2 : 1][kLinePath ? kRawPR : 1];
     if (direct_w) {
-        const unsigned *w32 = reinterpret_cast<const unsigned *>(w);
+        if constexpr (kLinePath) {
+            // piece p of half h: input channel 16h + p/216, bytes 16*(p%216)
+            // of its 64*27 weights (contiguous: Cout is a multiple of 64)
 #pragma unroll
-        for (int j = 0; j < kCouplesPerThread; ++j) {
-            const int q = tid + j * kThreads;
-            // unconditional loads (couples past Cin read couple 0, zeroed below)
-            const unsigned *src = w32 + ((q < kCouples && (q >> 5) < Cin) ? q * 27 : 0);
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int k = 0; k < 27; ++k) wd[j][k] = src[k];
+                for (int r = 0; r < kRawPR; ++r) {
+                    const int p = tid + r * kThreads;
+                    const int ci = 16 * h + p / 216;
+                    const bool ok = p < kRawPieces && ci < Cin;
+                    const unsigned short *src = ok ? w + ((int64_t)ci * Cout + co0) * 27 + 8 * (p % 216) : w;
+                    rw[h][r] = *reinterpret_cast<const u32x4 *>(src);
+                }
+        } else {
+            const unsigned *w32 = reinterpret_cast<const unsigned *>(w);
+#pragma unroll
+            for (int j = 0; j < kCouplesPerThread; ++j) {
+                const int q = tid + j * kThreads;
+                // unconditional loads (couples past Cin read couple 0, zeroed below)
+                const unsigned *src = w32 + ((q < kCouples && (q >> 5) < Cin) ? q * 27 : 0);
+#pragma unroll
+                for (int k = 0; k < 27; ++k) wd[j][k] = src[k];
+            }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     if (t_begin < t_end) fetch(n, d, hp);
     int n2 = n, d2 = d, hp2 = hp;   // the next tile to stage
-    const bool early_slab = direct_w && slab_bytes(kTH, W, CS) <= raw_bytes();
+    const bool early_slab = !kLinePath && direct_w && slab_bytes(kTH, W, CS) <= raw_bytes();
 
-    if (direct_w) {
+    if (direct_w && kLinePath) {
+        unsigned short *rawc = lds + kTabBytes / 2;
+        unsigned *tab = reinterpret_cast<unsigned *>(lds);
+        // forming thread: wave -> channel block fcb and input-channel quad
+        // fcq; lane -> output channel 16*fcb + col, input channels
+        // 16h + 8*fcq + 2*g + {0, 1}: dword g of the fragment of lane
+        // (fcq + 2h, col) of block fcb
+        const int fcb = wave & 3, fcq = wave >> 2;
+        const int fco = 16 * fcb + col;
 #pragma unroll
-        for (int j = 0; j < kCouplesPerThread; ++j) {
-            const int q = tid + j * kThreads;
-            if (q < kCouples) {
-                const int ci = q >> 5, cl = 2 * (q & 31);
-                const bool ok = ci < Cin;
+        for (int h = 0; h < 2; ++h) {
+            if (h == 1) __syncthreads();                       // half 0's copy consumed
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    float wv[27];
-#pragma unroll
-                    for (int k = 0; k < 27; ++k) {
-                        const int e = 27 * half + k;   // u16 element of the couple
-                        const unsigned u = (wd[j][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-                        wv[k] = ok ? bf16_to_f32((unsigned short)u) : 0.0f;
-                    }
-                    emit(wv, cl + half, ci);
+            for (int r = 0; r < kRawPR; ++r) {
+                const int p = tid + r * kThreads;
+                if (p < kRawPieces) {
+                    const u32x4 v = (16 * h + p / 216) < Cin ? rw[h][r] : u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(rawc + (p / 216) * kRawRow + 8 * (p % 216)) = v;
                 }
             }
+            __syncthreads();
+            float we[2][8];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                // the record's 27 weights start at u16 ro (odd when fco is
+                // odd): read the 14 aligned dwords around it and shift each
+                // pair into place
+                const int ro = (8 * fcq + 2 * g + e) * kRawRow + fco * 27;
+                const unsigned *rd = reinterpret_cast<const unsigned *>(rawc) + (ro >> 1);
+                const unsigned sh = 16u * (unsigned)(ro & 1);
+                unsigned dw[14];
+#pragma unroll
+                for (int m = 0; m < 14; ++m) dw[m] = rd[m];
+                float wv[27];
+#pragma unroll
+                for (int m = 0; m < 14; ++m) {
+                    const unsigned pr = __builtin_amdgcn_alignbit(dw[m < 13 ? m + 1 : 13], dw[m], sh);
+                    wv[2 * m] = __uint_as_float(pr << 16);
+                    if (2 * m + 1 < 27) wv[2 * m + 1] = __uint_as_float(pr & 0xffff0000u);
+                }
+                // per axis, input offset 0 takes kernel taps {1,2} and offset
+                // 1 takes tap {0}; the 3-D sums are formed axis by axis (the
+                // same sums as emit() below)
+                float s1w[9][2];
+#pragma unroll
+                for (int rr = 0; rr < 9; ++rr) {
+                    s1w[rr][0] = wv[rr * 3 + 1] + wv[rr * 3 + 2];
+                    s1w[rr][1] = wv[rr * 3 + 0];
+                }
+                float s2w[3][2][2];
+#pragma unroll
+                for (int kd = 0; kd < 3; ++kd)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        s2w[kd][0][c] = s1w[kd * 3 + 1][c] + s1w[kd * 3 + 2][c];
+                        s2w[kd][1][c] = s1w[kd * 3 + 0][c];
+                    }
+#pragma unroll
+                for (int tap = 0; tap < 8; ++tap) {
+                    const int a = tap >> 2, b = (tap >> 1) & 1, c = tap & 1;
+                    we[e][tap] = a ? s2w[0][b][c] : (s2w[1][b][c] + s2w[2][b][c]);
+                }
+            }
+            const int frag_lane = (fcq + 2 * h) * 16 + col;
+#pragma unroll
+            for (int tap = 0; tap < 8; ++tap) {
+                const unsigned short h0v = f32_to_bf16(we[0][tap]), h1v = f32_to_bf16(we[1][tap]);
+                const unsigned short l0v = f32_to_bf16(we[0][tap] - bf16_to_f32(h0v));
+                const unsigned short l1v = f32_to_bf16(we[1][tap] - bf16_to_f32(h1v));
+                tab[(((fcb * 8 + tap) * 2 + 0) * 64 + frag_lane) * 4 + g] = (unsigned)h0v | ((unsigned)h1v << 16);
+                tab[(((fcb * 8 + tap) * 2 + 1) * 64 + frag_lane) * 4 + g] = (unsigned)l0v | ((unsigned)l1v << 16);
+            }
         }
-        if (early_slab && t_begin < t_end) {
-            // slab buffer 0 lies below the filter table here: stage the first
-            // tile now and issue the second tile's loads before the fragments
-            put_all(slab, n, d, hp);
-            next_pos(n2, d2, hp2);
-            if (t_begin + 1 < t_end) fetch(n2, d2, hp2);
+    } else if (direct_w) {
+        if constexpr (!kLinePath) {
+#pragma unroll
+            for (int j = 0; j < kCouplesPerThread; ++j) {
+                const int q = tid + j * kThreads;
+                if (q < kCouples) {
+                    const int ci = q >> 5, cl = 2 * (q & 31);
+                    const bool ok = ci < Cin;
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        float wv[27];
+#pragma unroll
+                        for (int k = 0; k < 27; ++k) {
+                            const int e = 27 * half + k;   // u16 element of the couple
+                            const unsigned u = (wd[j][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+                            wv[k] = ok ? bf16_to_f32((unsigned short)u) : 0.0f;
+                        }
+                        emit(wv, cl + half, ci);
+                    }
+                }
+            }
+            if (early_slab && t_begin < t_end) {
+                // slab buffer 0 lies below the filter table here: stage the first
+                // tile now and issue the second tile's loads before the fragments
+                put_all(slab, n, d, hp);
+                next_pos(n2, d2, hp2);
+                if (t_begin + 1 < t_end) fetch(n2, d2, hp2);
+            }
         }
     } else {
         // general path: raw weights of a 16-channel chunk staged in LDS as
@@ -329,9 +443,13 @@ void fused3d_bf16_kernel(const unsigned short *__restrict__ x,
                 const int kap = 32 * j + 8 * g;
                 const int tap = kap / Cin8, ci0 = kap % Cin8;
                 // one 16-byte read: rows are 16-byte aligned (WS = Cin8 + 8),
-                // and the 80-byte row stride spreads lanes over all banks
-                A[i][j][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(
-                    weffT + ((h * 8 + tap) * kCoGroup + cl) * WS + ci0));
+                // and the 80-byte row stride spreads lanes over all banks; the
+                // line path's table is in fragment order
+                const unsigned short *src =
+                    (kLinePath && direct_w)
+                        ? lds + ((((2 * cp + i) * 8 + j) * 2 + h) * 64 + lane) * 8
+                        : weffT + ((h * 8 + tap) * kCoGroup + cl) * WS + ci0;
+                A[i][j][h] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8 *>(src));
             }
     // folded epilogue ((S/8 + cb)*s1 + b)*s2 = S*alpha + beta[co]
     const float alpha = 0.125f * s1 * s2;
