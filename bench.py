@@ -85,9 +85,10 @@ KERNELS = [
     # bf16 pool kernels first: the fp32 ones share the name prefix
     ("avgpool3d_k3s2p1_vec_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
     ("avgpool3d_k3s2p1_elem_kernel<unsigned short", "avgpool3d_bf16", "avgpool3d.hip", 4831838208),
-    # count_include_pad=False instantiations (last template argument false)
-    ("avgpool3d_k3s2p1_vec_kernel<float, false, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
-    ("avgpool3d_k3s2p1_vec_kernel<float, true, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
+    # count_include_pad=False instantiations (the include-pad template argument
+    # false; the vector kernel's column-group count follows it)
+    ("avgpool3d_k3s2p1_vec_kernel<float, false, false", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
+    ("avgpool3d_k3s2p1_vec_kernel<float, true, false", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
     ("avgpool3d_k3s2p1_elem_kernel<float, false>", "avgpool3d_nopad", "avgpool3d.hip", 9663676416),
     ("avgpool3d_k3s2p1_", "avgpool3d", "avgpool3d.hip", 9663676416),
     # the stride-2 polyphase kernel first: it shares the fp32 prefix
