@@ -313,6 +313,18 @@ CONV1D_GENERAL = [
     (4, 32, 64, 20000, 5, 2, 2, 3, 1, False, "f32"),
     (4, 32, 64, 20000, 5, 2, 3, 3, 0, True, "f32"),   # odd output length: 4-byte aligned pairs
     (3, 32, 40, 4000, 5, 2, 4, 3, 2, True, "f32"),    # odd output length, even pad
+    # stride 3 on the same kernel: three residue classes of o + pad (at
+    # dilation 3 every tap falls in class 0; classes 1 and 2 are the bias),
+    # 12-byte stores of three outputs, pads of every residue mod 3
+    (1, 32, 64, 4, 5, 3, 0, 3, 0, False, "f32"),      # shortest input
+    (2, 32, 64, 64, 5, 3, 1, 3, 1, True, "f32"),
+    (1, 32, 64, 100, 5, 3, 2, 3, 2, True, "f32"),
+    (1, 32, 70, 520, 5, 3, 3, 3, 0, True, "f32"),     # two output-channel groups, ragged
+    (1, 32, 16, 260, 5, 3, 7, 3, 1, False, "f32"),    # pad past the first tile's halo
+    (1, 32, 64, 8, 5, 3, 13, 3, 2, True, "f32"),      # pad larger than the input
+    (3, 32, 64, 1028, 5, 3, 1, 3, 1, True, "f32"),    # tiles straddling batch items
+    (8, 32, 64, 20004, 5, 3, 4, 3, 2, True, "f32"),   # more tiles than waves: halos carried
+    (4, 32, 64, 20000, 5, 3, 0, 3, 0, True, "f32"),
     # stride 1 with a pad or output padding on the fp32 matrix cores (the
     # unpadded kernel over a shifted output window; output length % 4 == 0):
     # pads of every residue mod 4, "same" padding, pad past the halo

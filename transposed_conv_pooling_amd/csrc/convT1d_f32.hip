@@ -604,7 +604,7 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
 #pragma unroll
                 for (int b = 0; b < NB; ++b) fb[buf][b] = xl[-dl + 4 * c * G::kStr + 16 * b];
             };
-            ldf(0, 0);
+            if constexpr (kSteps > 0) ldf(0, 0);     // a class without taps keeps the bias
 #pragma unroll
             for (int st = 0; st < kSteps; ++st) {
                 if (st + 1 < kSteps) ldf(st + 1, (st + 1) & 1);
@@ -618,27 +618,26 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
             }
         });
 
-        // Stores.  With S = 2, class 0 at q is output 2q - pad and class 1
-        // at q is output 2q + 1 - pad, so each lane's pair of values is one
-        // 8-byte store and 16 lanes write 128 contiguous bytes of one
-        // channel.  A pair is 8-byte aligned when pad and Lo are even;
-        // otherwise 4-byte aligned, which gfx950's vector memory accepts
-        // (the compiler emits such stores for 4-byte-aligned data).  Tiles
+        // Stores.  Class rho at q is output S*q + rho - pad, so a lane's S
+        // values at q are S consecutive outputs: with S = 2 one 8-byte store,
+        // with S = 3 one 12-byte store, and 16 lanes write 16*S contiguous
+        // floats of one channel.  The vector is 4-byte aligned when pad or
+        // Lo is not a multiple of S (gfx950's vector memory accepts such
+        // stores; the compiler emits them for 4-byte-aligned data).  Tiles
         // whose outputs reach past either end of the row take one 4-byte
         // store per output instead.
-        static_assert(S == 2, "paired stores are written for stride 2");
-        const int olo = 2 * q0 - pad, ohi = 2 * (q0 + G::kTQ) - 1 - pad;   // tile's first, last output
-        const bool paired = olo >= 0 && ohi < Lo;
-        if (paired) {
-            typedef float v2f_ __attribute__((ext_vector_type(2)));
+        const int olo = S * q0 - pad, ohi = S * (q0 + G::kTQ) - 1 - pad;   // tile's first, last output
+        const bool grouped = (S == 2 || S == 3) && olo >= 0 && ohi < Lo;
+        if (grouped) {
             typedef int v2i_ __attribute__((ext_vector_type(2)));
-            // byte offset of this lane's first pair in row co = 16m + 4kq + r
+            typedef int v3i_ __attribute__((ext_vector_type(3)));
+            // byte offset of this lane's first group in row co = 16m + 4kq + r
             // of the channel block (row0b plus (16m + r) rows), and an offset
             // past the output for lanes that store nothing (with the
             // constant per-block offsets added it stays below 2^32 and above
             // the output's size)
             constexpr unsigned kOff = 0x80000000u;
-            const int ob = (2 * (q0 + col) - pad) * 4;
+            const int ob = (S * (q0 + col) - pad) * 4;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -648,16 +647,21 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
                     const unsigned base = rowok ? (unsigned)(rowb + ob) : kOff;
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
-                        // identity DPP moves: the pair goes out through VGPRs
-                        // (taken straight from the accumulators, whose two
+                        // identity DPP moves: the group goes out through
+                        // VGPRs (taken straight from the accumulators, whose
                         // values are not adjacent registers, it made the
                         // compiler spill 85 registers)
-                        const float v0 = __int_as_float(__builtin_amdgcn_update_dpp(
-                            0, __float_as_int(acc[0][m][b][r]), 0xE4, 0xf, 0xf, false));   // quad_perm:[0,1,2,3]
-                        const float v1 = __int_as_float(__builtin_amdgcn_update_dpp(
-                            0, __float_as_int(acc[1][m][b][r]), 0xE4, 0xf, 0xf, false));
-                        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i_, (v2f_){v0, v1}), yr,
-                                                              (int)(base + 128u * b), 0, 0);   // 16 q = 32 outputs per block
+                        int v[S];
+                        static_for<0, S>([&](auto rc) {
+                            constexpr int rho = decltype(rc)::value;
+                            v[rho] = __builtin_amdgcn_update_dpp(
+                                0, __float_as_int(acc[rho][m][b][r]), 0xE4, 0xf, 0xf, false);   // quad_perm:[0,1,2,3]
+                        });
+                        const int boff = (int)(base + 64u * S * b);   // 16 q = 16*S outputs per block
+                        if constexpr (S == 2)
+                            __builtin_amdgcn_raw_buffer_store_b64((v2i_){v[0], v[1]}, yr, boff, 0, 0);
+                        else if constexpr (S == 3)
+                            __builtin_amdgcn_raw_buffer_store_b96((v3i_){v[0], v[1], v[2]}, yr, boff, 0, 0);
                     }
                 }
         } else {
@@ -766,24 +770,16 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
 bool convT1d_f32_poly_supported(int64_t Cin, int K, int stride, int dilation, int64_t L,
                                 const void *x)
 {
-    return Cin == 32 && K == 5 && dilation == 3 && stride == 2 && L % 4 == 0 &&
+    return Cin == 32 && K == 5 && dilation == 3 && (stride == 2 || stride == 3) && L % 4 == 0 &&
            (((uintptr_t)x) & 15) == 0;
 }
 
-hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *bias, int64_t N,
-                                   int64_t Cin, int64_t L, int64_t Cout, int K, int stride,
-                                   int pad, int dilation, int out_pad, float *out,
-                                   hipStream_t stream)
+namespace {
+template <int S, int NB, int WW>
+hipError_t launch_poly(const float *x, const float *w, const float *bias, int64_t N, int64_t Cin,
+                       int64_t L, int64_t Cout, int K, int pad, int dilation, int out_pad,
+                       float *out, hipStream_t stream)
 {
-    if (!convT1d_f32_poly_supported(Cin, K, stride, dilation, L, x)) return hipErrorInvalidValue;
-    constexpr int S = 2;
-    // 96-q tiles (6 blocks of 16) and 4-wave workgroups: the two classes'
-    // 48 accumulators of a wave (192 registers) live in the accumulation
-    // registers beside 256 vector registers, at one wave per SIMD.  Against
-    // 32-q tiles at two waves per SIMD (no room for more accumulators) the
-    // larger tile spreads each tile's strip handling and store setup over
-    // three times the MFMAs: 1.04 -> 0.91 ms at the page's stride-2 shape.
-    constexpr int NB = 6, WW = 4;
     typedef PolyGeom<32, 5, 3, S, NB, WW> G;
     const int64_t Lo = (L - 1) * S - 2 * (int64_t)pad + (int64_t)dilation * (K - 1) + out_pad + 1;
     // q covers o + pad = S*q + rho for every output: q in [pad/S, ceil((Lo + pad)/S)),
@@ -804,6 +800,26 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
                        dim3(G::kThreads), lds, stream, x, w, bias, (int)Cin, (int)L, (int)Cout,
                        (int)Lo, pad, (int)qa4, tq_per_n, (int)ntiles, out);
     return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *bias, int64_t N,
+                                   int64_t Cin, int64_t L, int64_t Cout, int K, int stride,
+                                   int pad, int dilation, int out_pad, float *out,
+                                   hipStream_t stream)
+{
+    if (!convT1d_f32_poly_supported(Cin, K, stride, dilation, L, x)) return hipErrorInvalidValue;
+    // 4-wave workgroups at one wave per SIMD, each wave's S classes x 4
+    // channel blocks x NB 16-q blocks of accumulators (192 registers) in the
+    // accumulation registers beside 256 vector registers.  Stride 2: 96-q
+    // tiles (6 blocks); against 32-q tiles at two waves per SIMD (no room for
+    // more accumulators) the larger tile spreads each tile's strip handling
+    // and store setup over three times the MFMAs: 1.04 -> 0.91 ms at the
+    // page's stride-2 shape.  Stride 3: 64-q tiles (4 blocks).
+    if (stride == 2)
+        return launch_poly<2, 6, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
+                                    stream);
+    return launch_poly<3, 4, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out, stream);
 }
 
 }  // namespace ct
