@@ -234,10 +234,10 @@ CT_API ct_status ct_avgpool3d_bf16(const uint16_t *x,
  *     multiple of 4, x 16-byte aligned): stride 1 with any pad and output
  *     padding on the same matrix-core kernel over a shifted output window
  *     (any L_out: when L_out % 4 != 0 or out is not 16-byte aligned, rows
- *     are stored with 4-byte aligned vectors); stride 2 or 3 with any pad
- *     and output padding as stride-1 gathers over the residue classes of
- *     o + pad on the fp32 matrix cores (at dilation 3 and stride 3 all five
- *     taps fall in one class; the other two classes' outputs are the bias).
+ *     are stored with 4-byte aligned vectors); stride 2, 3 or 4 with any
+ *     pad and output padding as stride-1 gathers over the residue classes of
+ *     o + pad on the fp32 matrix cores (a class without taps, such as
+ *     classes 1 and 2 at dilation 3 and stride 3, outputs the bias).
  *   - bf16 at the page's channels and taps (Cin 32, K 5, dilation 3), stride
  *     1 with any pad and output padding, L a multiple of 8, x 16-byte
  *     aligned: an implicit GEMM on the bf16 matrix cores with fp32

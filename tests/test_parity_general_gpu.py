@@ -325,6 +325,13 @@ CONV1D_GENERAL = [
     (3, 32, 64, 1028, 5, 3, 1, 3, 1, True, "f32"),    # tiles straddling batch items
     (8, 32, 64, 20004, 5, 3, 4, 3, 2, True, "f32"),   # more tiles than waves: halos carried
     (4, 32, 64, 20000, 5, 3, 0, 3, 0, True, "f32"),
+    # stride 4: four classes (taps {0, 4}, {3}, {2}, {1}), 16-byte stores
+    (1, 32, 64, 4, 5, 4, 0, 3, 0, False, "f32"),      # shortest input
+    (2, 32, 64, 64, 5, 4, 1, 3, 1, True, "f32"),
+    (1, 32, 70, 520, 5, 4, 3, 3, 2, True, "f32"),     # two output-channel groups, ragged
+    (1, 32, 64, 8, 5, 4, 17, 3, 3, True, "f32"),      # pad larger than the input
+    (3, 32, 64, 1028, 5, 4, 2, 3, 1, True, "f32"),    # tiles straddling batch items
+    (8, 32, 64, 20004, 5, 4, 5, 3, 0, True, "f32"),   # more tiles than waves: halos carried
     # stride 1 with a pad or output padding on the fp32 matrix cores (the
     # unpadded kernel over a shifted output window; output length % 4 == 0):
     # pads of every residue mod 4, "same" padding, pad past the halo

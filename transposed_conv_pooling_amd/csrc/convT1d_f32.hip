@@ -619,18 +619,19 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
         });
 
         // Stores.  Class rho at q is output S*q + rho - pad, so a lane's S
-        // values at q are S consecutive outputs: with S = 2 one 8-byte store,
-        // with S = 3 one 12-byte store, and 16 lanes write 16*S contiguous
+        // values at q are S consecutive outputs: one 8-, 12- or 16-byte store
+        // for S = 2, 3 or 4, and 16 lanes write 16*S contiguous
         // floats of one channel.  The vector is 4-byte aligned when pad or
         // Lo is not a multiple of S (gfx950's vector memory accepts such
         // stores; the compiler emits them for 4-byte-aligned data).  Tiles
         // whose outputs reach past either end of the row take one 4-byte
         // store per output instead.
         const int olo = S * q0 - pad, ohi = S * (q0 + G::kTQ) - 1 - pad;   // tile's first, last output
-        const bool grouped = (S == 2 || S == 3) && olo >= 0 && ohi < Lo;
+        const bool grouped = (S >= 2 && S <= 4) && olo >= 0 && ohi < Lo;
         if (grouped) {
             typedef int v2i_ __attribute__((ext_vector_type(2)));
             typedef int v3i_ __attribute__((ext_vector_type(3)));
+            typedef int v4i_ __attribute__((ext_vector_type(4)));
             // byte offset of this lane's first group in row co = 16m + 4kq + r
             // of the channel block (row0b plus (16m + r) rows), and an offset
             // past the output for lanes that store nothing (with the
@@ -662,6 +663,8 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
                             __builtin_amdgcn_raw_buffer_store_b64((v2i_){v[0], v[1]}, yr, boff, 0, 0);
                         else if constexpr (S == 3)
                             __builtin_amdgcn_raw_buffer_store_b96((v3i_){v[0], v[1], v[2]}, yr, boff, 0, 0);
+                        else if constexpr (S == 4)
+                            __builtin_amdgcn_raw_buffer_store_b128((v4i_){v[0], v[1], v[2], v[3]}, yr, boff, 0, 0);
                     }
                 }
         } else {
@@ -770,7 +773,7 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
 bool convT1d_f32_poly_supported(int64_t Cin, int K, int stride, int dilation, int64_t L,
                                 const void *x)
 {
-    return Cin == 32 && K == 5 && dilation == 3 && (stride == 2 || stride == 3) && L % 4 == 0 &&
+    return Cin == 32 && K == 5 && dilation == 3 && stride >= 2 && stride <= 4 && L % 4 == 0 &&
            (((uintptr_t)x) & 15) == 0;
 }
 
@@ -815,11 +818,15 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     // tiles (6 blocks); against 32-q tiles at two waves per SIMD (no room for
     // more accumulators) the larger tile spreads each tile's strip handling
     // and store setup over three times the MFMAs: 1.04 -> 0.91 ms at the
-    // page's stride-2 shape.  Stride 3: 64-q tiles (4 blocks).
+    // page's stride-2 shape.  Stride 3: 64-q tiles (4 blocks); stride 4: 48-q
+    // tiles (3 blocks).
     if (stride == 2)
         return launch_poly<2, 6, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
                                     stream);
-    return launch_poly<3, 4, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out, stream);
+    if (stride == 3)
+        return launch_poly<3, 4, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
+                                    stream);
+    return launch_poly<4, 3, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out, stream);
 }
 
 }  // namespace ct
