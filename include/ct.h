@@ -234,7 +234,7 @@ CT_API ct_status ct_avgpool3d_bf16(const uint16_t *x,
  *     multiple of 4, x 16-byte aligned): stride 1 with any pad and output
  *     padding on the same matrix-core kernel over a shifted output window
  *     (any L_out: when L_out % 4 != 0 or out is not 16-byte aligned, rows
- *     are stored with 4-byte aligned vectors); stride 2, 3 or 4 with any
+ *     are stored with 4-byte aligned vectors); stride 2 to 8 with any
  *     pad and output padding as stride-1 gathers over the residue classes of
  *     o + pad on the fp32 matrix cores (a class without taps, such as
  *     classes 1 and 2 at dilation 3 and stride 3, outputs the bias).

@@ -332,6 +332,19 @@ CONV1D_GENERAL = [
     (1, 32, 64, 8, 5, 4, 17, 3, 3, True, "f32"),      # pad larger than the input
     (3, 32, 64, 1028, 5, 4, 2, 3, 1, True, "f32"),    # tiles straddling batch items
     (8, 32, 64, 20004, 5, 4, 5, 3, 0, True, "f32"),   # more tiles than waves: halos carried
+    # strides 5 to 8: 32-q tiles, a 16-byte store and one of 4 to 16 bytes
+    # per lane and block; at 6 and above some classes have no tap (bias only)
+    (1, 32, 64, 4, 5, 5, 0, 3, 0, False, "f32"),      # shortest input
+    (2, 32, 70, 520, 5, 5, 3, 3, 4, True, "f32"),     # two output-channel groups, ragged
+    (3, 32, 64, 1028, 5, 5, 7, 3, 2, True, "f32"),    # tiles straddling batch items
+    (1, 32, 64, 8, 5, 6, 23, 3, 5, True, "f32"),      # pad larger than the input
+    (2, 32, 64, 300, 5, 6, 1, 3, 1, False, "f32"),
+    (4, 32, 64, 20000, 5, 6, 4, 3, 3, True, "f32"),   # more tiles than waves: halos carried
+    (1, 32, 16, 260, 5, 7, 9, 3, 6, True, "f32"),
+    (3, 32, 70, 1028, 5, 7, 2, 3, 0, True, "f32"),
+    (1, 32, 64, 4, 5, 8, 0, 3, 7, False, "f32"),      # shortest input, largest output padding
+    (2, 32, 64, 520, 5, 8, 5, 3, 1, True, "f32"),
+    (8, 32, 64, 20004, 5, 8, 12, 3, 2, True, "f32"),  # more tiles than waves: halos carried
     # stride 1 with a pad or output padding on the fp32 matrix cores (the
     # unpadded kernel over a shifted output window; output length % 4 == 0):
     # pads of every residue mod 4, "same" padding, pad past the halo

@@ -620,14 +620,14 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
 
         // Stores.  Class rho at q is output S*q + rho - pad, so a lane's S
         // values at q are S consecutive outputs: one 8-, 12- or 16-byte store
-        // for S = 2, 3 or 4, and 16 lanes write 16*S contiguous
-        // floats of one channel.  The vector is 4-byte aligned when pad or
+        // for S = 2, 3 or 4 (two stores, 16 bytes and the rest, for S = 5 to
+        // 8), and 16 lanes write 16*S contiguous floats of one channel.  The vector is 4-byte aligned when pad or
         // Lo is not a multiple of S (gfx950's vector memory accepts such
         // stores; the compiler emits them for 4-byte-aligned data).  Tiles
         // whose outputs reach past either end of the row take one 4-byte
         // store per output instead.
         const int olo = S * q0 - pad, ohi = S * (q0 + G::kTQ) - 1 - pad;   // tile's first, last output
-        const bool grouped = (S >= 2 && S <= 4) && olo >= 0 && ohi < Lo;
+        const bool grouped = olo >= 0 && ohi < Lo;
         if (grouped) {
             typedef int v2i_ __attribute__((ext_vector_type(2)));
             typedef int v3i_ __attribute__((ext_vector_type(3)));
@@ -658,13 +658,20 @@ void convT1d_f32_poly_kernel(const float *__restrict__ x, const float *__restric
                             v[rho] = __builtin_amdgcn_update_dpp(
                                 0, __float_as_int(acc[rho][m][b][r]), 0xE4, 0xf, 0xf, false);   // quad_perm:[0,1,2,3]
                         });
-                        const int boff = (int)(base + 64u * S * b);   // 16 q = 16*S outputs per block
-                        if constexpr (S == 2)
-                            __builtin_amdgcn_raw_buffer_store_b64((v2i_){v[0], v[1]}, yr, boff, 0, 0);
-                        else if constexpr (S == 3)
-                            __builtin_amdgcn_raw_buffer_store_b96((v3i_){v[0], v[1], v[2]}, yr, boff, 0, 0);
-                        else if constexpr (S == 4)
-                            __builtin_amdgcn_raw_buffer_store_b128((v4i_){v[0], v[1], v[2], v[3]}, yr, boff, 0, 0);
+                        // 16 q = 16*S outputs per block; the group goes out
+                        // in pieces of up to four values
+                        static_for<0, (S + 3) / 4>([&](auto pc) {
+                            constexpr int c = decltype(pc)::value, n = S - 4 * c < 4 ? S - 4 * c : 4;
+                            const int boff = (int)(base + 64u * S * b + 16u * c);
+                            if constexpr (n == 1)
+                                __builtin_amdgcn_raw_buffer_store_b32(v[4 * c], yr, boff, 0, 0);
+                            else if constexpr (n == 2)
+                                __builtin_amdgcn_raw_buffer_store_b64((v2i_){v[4 * c], v[4 * c + 1]}, yr, boff, 0, 0);
+                            else if constexpr (n == 3)
+                                __builtin_amdgcn_raw_buffer_store_b96((v3i_){v[4 * c], v[4 * c + 1], v[4 * c + 2]}, yr, boff, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b128((v4i_){v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]}, yr, boff, 0, 0);
+                        });
                     }
                 }
         } else {
@@ -773,7 +780,7 @@ hipError_t launch_convT1d_f32(const float *x, const float *w, const float *bias,
 bool convT1d_f32_poly_supported(int64_t Cin, int K, int stride, int dilation, int64_t L,
                                 const void *x)
 {
-    return Cin == 32 && K == 5 && dilation == 3 && stride >= 2 && stride <= 4 && L % 4 == 0 &&
+    return Cin == 32 && K == 5 && dilation == 3 && stride >= 2 && stride <= 8 && L % 4 == 0 &&
            (((uintptr_t)x) & 15) == 0;
 }
 
@@ -826,7 +833,19 @@ hipError_t launch_convT1d_f32_poly(const float *x, const float *w, const float *
     if (stride == 3)
         return launch_poly<3, 4, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
                                     stream);
-    return launch_poly<4, 3, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out, stream);
+    if (stride == 4)
+        return launch_poly<4, 3, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
+                                    stream);
+    if (stride == 5)
+        return launch_poly<5, 2, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
+                                    stream);
+    if (stride == 6)
+        return launch_poly<6, 2, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
+                                    stream);
+    if (stride == 7)
+        return launch_poly<7, 2, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out,
+                                    stream);
+    return launch_poly<8, 2, 4>(x, w, bias, N, Cin, L, Cout, K, pad, dilation, out_pad, out, stream);
 }
 
 }  // namespace ct

@@ -402,13 +402,13 @@ ct_status ct_convT1d(const void *x, int x_dtype, const void *w, int w_dtype, con
                     (Cout + 63) / 64 <= 65535 && prod({Cout, Lo, 4}, &item) &&
                     item < (int64_t(1) << 31) - 64;
     }
-    // Stride 2 to 4 in fp32 at the page's channel and tap geometry runs as
+    // Stride 2 to 8 in fp32 at the page's channel and tap geometry runs as
     // stride-1 gathers over the residue classes of o + pad on the fp32
     // matrix cores.
-    bool poly = x_dtype == CT_F32 && stride >= 2 && stride <= 4 &&
+    bool poly = x_dtype == CT_F32 && stride >= 2 && stride <= 8 &&
                 ct::convT1d_f32_poly_supported(Cin, K, stride, dilation, L, x);
     if (poly) {
-        const int64_t tq = ((Lo + pad + stride - 1) / stride + 64) / 64 + 1;
+        const int64_t tq = ((Lo + pad + stride - 1) / stride + 16) / 16 + 1;   // 16-q tiles bound every stride's
         int64_t ntq, item;
         poly = Lo <= kI32Max / 2 && pad <= kGenericMaxLen && prod({N, tq}, &ntq) &&
                ntq <= kI32Max && (Cout + 63) / 64 <= 65535 && prod({Cout, Lo, 4}, &item) &&
